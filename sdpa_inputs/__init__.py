@@ -1,0 +1,223 @@
+"""Seeded synthetic inputs for the attention forward: shapes, seeds, value draws.
+
+This module is shared by the GPU path's tests/bench and by the CPU oracle's tests, so it holds
+no attention arithmetic at all: it only draws numbers and stores them in the dtype the kernel
+receives. Both sides get the *same bytes*: bf16 inputs are produced once here (fp32 draw, then
+round-to-nearest-even to bf16) and handed to the GPU as raw 16-bit words and to the oracle as
+float64 upcasts of those same words.
+
+The workloads take their shapes from the pages:
+  * Mistral-7B attention (32 query heads, 8 KV heads, head dim 128, sliding window 4096,
+    batch 4, seq 4096/8192) -- transformers issue "Slowdown in Training Speed Due to SDPA Mask
+    Fix in Version 4.40.0" (the throughput table and the reproduction script);
+  * T5-small encoder attention (12 heads, head dim 64) with bucketed relative-position bias or a
+    full additive bias -- the FAT5 (flashT5) README, attention-bias list;
+  * MHA / GQA / MQA head sharing -- "jax-gpu-05-attention-gpu" codelab, section 9.
+Values are N(0,1) draws (the codelab draws Q, K, V with a normal generator, section 3). The
+pages' own datasets (alpaca-cleaned, CulturaX, ...) are not used: these synthetic tensors
+stand in for the activations those runs would produce.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import numpy as np
+
+MASK_NONE, MASK_CAUSAL, MASK_SLIDING = 0, 1, 2
+BIAS_NONE, BIAS_T5, BIAS_FULL = 0, 1, 2
+MASK_NAMES = {MASK_NONE: "none", MASK_CAUSAL: "causal", MASK_SLIDING: "sliding"}
+BIAS_NAMES = {BIAS_NONE: "none", BIAS_T5: "t5", BIAS_FULL: "full"}
+
+# T5 relative-position table geometry (fixed constants of the bias kind).
+T5_NUM_BUCKETS = 32
+T5_MAX_DISTANCE = 128
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    Sq: int
+    Sk: int
+    D: int
+    dtype: str            # "bf16" or "f32": the dtype of q, k, v (and of a full bias)
+    mask_kind: int
+    window: int = 0
+    bias_kind: int = BIAS_NONE
+    seed: int = 0         # base seed; q = seed, k = seed+1, v = seed+2, t5 table = seed+3, bias = seed+4
+    kv_seed: Optional[int] = None   # overrides the k/v seed base (k = kv_seed+1, v = kv_seed+2)
+    bias_std: float = 0.5
+
+    @property
+    def scale(self) -> float:
+        return float(np.float32(1.0 / np.sqrt(self.D)))
+
+    def replace(self, **kw) -> "Workload":
+        return dataclasses.replace(self, **kw)
+
+    def describe(self) -> dict:
+        d = dict(workload=self.name, B=self.B, Hq=self.Hq, Hkv=self.Hkv, Sq=self.Sq, Sk=self.Sk,
+                 D=self.D, dtype=self.dtype, mask=MASK_NAMES[self.mask_kind],
+                 bias=BIAS_NAMES[self.bias_kind])
+        if self.mask_kind == MASK_SLIDING:
+            d["window"] = self.window
+        return d
+
+
+def _c5(hkv: int) -> Workload:
+    return Workload(f"headshare_hkv{hkv}_b16_s4096", 16, 32, hkv, 4096, 4096, 128, "bf16",
+                    MASK_CAUSAL, seed=5000, kv_seed=5000 + 10 * hkv)
+
+
+# The five workloads (c1..c5); c3c is the full-causal comparison run of c3, c4f the full-bias
+# variant of c4, c5 is swept over Hkv in {32, 8, 1}.
+WORKLOADS = {
+    "c1": Workload("tiny_causal_f32_b1_h2_s128_d64", 1, 2, 2, 128, 128, 64, "f32", MASK_CAUSAL,
+                   seed=1000),
+    "c2": Workload("mistral_gqa_sliding4096_b4_s4096", 4, 32, 8, 4096, 4096, 128, "bf16",
+                   MASK_SLIDING, window=4096, seed=2000),
+    "c3": Workload("mistral_gqa_sliding4096_b4_s8192", 4, 32, 8, 8192, 8192, 128, "bf16",
+                   MASK_SLIDING, window=4096, seed=3000),
+    "c3c": Workload("mistral_gqa_causal_b4_s8192", 4, 32, 8, 8192, 8192, 128, "bf16",
+                    MASK_CAUSAL, seed=3000),
+    "c4t5": Workload("t5_encoder_rpe_b8_h12_s2048_d64", 8, 12, 12, 2048, 2048, 64, "bf16",
+                     MASK_NONE, bias_kind=BIAS_T5, seed=4000),
+    "c4full": Workload("t5_encoder_fullbias_b8_h12_s2048_d64", 8, 12, 12, 2048, 2048, 64, "bf16",
+                       MASK_NONE, bias_kind=BIAS_FULL, seed=4000),
+    "c5mha": _c5(32),
+    "c5gqa": _c5(8),
+    "c5mqa": _c5(1),
+}
+
+
+# ----------------------------------------------------------------------------------------------
+# bf16 storage helpers (bit manipulation only)
+# ----------------------------------------------------------------------------------------------
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (round to nearest, ties to even); return raw uint16 words.
+
+    Inputs here are finite normal draws, so no NaN/Inf special-casing is needed (asserted).
+    """
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    assert np.isfinite(x).all()
+    u = x.view(np.uint32)
+    lsb = (u >> np.uint32(16)) & np.uint32(1)
+    r = (u + np.uint32(0x7FFF) + lsb) >> np.uint32(16)
+    return r.astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Exact widening of bf16 words to float32 (the bf16 word is the top half of the f32 word)."""
+    b = np.ascontiguousarray(b, dtype=np.uint16)
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def bf16_bits_to_f64(b: np.ndarray) -> np.ndarray:
+    return bf16_bits_to_f32(b).astype(np.float64)
+
+
+# ----------------------------------------------------------------------------------------------
+# Draws
+# ----------------------------------------------------------------------------------------------
+def normal_f32(seed: int, shape, std: float = 1.0) -> np.ndarray:
+    x = np.random.default_rng(seed).standard_normal(shape, dtype=np.float32)
+    if std != 1.0:
+        x *= np.float32(std)
+    return x
+
+
+@dataclasses.dataclass
+class Inputs:
+    """One workload's inputs, in the storage the kernel receives.
+
+    For bf16 workloads q/k/v (and a full bias) are uint16 bf16 words; for f32 they are float32.
+    t5_table is always float32 [Hq][32].
+    """
+    wl: Workload
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    t5_table: Optional[np.ndarray] = None
+    bias: Optional[np.ndarray] = None
+
+    def as_f64(self):
+        """float64 views of the exact values the kernel sees: (q, k, v, bias-or-table)."""
+        conv = bf16_bits_to_f64 if self.wl.dtype == "bf16" else (lambda a: a.astype(np.float64))
+        extra = None
+        if self.wl.bias_kind == BIAS_T5:
+            extra = self.t5_table.astype(np.float64)
+        elif self.wl.bias_kind == BIAS_FULL:
+            extra = conv(self.bias)
+        return conv(self.q), conv(self.k), conv(self.v), extra
+
+
+def _store(x: np.ndarray, dtype: str) -> np.ndarray:
+    return f32_to_bf16_bits(x) if dtype == "bf16" else np.ascontiguousarray(x, np.float32)
+
+
+def make_inputs(wl: Workload) -> Inputs:
+    """Draw q [B,Sq,Hq,D], k/v [B,Sk,Hkv,D] (+ t5 table [Hq,32] or bias [B,Hq,Sq,Sk])."""
+    kvs = wl.seed if wl.kv_seed is None else wl.kv_seed
+    q = _store(normal_f32(wl.seed, (wl.B, wl.Sq, wl.Hq, wl.D)), wl.dtype)
+    k = _store(normal_f32(kvs + 1, (wl.B, wl.Sk, wl.Hkv, wl.D)), wl.dtype)
+    v = _store(normal_f32(kvs + 2, (wl.B, wl.Sk, wl.Hkv, wl.D)), wl.dtype)
+    inp = Inputs(wl, q, k, v)
+    if wl.bias_kind == BIAS_T5:
+        inp.t5_table = normal_f32(wl.seed + 3, (wl.Hq, T5_NUM_BUCKETS))
+    elif wl.bias_kind == BIAS_FULL:
+        inp.bias = _store(normal_f32(wl.seed + 4, (wl.B, wl.Hq, wl.Sq, wl.Sk), wl.bias_std),
+                          wl.dtype)
+    return inp
+
+
+def small(wl: Workload, *, B=None, Hq=None, Hkv=None, Sq=None, Sk=None, window=None,
+          name_suffix="small") -> Workload:
+    """A reduced copy of a workload with the same kinds (for element-by-element parity)."""
+    kw = {}
+    for key, val in dict(B=B, Hq=Hq, Hkv=Hkv, Sq=Sq, Sk=Sk, window=window).items():
+        if val is not None:
+            kw[key] = val
+    return wl.replace(name=f"{wl.name}_{name_suffix}", **kw)
+
+
+# ----------------------------------------------------------------------------------------------
+# Work counts (index arithmetic only; used to price the run in FLOP and bytes)
+# ----------------------------------------------------------------------------------------------
+def visible_pairs(Sq: int, Sk: int, mask_kind: int, window: int = 0) -> int:
+    """Number of (query, key) pairs the mask leaves visible in one (batch, head).
+
+    Query i sits at absolute position i + (Sk - Sq) (bottom-right alignment). Pure counting.
+    """
+    off = Sk - Sq
+    total = 0
+    for i in range(Sq):
+        p = i + off
+        if mask_kind == MASK_NONE:
+            total += Sk
+            continue
+        hi = min(p, Sk - 1)            # last visible key
+        if hi < 0:
+            continue
+        lo = 0 if mask_kind == MASK_CAUSAL else max(0, p - window + 1)
+        total += max(0, hi - lo + 1)
+    return total
+
+
+def effective_flops(wl: Workload) -> float:
+    """4*D flop per visible pair (Q.K^T and P.V, 2 flop per multiply-add); exps not counted."""
+    return 4.0 * wl.D * visible_pairs(wl.Sq, wl.Sk, wl.mask_kind, wl.window) * wl.B * wl.Hq
+
+
+def algorithmic_bytes(wl: Workload) -> float:
+    """Read q, k, v (and a full bias) once, write out and lse once."""
+    es = 2 if wl.dtype == "bf16" else 4
+    b = es * wl.B * wl.D * (2 * wl.Sq * wl.Hq + 2 * wl.Sk * wl.Hkv)
+    b += 4 * wl.B * wl.Hq * wl.Sq
+    if wl.bias_kind == BIAS_FULL:
+        b += es * wl.B * wl.Hq * wl.Sq * wl.Sk
+    elif wl.bias_kind == BIAS_T5:
+        b += 4 * wl.Hq * T5_NUM_BUCKETS
+    return float(b)
