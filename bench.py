@@ -1,0 +1,240 @@
+"""Benchmark of the fused attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2] [--sweep]
+
+A step is one fused forward (tile plan, Q load, K/V streaming, Q.K^T, mask/bias, online
+softmax, P.V, epilogue: one kernel launch) over one batch of synthetic input already resident
+in HBM. The default workload is the Mistral-7B-shaped GQA prefill: B=4, Hq=32, Hkv=8, S=4096,
+D=128, bf16, sliding window 4096 (= seqlen, i.e. exactly causal).
+
+Prints ONE JSON line on stdout. `value` is effective TFLOP/s: 4*D flop per visible
+(query, key) pair (Q.K^T and P.V), masked pairs excluded, exps not counted. Timing: W untimed
+warmup launches, then K launches bracketed by device synchronisation, each launch also
+bracketed by HIP events on the stream it runs on (the median-of-repeats-with-device-sync
+method of the "jax-gpu-05-attention-gpu" codelab, section 8). The CPU baseline is the fp64
+oracle timed on a bounded sample of the same workload on this host's cores.
+
+--sweep additionally times every other workload and prints one JSON line per workload on
+stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import sdpa_inputs as si  # noqa: E402
+
+METRIC = "attention fwd effective TFLOP/s (masked tiles excluded) + % of bf16 MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0           # MI355X HBM3E, published
+KERNEL_SOURCES = ["scaled_dot_product_03_amd/csrc/sdpa_fwd_bf16.hip",
+                  "scaled_dot_product_03_amd/csrc/sdpa_params.h"]
+TRAFFIC_FILE = "profiles/sdpa_fwd_bf16_c2_traffic.json"
+
+
+def kernel_sha() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str):
+    """HBM bytes per launch measured by rocprofv3 counters, if taken on this exact kernel."""
+    path = os.path.join(ROOT, TRAFFIC_FILE)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_sha") != kernel_sha() or rec.get("workload") != workload:
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+def to_device(inp: si.Inputs):
+    import torch
+
+    def dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    bias = None
+    if inp.wl.bias_kind == si.BIAS_T5:
+        bias = torch.from_numpy(inp.t5_table).cuda()
+    elif inp.wl.bias_kind == si.BIAS_FULL:
+        bias = dev(inp.bias)
+    return dev(inp.q), dev(inp.k), dev(inp.v), bias
+
+
+def time_workload(sdpa, wl: si.Workload, steps: int, warmup: int):
+    """Returns dict with ms_per_step (wall, synchronised), kernel_ms_avg / median (events)."""
+    import torch
+    inp = si.make_inputs(wl)
+    q, k, v, bias = to_device(inp)
+    del inp
+    out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    lse = torch.empty((wl.B, wl.Hq, wl.Sq), dtype=torch.float32, device=q.device)
+    stream = torch.cuda.current_stream()
+
+    def launch():
+        sdpa.fwd(q, k, v, scale=wl.scale, mask=wl.mask_kind, window=wl.window,
+                 bias_kind=wl.bias_kind, bias=bias, out=out, lse=lse,
+                 stream=stream.cuda_stream)
+
+    for _ in range(warmup):
+        launch()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record(stream)
+        launch()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
+    del q, k, v, bias, out, lse
+    torch.cuda.empty_cache()
+    return dict(ms_per_step=1e3 * wall / steps, kernel_ms_avg=float(ev.mean()),
+                kernel_ms_median=float(np.median(ev)), kernel_ms_min=float(ev.min()))
+
+
+def cpu_baseline(wl: si.Workload, budget_s: float = 12.0):
+    """The fp64 oracle on the same workload, timed on this host's cores: (batch, head) pairs
+    in rounds of `threads` pairs (one pair per thread, BLAS pinned to one thread each) until
+    the whole workload is done or the time budget is spent, repeating the workload while less
+    than half the budget has elapsed. Effective TFLOP/s over the pairs it finished."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:          # pragma: no cover
+        threadpool_limits = None
+    threads = oracle.default_threads()
+    inp = si.make_inputs(wl)
+    q, k, v, extra = inp.as_f64()
+    del inp
+    pairs = [(b, h) for b in range(wl.B) for h in range(wl.Hq)]
+    done = 0
+    passes = 0
+    t0 = time.perf_counter()
+    ctx = threadpool_limits(limits=1) if threadpool_limits else None
+    if ctx:
+        ctx.__enter__()
+    try:
+        while True:
+            i = done % len(pairs)
+            chunk = pairs[i:i + threads]
+            oracle.sdpa_forward(q, k, v, scale=float(np.float32(wl.scale)),
+                                mask_kind=wl.mask_kind, window=wl.window,
+                                bias_kind=wl.bias_kind, bias=extra, threads=threads,
+                                heads=chunk)
+            done += len(chunk)
+            el = time.perf_counter() - t0
+            if done % len(pairs) == 0:
+                passes += 1
+                if el >= budget_s / 2:
+                    break
+            if el >= budget_s:
+                break
+    finally:
+        if ctx:
+            ctx.__exit__(None, None, None)
+    secs = time.perf_counter() - t0
+    per_head = 4.0 * wl.D * si.visible_pairs(wl.Sq, wl.Sk, wl.mask_kind, wl.window)
+    what = (f"the whole workload {passes}x" if done % len(pairs) == 0 and passes
+            else f"{done} of {len(pairs)} (batch, head) pairs")
+    return {"value": per_head * done / secs / 1e12, "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{what} of {wl.name} ({len(pairs)} (batch, head) pairs, all "
+                      f"{wl.Sq} query rows each), fp64 numpy, one pair per thread, "
+                      f"{secs:.1f} s"}
+
+
+def report(wl: si.Workload, t: dict):
+    flops = si.effective_flops(wl)
+    achieved = flops / (t["kernel_ms_avg"] * 1e-3) / 1e12
+    return flops, achieved
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c2", choices=sorted(si.WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweep", action="store_true")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py: this benchmark runs on exactly one GPU (asked for {args.gpus}); "
+              "the attention forward has no multi-GPU path", file=sys.stderr)
+        return 2
+
+    import torch
+    import scaled_dot_product_03_amd as sdpa
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    sdpa.load()
+
+    wl = si.WORKLOADS[args.workload]
+    t = time_workload(sdpa, wl, args.steps, args.warmup)
+    flops, achieved = report(wl, t)
+    value = flops / (t["ms_per_step"] * 1e-3) / 1e12
+    traffic = load_traffic(wl.name)
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(t["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "config": {**wl.describe(), "effective_gflop": round(flops / 1e9, 2),
+                   "kernel_ms_median": round(t["kernel_ms_median"], 4),
+                   "hbm_gbs_algorithmic": round(si.algorithmic_bytes(wl) /
+                                                (t["kernel_ms_avg"] * 1e-3) / 1e9, 1)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(line), flush=True)
+
+    if args.sweep:
+        for key in ["c2", "c3", "c3c", "c4t5", "c4full", "c5mha", "c5gqa", "c5mqa"]:
+            w2 = si.WORKLOADS[key]
+            t2 = time_workload(sdpa, w2, max(5, args.steps // 2), args.warmup)
+            f2, a2 = report(w2, t2)
+            rec = {"workload": key, **w2.describe(), "kernel_ms_avg": round(t2["kernel_ms_avg"], 4),
+                   "kernel_ms_median": round(t2["kernel_ms_median"], 4),
+                   "effective_tflops": round(a2, 2),
+                   "pct_of_bf16_peak": round(100 * a2 / PEAK_BF16_TFLOPS, 2),
+                   "hbm_gbs_algorithmic": round(si.algorithmic_bytes(w2) /
+                                                (t2["kernel_ms_avg"] * 1e-3) / 1e9, 1)}
+            print(json.dumps(rec), file=sys.stderr, flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

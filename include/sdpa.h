@@ -1,0 +1,109 @@
+/*
+ * sdpa.h -- C ABI of the MI355X (gfx950) fused scaled-dot-product attention forward.
+ *
+ * Operation (one call = one fused kernel launch):
+ *     O   = softmax(Q.K^T * scale + bias + mask) . V
+ *     LSE = log(sum_j exp(Q.K^T * scale + bias + mask))        (natural log, per query row)
+ *   Definition: the four steps (score, scale + softmax, attend, output with Q's shape) of the
+ *   "jax-gpu-05-attention-gpu" codelab, section 1, and of the Medium post "Simplified
+ *   Explanation of Attention", steps 1-4. Masks are generated inside the kernel from indices
+ *   (codelab section 7, is_causal; transformers issue "Slowdown in Training Speed Due to SDPA
+ *   Mask Fix in Version 4.40.0" for the sliding window). Biases: T5 bucketed relative-position
+ *   bias or a full additive bias (FAT5 / flashT5 README, attention-bias list). Head sharing:
+ *   MHA / GQA / MQA (codelab section 9).
+ *
+ * Layout (codelab section 3: batch, sequence, heads, head dim; innermost dim contiguous):
+ *   q, out : [B][Sq][Hq][D]          k, v : [B][Sk][Hkv][D]          lse : [B][Hq][Sq] fp32
+ *   Query head h reads KV head h / (Hq / Hkv) (contiguous groups).
+ *   Query row i sits at absolute position i + (Sk - Sq) (bottom-right alignment).
+ *
+ * Masks (mask_kind):
+ *   SDPA_MASK_NONE     every key visible.
+ *   SDPA_MASK_CAUSAL   key j visible from query position p iff j <= p.
+ *   SDPA_MASK_SLIDING  key j visible iff 0 <= p - j < window (window >= Sk equals CAUSAL,
+ *                      bit for bit). `window` is ignored for the other kinds.
+ *   A query row that sees no key gets O = 0 and LSE = -inf.
+ *
+ * Biases (bias_kind, bias_tbl):
+ *   SDPA_BIAS_NONE  bias_tbl must be NULL.
+ *   SDPA_BIAS_T5    bias_tbl = fp32 table [Hq][32]; the score of (query position p, key j) in
+ *                   head h gets tbl[h][bucket(j - p)], where bucket is the T5 bidirectional
+ *                   scheme: 16 buckets per sign of j - p (keys after the query use buckets
+ *                   16..31), distances 0..7 exact, 8..127 log-spaced, >= 128 (in fact >= 91)
+ *                   saturating at the last bucket of the half.
+ *   SDPA_BIAS_FULL  bias_tbl = [B][Hq][Sq][Sk] in the input dtype (bf16 for sdpa_fwd and
+ *                   sdpa_fwd_bf16_f32out, fp32 for sdpa_fwd_f32).
+ *
+ * Conventions for every entry point:
+ *   - All pointers are DEVICE pointers owned by the caller. The library allocates nothing,
+ *     keeps nothing after returning, and writes every element of out and lse.
+ *   - q, k, v, out and a full bias must be 16-byte aligned; lse 4-byte aligned.
+ *   - stream is a hipStream_t (NULL = the default stream). The call only enqueues work; inputs
+ *     must stay alive until the stream has finished it.
+ *   - Returns SDPA_OK or the first failed check; on error nothing is launched. No exception
+ *     crosses this boundary. Launch failures return SDPA_ERR_LAUNCH.
+ *   - Thread-safe: no mutable global state. Results are bitwise reproducible run to run for a
+ *     given shape (fixed tile shape chosen from the shape alone, fixed key order, no atomics),
+ *     the determinism the transformers issue "Transformer models are not deterministic when
+ *     using Flash Attention 2" asks of a fused kernel.
+ *   - Validation: B, Hq, Hkv, Sq, Sk >= 1; Hq % Hkv == 0; D in {64, 128}; scale finite;
+ *     SLIDING needs window >= 1; bias_tbl non-NULL iff bias_kind != NONE; B*Hq*Sq*D,
+ *     B*Hkv*Sk*D (and B*Hq*Sq*Sk for a full bias) below 2^40 elements.
+ */
+#ifndef SDPA_MI355X_SDPA_H
+#define SDPA_MI355X_SDPA_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SDPA_ABI_VERSION 1
+
+enum sdpa_mask_kind { SDPA_MASK_NONE = 0, SDPA_MASK_CAUSAL = 1, SDPA_MASK_SLIDING = 2 };
+enum sdpa_bias_kind { SDPA_BIAS_NONE = 0, SDPA_BIAS_T5 = 1, SDPA_BIAS_FULL = 2 };
+
+enum sdpa_status {
+    SDPA_OK = 0,
+    SDPA_ERR_NULL = 1,      /* a required pointer is NULL */
+    SDPA_ERR_SHAPE = 2,     /* B, Hq, Hkv, Sq or Sk < 1, or a tensor too large */
+    SDPA_ERR_HEADS = 3,     /* Hq not a multiple of Hkv */
+    SDPA_ERR_HEADDIM = 4,   /* D not in {64, 128} */
+    SDPA_ERR_MASK = 5,      /* unknown mask_kind */
+    SDPA_ERR_WINDOW = 6,    /* SLIDING with window < 1 */
+    SDPA_ERR_BIAS = 7,      /* unknown bias_kind, or bias_tbl NULL/non-NULL against it */
+    SDPA_ERR_SCALE = 8,     /* scale not finite */
+    SDPA_ERR_ALIGN = 9,     /* a pointer is not aligned as required */
+    SDPA_ERR_LAUNCH = 10    /* the HIP launch reported an error */
+};
+
+/*
+ * bf16 forward: q, k, v, out are bf16 (raw 16-bit words); lse fp32. The hot path: bf16 MFMA
+ * for Q.K^T and P.V with fp32 accumulation, fp32 online softmax, O rounded to bf16 (nearest
+ * even) from exactly the fp32 value sdpa_fwd_bf16_f32out returns.
+ */
+int sdpa_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+             int B, int Hq, int Hkv, int Sq, int Sk, int D, float scale,
+             int mask_kind, int window, int bias_kind, const void* bias_tbl, void* stream);
+
+/* Same kernel as sdpa_fwd (bf16 inputs), but out is fp32: [B][Sq][Hq][D] float. */
+int sdpa_fwd_bf16_f32out(const void* q, const void* k, const void* v, float* out, float* lse,
+                         int B, int Hq, int Hkv, int Sq, int Sk, int D, float scale,
+                         int mask_kind, int window, int bias_kind, const void* bias_tbl,
+                         void* stream);
+
+/* fp32 forward (fp32 q, k, v, out, full bias): the high-precision path, fp32 FMA arithmetic. */
+int sdpa_fwd_f32(const float* q, const float* k, const float* v, float* out, float* lse,
+                 int B, int Hq, int Hkv, int Sq, int Sk, int D, float scale,
+                 int mask_kind, int window, int bias_kind, const void* bias_tbl, void* stream);
+
+/* Static English text for a status code (never NULL). */
+const char* sdpa_status_str(int status);
+
+/* SDPA_ABI_VERSION of the built library. */
+int sdpa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SDPA_MI355X_SDPA_H */

@@ -1,0 +1,159 @@
+"""MI355X (gfx950) fused scaled-dot-product attention forward.
+
+Thin Python binding over the C ABI in include/sdpa.h (libsdpa_mi355x.so, built in-tree by
+scaled_dot_product_03_amd.build). This module only marshals arguments: torch supplies device
+memory and the current stream, every step of the attention runs in the HIP kernels. There is no
+fallback: if the library is missing, calls raise.
+
+    out, lse = fwd(q, k, v, mask="causal")           # q [B,Sq,Hq,D], k/v [B,Sk,Hkv,D]
+
+Layout follows the "jax-gpu-05-attention-gpu" codelab, section 3 (batch, sequence, heads,
+head dim). lse is [B, Hq, Sq] fp32 (natural log).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_NAME = "libsdpa_mi355x.so"
+
+MASK_NONE, MASK_CAUSAL, MASK_SLIDING = 0, 1, 2
+BIAS_NONE, BIAS_T5, BIAS_FULL = 0, 1, 2
+_MASKS = {"none": MASK_NONE, "causal": MASK_CAUSAL, "sliding": MASK_SLIDING}
+_BIASES = {"none": BIAS_NONE, "t5": BIAS_T5, "full": BIAS_FULL}
+
+SDPA_OK = 0
+STATUS_NAMES = {0: "SDPA_OK", 1: "SDPA_ERR_NULL", 2: "SDPA_ERR_SHAPE", 3: "SDPA_ERR_HEADS",
+                4: "SDPA_ERR_HEADDIM", 5: "SDPA_ERR_MASK", 6: "SDPA_ERR_WINDOW",
+                7: "SDPA_ERR_BIAS", 8: "SDPA_ERR_SCALE", 9: "SDPA_ERR_ALIGN",
+                10: "SDPA_ERR_LAUNCH"}
+
+# symbols exported by the library (must match include/sdpa.h)
+ENTRY_POINTS = ("sdpa_fwd", "sdpa_fwd_bf16_f32out", "sdpa_fwd_f32", "sdpa_status_str",
+                "sdpa_abi_version")
+
+_lib = None
+
+
+class SdpaError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {msg}")
+        self.status = status
+
+
+def lib_path() -> str:
+    return os.path.join(PKG, LIB_NAME)
+
+
+def load():
+    """Load the shared library (once). Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = lib_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
+                           "`python -m scaled_dot_product_03_amd.build`")
+    L = ctypes.CDLL(path)
+    fwd_args = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 6 + [ctypes.c_float] + \
+               [ctypes.c_int] * 3 + [ctypes.c_void_p, ctypes.c_void_p]
+    for name in ("sdpa_fwd", "sdpa_fwd_bf16_f32out", "sdpa_fwd_f32"):
+        fn = getattr(L, name)
+        fn.argtypes = fwd_args
+        fn.restype = ctypes.c_int
+    L.sdpa_status_str.argtypes = [ctypes.c_int]
+    L.sdpa_status_str.restype = ctypes.c_char_p
+    L.sdpa_abi_version.argtypes = []
+    L.sdpa_abi_version.restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def status_str(status: int) -> str:
+    return load().sdpa_status_str(status).decode()
+
+
+def call_raw(entry: str, q, k, v, out, lse, B, Hq, Hkv, Sq, Sk, D, scale, mask_kind, window,
+             bias_kind, bias, stream) -> int:
+    """Call an entry point with raw integer pointers; returns the status code."""
+    fn = getattr(load(), entry)
+    return fn(q, k, v, out, lse, B, Hq, Hkv, Sq, Sk, D, ctypes.c_float(scale), mask_kind, window,
+              bias_kind, bias, stream)
+
+
+def _kind(val, table, what):
+    if isinstance(val, str):
+        if val not in table:
+            raise ValueError(f"unknown {what} {val!r}")
+        return table[val]
+    return int(val)
+
+
+def fwd(q, k, v, *, scale: Optional[float] = None, mask="causal", window: int = 0,
+        bias_kind="none", bias=None, out=None, lse=None, out_dtype=None, stream=None):
+    """Fused attention forward on the current HIP stream. Returns (out, lse).
+
+    q [B,Sq,Hq,D], k/v [B,Sk,Hkv,D]: contiguous cuda tensors, all bf16 or all fp32.
+    mask: "none" | "causal" | "sliding" (window keys, including the query's own position).
+    bias_kind: "none" | "t5" (bias = fp32 table [Hq, 32]) | "full" (bias [B, Hq, Sq, Sk] in
+    the input dtype). out_dtype: torch.float32 with bf16 inputs selects the fp32 epilogue.
+    """
+    import torch
+
+    L = load()
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-D [B, S, H, D]")
+    B, Sq, Hq, D = q.shape
+    Bk, Sk, Hkv, Dk = k.shape
+    if (Bk, Dk) != (B, D) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("shape mismatch between q, k, v")
+    if q.dtype != k.dtype or q.dtype != v.dtype:
+        raise ValueError("q, k, v must share a dtype")
+    for t in (q, k, v):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("q, k, v must be contiguous cuda tensors")
+    mk = _kind(mask, _MASKS, "mask")
+    bk = _kind(bias_kind, _BIASES, "bias kind")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if q.dtype == torch.bfloat16:
+        odt = out_dtype or torch.bfloat16
+        entry = "sdpa_fwd" if odt == torch.bfloat16 else "sdpa_fwd_bf16_f32out"
+        if odt not in (torch.bfloat16, torch.float32):
+            raise ValueError("out_dtype must be bf16 or fp32")
+    elif q.dtype == torch.float32:
+        odt = torch.float32
+        entry = "sdpa_fwd_f32"
+        if out_dtype not in (None, torch.float32):
+            raise ValueError("fp32 inputs produce fp32 output")
+    else:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    bias_ptr = None
+    if bk == BIAS_T5:
+        if bias is None or bias.dtype != torch.float32 or tuple(bias.shape) != (Hq, 32) \
+                or not bias.is_contiguous() or not bias.is_cuda:
+            raise ValueError("t5 bias must be a contiguous cuda fp32 [Hq, 32] table")
+        bias_ptr = bias.data_ptr()
+    elif bk == BIAS_FULL:
+        if bias is None or bias.dtype != q.dtype or tuple(bias.shape) != (B, Hq, Sq, Sk) \
+                or not bias.is_contiguous() or not bias.is_cuda:
+            raise ValueError("full bias must be a contiguous cuda [B, Hq, Sq, Sk] tensor "
+                             "in the input dtype")
+        bias_ptr = bias.data_ptr()
+    elif bias is not None:
+        raise ValueError("bias given with bias_kind='none'")
+    if out is None:
+        out = torch.empty((B, Sq, Hq, D), dtype=odt, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = getattr(L, entry)(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                           lse.data_ptr(), B, Hq, Hkv, Sq, Sk, D, ctypes.c_float(scale), mk,
+                           int(window), bk, bias_ptr, stream)
+    if st != SDPA_OK:
+        raise SdpaError(st, L.sdpa_status_str(st).decode())
+    return out, lse

@@ -1,0 +1,128 @@
+// C ABI of the fused attention forward (declared in include/sdpa.h): argument validation and
+// dispatch to the gfx950 kernels. Every check runs before any HIP call, so an invalid call
+// returns its status without touching the device.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "sdpa.h"
+#include "sdpa_params.h"
+
+namespace sdpa {
+hipError_t launch_fwd_bf16(FwdParams p, int D, int mask, int bias, bool out_f32, hipStream_t s);
+hipError_t launch_fwd_f32(FwdParams p, int D, int mask, int bias, hipStream_t s);
+}  // namespace sdpa
+
+namespace {
+
+constexpr long long kMaxElems = 1LL << 40;
+
+bool aligned(const void* ptr, uintptr_t a) { return ((uintptr_t)ptr & (a - 1)) == 0; }
+
+int validate(const void* q, const void* k, const void* v, const void* out, const float* lse,
+             int B, int Hq, int Hkv, int Sq, int Sk, int D, float scale, int mask_kind,
+             int window, int bias_kind, const void* bias_tbl, int elem_bytes) {
+    if (!q || !k || !v || !out || !lse) return SDPA_ERR_NULL;
+    if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || Sk < 1) return SDPA_ERR_SHAPE;
+    if (Hq % Hkv != 0) return SDPA_ERR_HEADS;
+    if (D != 64 && D != 128) return SDPA_ERR_HEADDIM;
+    if (mask_kind != SDPA_MASK_NONE && mask_kind != SDPA_MASK_CAUSAL &&
+        mask_kind != SDPA_MASK_SLIDING)
+        return SDPA_ERR_MASK;
+    if (mask_kind == SDPA_MASK_SLIDING && window < 1) return SDPA_ERR_WINDOW;
+    if (bias_kind != SDPA_BIAS_NONE && bias_kind != SDPA_BIAS_T5 && bias_kind != SDPA_BIAS_FULL)
+        return SDPA_ERR_BIAS;
+    if ((bias_kind == SDPA_BIAS_NONE) != (bias_tbl == nullptr)) return SDPA_ERR_BIAS;
+    if (!isfinite(scale)) return SDPA_ERR_SCALE;
+    const long long qe = (long long)B * Sq * Hq * D;
+    const long long ke = (long long)B * Sk * Hkv * D;
+    if (qe >= kMaxElems || ke >= kMaxElems) return SDPA_ERR_SHAPE;
+    if (bias_kind == SDPA_BIAS_FULL && (long long)B * Hq * Sq * Sk >= kMaxElems) return SDPA_ERR_SHAPE;
+    // grid: one workgroup per 64-row (fp32) or 128-row (bf16) query tile of each (b, head)
+    if ((long long)B * Hq * ((Sq + 63) / 64) >= (1LL << 31)) return SDPA_ERR_SHAPE;
+    if (elem_bytes == 4 && (B > 65535 || Hq > 65535)) return SDPA_ERR_SHAPE;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
+        !aligned(lse, 4))
+        return SDPA_ERR_ALIGN;
+    if (bias_kind == SDPA_BIAS_T5 && !aligned(bias_tbl, 4)) return SDPA_ERR_ALIGN;
+    if (bias_kind == SDPA_BIAS_FULL && !aligned(bias_tbl, 16)) return SDPA_ERR_ALIGN;
+    return SDPA_OK;
+}
+
+sdpa::FwdParams make_params(const void* q, const void* k, const void* v, void* out, float* lse,
+                            int B, int Hq, int Hkv, int Sq, int Sk, float scale, int mask_kind,
+                            int window, const void* bias_tbl) {
+    sdpa::FwdParams p{};
+    p.q = q; p.k = k; p.v = v; p.out = out; p.lse = lse; p.bias = bias_tbl;
+    p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.Sq = Sq; p.Sk = Sk;
+    p.G = Hq / Hkv;
+    p.off = Sk - Sq;
+    // Sliding windows wider than the key range are the causal mask: clamp so window
+    // arithmetic stays in range (the visible set is unchanged).
+    p.window = (mask_kind == SDPA_MASK_SLIDING) ? (window > Sk ? Sk + 1 : window) : 0;
+    p.scale = scale;
+    p.scale_log2 = scale * 1.4426950408889634f;
+    return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sdpa_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq,
+             int Hkv, int Sq, int Sk, int D, float scale, int mask_kind, int window,
+             int bias_kind, const void* bias_tbl, void* stream) {
+    int st = validate(q, k, v, out, lse, B, Hq, Hkv, Sq, Sk, D, scale, mask_kind, window,
+                      bias_kind, bias_tbl, 2);
+    if (st != SDPA_OK) return st;
+    sdpa::FwdParams p = make_params(q, k, v, out, lse, B, Hq, Hkv, Sq, Sk, scale, mask_kind,
+                                    window, bias_tbl);
+    hipError_t e = sdpa::launch_fwd_bf16(p, D, mask_kind, bias_kind, false, (hipStream_t)stream);
+    return e == hipSuccess ? SDPA_OK : SDPA_ERR_LAUNCH;
+}
+
+int sdpa_fwd_bf16_f32out(const void* q, const void* k, const void* v, float* out, float* lse,
+                         int B, int Hq, int Hkv, int Sq, int Sk, int D, float scale,
+                         int mask_kind, int window, int bias_kind, const void* bias_tbl,
+                         void* stream) {
+    int st = validate(q, k, v, out, lse, B, Hq, Hkv, Sq, Sk, D, scale, mask_kind, window,
+                      bias_kind, bias_tbl, 2);
+    if (st != SDPA_OK) return st;
+    sdpa::FwdParams p = make_params(q, k, v, out, lse, B, Hq, Hkv, Sq, Sk, scale, mask_kind,
+                                    window, bias_tbl);
+    hipError_t e = sdpa::launch_fwd_bf16(p, D, mask_kind, bias_kind, true, (hipStream_t)stream);
+    return e == hipSuccess ? SDPA_OK : SDPA_ERR_LAUNCH;
+}
+
+int sdpa_fwd_f32(const float* q, const float* k, const float* v, float* out, float* lse, int B,
+                 int Hq, int Hkv, int Sq, int Sk, int D, float scale, int mask_kind, int window,
+                 int bias_kind, const void* bias_tbl, void* stream) {
+    int st = validate(q, k, v, out, lse, B, Hq, Hkv, Sq, Sk, D, scale, mask_kind, window,
+                      bias_kind, bias_tbl, 4);
+    if (st != SDPA_OK) return st;
+    sdpa::FwdParams p = make_params(q, k, v, out, lse, B, Hq, Hkv, Sq, Sk, scale, mask_kind,
+                                    window, bias_tbl);
+    hipError_t e = sdpa::launch_fwd_f32(p, D, mask_kind, bias_kind, (hipStream_t)stream);
+    return e == hipSuccess ? SDPA_OK : SDPA_ERR_LAUNCH;
+}
+
+const char* sdpa_status_str(int status) {
+    switch (status) {
+        case SDPA_OK: return "ok";
+        case SDPA_ERR_NULL: return "a required pointer is NULL";
+        case SDPA_ERR_SHAPE: return "invalid or too large shape (B, Hq, Hkv, Sq, Sk)";
+        case SDPA_ERR_HEADS: return "Hq is not a multiple of Hkv";
+        case SDPA_ERR_HEADDIM: return "head dim D must be 64 or 128";
+        case SDPA_ERR_MASK: return "unknown mask_kind";
+        case SDPA_ERR_WINDOW: return "sliding window must be >= 1";
+        case SDPA_ERR_BIAS: return "unknown bias_kind or bias_tbl inconsistent with it";
+        case SDPA_ERR_SCALE: return "scale is not finite";
+        case SDPA_ERR_ALIGN: return "pointer misaligned (q/k/v/out/full bias need 16 bytes)";
+        case SDPA_ERR_LAUNCH: return "HIP kernel launch failed";
+        default: return "unknown status";
+    }
+}
+
+int sdpa_abi_version(void) { return SDPA_ABI_VERSION; }
+
+}  // extern "C"

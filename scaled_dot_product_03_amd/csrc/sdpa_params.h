@@ -1,0 +1,78 @@
+// Launch parameters and index helpers shared by the gfx950 attention-forward kernels and the
+// host launcher. Only index arithmetic lives here; the kernels hold the attention math.
+#pragma once
+
+#include <stdint.h>
+
+namespace sdpa {
+
+enum { MASK_NONE = 0, MASK_CAUSAL = 1, MASK_SLIDING = 2 };
+enum { BIAS_NONE = 0, BIAS_T5 = 1, BIAS_FULL = 2 };
+
+// T5 relative-position table: [Hq][32] fp32. Within one sign of (key - query) the bucket
+// saturates for distances >= 91, so a relative position only matters inside [-91, 91].
+constexpr int kT5Buckets = 32;
+constexpr int kT5Sat = 91;
+
+struct FwdParams {
+    const void* q;       // [B][Sq][Hq][D]
+    const void* k;       // [B][Sk][Hkv][D]
+    const void* v;       // [B][Sk][Hkv][D]
+    void* out;           // [B][Sq][Hq][D]
+    float* lse;          // [B][Hq][Sq]
+    const void* bias;    // T5 table [Hq][32] fp32, or full bias [B][Hq][Sq][Sk]
+    int B, Hq, Hkv, Sq, Sk;
+    int G;               // Hq / Hkv: query heads per KV head
+    int off;             // Sk - Sq: absolute position of query row i is i + off
+    int window;          // sliding window (keys with 0 <= pos - j < window are visible)
+    int n_qt;            // query tiles per (batch, head)
+    int xcd_remap;       // 1: place all work of one (batch, KV head) on one XCD
+    float scale;         // softmax scale
+    float scale_log2;    // scale * log2(e)
+};
+
+// T5 bidirectional bucket of rel = key position - query position (integer form of the T5 log
+// spacing: for 8 <= n < 91 the bucket 8 + floor(8 log(n/8) / log 16) equals 1 + bitlen(n^2)).
+__host__ __device__ inline int t5_bucket(int rel) {
+    int n = rel < 0 ? -rel : rel;
+    int b;
+    if (n < 8) {
+        b = n;
+    } else if (n >= kT5Sat) {
+        b = 15;
+    } else {
+        unsigned nn = (unsigned)(n * n);
+        int bitlen = 32 - __builtin_clz(nn);
+        b = 1 + bitlen;
+    }
+    return b + (rel > 0 ? 16 : 0);
+}
+
+// Decode a workgroup index into (batch, query head, query tile). Query tiles of one
+// (batch, KV head) are consecutive, heaviest (latest, for causal masks) first; with
+// xcd_remap, workgroup x runs on XCD x % 8 (round-robin dispatch), and every XCD receives
+// whole (batch, KV head) groups so the G query heads sharing K/V hit the same L2.
+struct WorkItem { int b, hq, qt; };
+
+__host__ __device__ inline WorkItem decode_work(const FwdParams& p, int x) {
+    const int per_group = p.G * p.n_qt;
+    int group, r;
+    if (p.xcd_remap) {
+        const int xcd = x & 7, slot = x >> 3;
+        const int gl = slot / per_group;
+        r = slot - gl * per_group;
+        group = gl * 8 + xcd;
+    } else {
+        group = x / per_group;
+        r = x - group * per_group;
+    }
+    WorkItem w;
+    w.b = group / p.Hkv;
+    const int kvh = group - w.b * p.Hkv;
+    const int qi = r / p.G;
+    w.hq = kvh * p.G + (r - qi * p.G);
+    w.qt = p.n_qt - 1 - qi;
+    return w;
+}
+
+}  // namespace sdpa

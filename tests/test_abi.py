@@ -1,0 +1,107 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol include/sdpa.h
+declares, and every invalid call returns its status before any HIP call (so these calls are
+safe on a machine without a GPU: validation fails first and nothing is launched)."""
+import math
+import os
+import re
+
+import pytest
+
+import scaled_dot_product_03_amd as sdpa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sdpa.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(sdpa.lib_path()):
+        from scaled_dot_product_03_amd import build
+        build.build()
+    return sdpa.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(sdpa_\w+)\s*\(", text, flags=re.M)
+
+
+def test_header_declares_entry_points():
+    names = declared_functions()
+    assert sorted(names) == sorted(sdpa.ENTRY_POINTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_abi_version_and_status_strings(lib):
+    assert lib.sdpa_abi_version() == 1
+    for code in range(0, 11):
+        s = sdpa.status_str(code)
+        assert s and s != "unknown status"
+    assert sdpa.status_str(999) == "unknown status"
+
+
+# fake, aligned, never-dereferenced device addresses
+P = 0x10000
+GOOD = dict(q=P, k=P, v=P, out=P, lse=P, B=1, Hq=4, Hkv=2, Sq=8, Sk=8, D=64, scale=0.125,
+            mask_kind=1, window=0, bias_kind=0, bias=None, stream=None)
+
+
+def call(entry="sdpa_fwd", **kw):
+    a = dict(GOOD)
+    a.update(kw)
+    return sdpa.call_raw(entry, a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"], a["Hq"],
+                         a["Hkv"], a["Sq"], a["Sk"], a["D"], a["scale"], a["mask_kind"],
+                         a["window"], a["bias_kind"], a["bias"], a["stream"])
+
+
+BAD_CASES = [
+    ("null q", dict(q=None), 1),
+    ("null lse", dict(lse=None), 1),
+    ("B=0", dict(B=0), 2),
+    ("Sk=0", dict(Sk=0), 2),
+    ("Hkv=0", dict(Hkv=0), 2),
+    ("Hq % Hkv", dict(Hq=6, Hkv=4), 3),
+    ("D=96", dict(D=96), 4),
+    ("D=256", dict(D=256), 4),
+    ("mask 3", dict(mask_kind=3), 5),
+    ("mask -1", dict(mask_kind=-1), 5),
+    ("sliding window 0", dict(mask_kind=2, window=0), 6),
+    ("sliding window -5", dict(mask_kind=2, window=-5), 6),
+    ("bias kind 3", dict(bias_kind=3, bias=P), 7),
+    ("t5 without table", dict(bias_kind=1, bias=None), 7),
+    ("full without tensor", dict(bias_kind=2, bias=None), 7),
+    ("no bias but pointer", dict(bias_kind=0, bias=P), 7),
+    ("scale nan", dict(scale=math.nan), 8),
+    ("scale inf", dict(scale=math.inf), 8),
+    ("misaligned q", dict(q=P + 8), 9),
+    ("misaligned out", dict(out=P + 2), 9),
+    ("misaligned lse", dict(lse=P + 2), 9),
+    ("misaligned full bias", dict(bias_kind=2, bias=P + 4), 9),
+    ("huge q", dict(B=1 << 16, Sq=1 << 16, Hq=1 << 8, Hkv=1 << 8, D=128), 2),
+]
+
+
+@pytest.mark.parametrize("entry", ["sdpa_fwd", "sdpa_fwd_bf16_f32out", "sdpa_fwd_f32"])
+@pytest.mark.parametrize("name,kw,code", BAD_CASES, ids=[c[0] for c in BAD_CASES])
+def test_invalid_arguments_return_status(lib, entry, name, kw, code):
+    assert call(entry, **kw) == code
+
+
+def test_first_failing_check_wins(lib):
+    # null pointer is checked before shapes, shapes before heads, heads before head dim
+    assert call(q=None, B=0) == 1
+    assert call(B=0, Hq=6, Hkv=4) == 2
+    assert call(Hq=6, Hkv=4, D=96) == 3
+    assert call(D=96, mask_kind=9) == 4
+
+
+def test_binding_rejects_before_launch(lib):
+    torch = pytest.importorskip("torch")
+    q = torch.zeros(1, 8, 2, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        sdpa.fwd(q, q, q)            # cpu tensors are refused by the binding

@@ -1,0 +1,104 @@
+"""GPU determinism and exact invariants of the kernel.
+
+Determinism follows the protocol of the transformers issue "Transformer models are not
+deterministic when using Flash Attention 2": repeat the same forward and compare with
+torch.equal against the first run (here 100 runs, on both out and LSE).
+"""
+import numpy as np
+import pytest
+
+import sdpa_inputs as si
+from helpers import out_to_f64, run_gpu, to_device
+
+pytestmark = pytest.mark.gpu
+W = si.WORKLOADS
+
+
+@pytest.mark.parametrize("key", ["c5gqa", "c5mqa", "c2", "c3", "c4t5", "c4full"])
+def test_bitwise_determinism_100_runs(gpu_lib, key):
+    import torch
+    wl = W[key]
+    inp = si.make_inputs(wl)
+    dev = to_device(inp)
+    o0, l0 = run_gpu(gpu_lib, wl, dev)
+    o0, l0 = o0.clone(), l0.clone()
+    same = True
+    for _ in range(99):
+        o, l = run_gpu(gpu_lib, wl, dev)
+        same = same and torch.equal(o, o0) and torch.equal(l, l0)
+    assert same
+    h = int(torch.sum(o0.view(torch.int16).to(torch.int64) * 1000003 % 65521).item())
+    print(f"{key}: deterministic over 100 runs, out checksum {h}")
+
+
+def _sk(wl, **kw):
+    return si.small(wl, **kw)
+
+
+def test_sliding_window_ge_seqlen_is_causal_bitwise(gpu_lib):
+    """Window >= seqlen must give exactly the plain causal result (transformers issue on the
+    SDPA mask fix: at seqlen == window the result must be that of the causal kernel)."""
+    import torch
+    for S, w in [(4096, 4096), (700, 700), (700, 5000), (513, 514)]:
+        wl = si.small(W["c2"], B=1, Hq=8, Hkv=2, Sq=S, Sk=S, window=w, name_suffix=f"{S}_{w}")
+        dev = to_device(si.make_inputs(wl))
+        o_s, l_s = run_gpu(gpu_lib, wl, dev)
+        o_c, l_c = run_gpu(gpu_lib, wl.replace(mask_kind=si.MASK_CAUSAL), dev)
+        assert torch.equal(o_s, o_c) and torch.equal(l_s, l_c), (S, w)
+
+
+def test_causal_row0_is_v0_bitwise(gpu_lib):
+    import torch
+    wl = si.small(W["c5gqa"], B=2, Hq=8, Hkv=2, Sq=300, Sk=300, name_suffix="row0")
+    inp = si.make_inputs(wl)
+    dev = to_device(inp)
+    o, _ = run_gpu(gpu_lib, wl, dev)
+    v = dev[2]
+    G = wl.Hq // wl.Hkv
+    assert torch.equal(o[:, 0], v[:, 0].repeat_interleave(G, dim=1))
+
+
+def test_window1_is_v_bitwise(gpu_lib):
+    import torch
+    wl = si.small(W["c2"], B=1, Hq=4, Hkv=2, Sq=200, Sk=200, window=1, name_suffix="w1")
+    dev = to_device(si.make_inputs(wl))
+    o, _ = run_gpu(gpu_lib, wl, dev)
+    assert torch.equal(o, dev[2].repeat_interleave(2, dim=2))
+
+
+def test_ones_value_gives_ones(gpu_lib):
+    import torch
+    wl = si.small(W["c4t5"], B=1, Hq=2, Hkv=2, Sq=300, Sk=300, name_suffix="v1")
+    q, k, v, bias = to_device(si.make_inputs(wl))
+    v = torch.ones_like(v)
+    o, _ = run_gpu(gpu_lib, wl, (q, k, v, bias), out_f32=True)
+    # P.V uses P rounded to bf16 (relative error <= 2^-9) while the normaliser sums the
+    # unrounded P, so O = sum(p_hat) / sum(p) lies within 2^-9 / (1 - 2^-9) of 1.
+    bound = 2.0 ** -9 / (1 - 2.0 ** -9) + 1e-6
+    assert torch.max(torch.abs(o - 1.0)).item() <= bound
+
+
+def test_zero_query_gives_visible_mean(gpu_lib):
+    import torch
+    wl = si.small(W["c3"], B=1, Hq=2, Hkv=1, Sq=400, Sk=400, window=37, name_suffix="q0")
+    q, k, v, bias = to_device(si.make_inputs(wl))
+    q = torch.zeros_like(q)
+    o, l = run_gpu(gpu_lib, wl, (q, k, v, bias), out_f32=True)
+    vv = v.float()[0, :, 0]                        # [S, D]
+    cs = torch.cat([torch.zeros_like(vv[:1]), torch.cumsum(vv.double(), 0)])
+    for i in [0, 1, 36, 37, 38, 399]:
+        lo = max(0, i - 37 + 1)
+        mean = (cs[i + 1] - cs[lo]) / (i + 1 - lo)
+        assert torch.max(torch.abs(o[0, i, 0].double() - mean)).item() <= 2e-3
+        assert abs(l[0, 0, i].item() - np.log(i + 1 - lo)) <= 1e-5
+
+
+def test_causal_last_row_equals_unmasked_last_row(gpu_lib):
+    """Codelab section 7: the last position attends to every position either way."""
+    wl = si.small(W["c5gqa"], B=1, Hq=4, Hkv=2, Sq=257, Sk=257, name_suffix="last")
+    dev = to_device(si.make_inputs(wl))
+    oc, _ = run_gpu(gpu_lib, wl, dev, out_f32=True)
+    on, _ = run_gpu(gpu_lib, wl.replace(mask_kind=si.MASK_NONE), dev, out_f32=True)
+    a, c = out_to_f64(oc), out_to_f64(on)
+    assert np.max(np.abs(a[:, -1] - c[:, -1])) <= 1e-5
+    assert np.max(np.abs(a[:, 0] - c[:, 0])) > 1e-2
