@@ -176,6 +176,9 @@ def main(argv=None):
     ap.add_argument("--workload", default="c2", choices=sorted(si.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="instead of attention, run `steps` device-to-device copies of MIB "
+                         "MiB (reference kernel for scaling HBM byte counters)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -189,6 +192,18 @@ def main(argv=None):
         print("bench.py: no GPU visible", file=sys.stderr)
         return 1
     sdpa.load()
+
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(7)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n, "bytes_written": n,
+                          "launches": args.steps}), flush=True)
+        return 0
 
     wl = si.WORKLOADS[args.workload]
     t = time_workload(sdpa, wl, args.steps, args.warmup)
