@@ -38,6 +38,9 @@ int validate(const void* q, const void* k, const void* v, const void* out, const
     const long long ke = (long long)B * Sk * Hkv * D;
     if (qe >= kMaxElems || ke >= kMaxElems) return SDPA_ERR_SHAPE;
     if (bias_kind == SDPA_BIAS_FULL && (long long)B * Hq * Sq * Sk >= kMaxElems) return SDPA_ERR_SHAPE;
+    // one batch of q/out or k/v is addressed with 32-bit element offsets inside the kernels
+    if ((long long)Sq * Hq * D >= (1LL << 31) || (long long)Sk * Hkv * D >= (1LL << 31))
+        return SDPA_ERR_SHAPE;
     // grid: one workgroup per 64-row (fp32) or 128-row (bf16) query tile of each (b, head)
     if ((long long)B * Hq * ((Sq + 63) / 64) >= (1LL << 31)) return SDPA_ERR_SHAPE;
     if (elem_bytes == 4 && (B > 65535 || Hq > 65535)) return SDPA_ERR_SHAPE;

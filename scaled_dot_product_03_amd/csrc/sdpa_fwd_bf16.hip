@@ -10,29 +10,37 @@
 //
 // Work decomposition (one workgroup = 4 wave64s = one 128-row query tile of one (batch, head)):
 //   * each wave owns 32 query rows; its Q fragment stays in VGPRs for the whole kernel;
-//   * keys are visited in tiles of 64, ascending; K (row-major) and V (transposed, [d][key])
-//     tiles are staged in a 2-deep LDS ring, the next tile's global loads in flight while the
-//     current one is computed;
+//   * keys are visited in tiles of 64, ascending; K and V tiles are staged row-major
+//     ([key][d], XOR-swizzled 16-byte chunks) in a 2-deep LDS ring, the next tile's global
+//     loads in flight while the current one is computed;
 //   * scores are computed transposed, S^T = K . Q^T, with v_mfma_f32_32x32x16_bf16: each lane
 //     then holds one query row (lane % 32) and 32 of the tile's keys, so the row max/sum are
 //     in-lane plus one permlane32 exchange with the lane holding the other 32 keys;
-//   * O^T += V^T . P^T with the same MFMA; P comes straight from the score registers (bf16,
-//     nearest even) as the B operand, so P never leaves the lane;
+//   * O^T += V^T . P^T with the same MFMA; the V^T operand comes from the row-major V tile
+//     through ds_read_b64_tr_b16 (transposing LDS read), P straight from the score registers
+//     (bf16, nearest even) as the B operand, so P never leaves the lane;
 //   * online softmax in the log2 domain with a lazy rescale: the running reference max only
-//     moves (and O is only rescaled) when a row's max grows by more than 2^8.
+//     moves (and O is only rescaled) when a row's max grows by more than 2^8;
+//   * interior tiles (no key masked for any row of the wave) run a separate code path with no
+//     per-element mask work; scale*log2(e) is folded into the exponent's FMA.
 // Reduction order is fixed (ascending key tiles, fixed MFMA chains, no atomics): results are
 // bitwise reproducible run to run.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "sdpa_params.h"
 
 namespace sdpa {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr int kThreads = 256;
 constexpr int kBM = 128;        // query rows per workgroup
@@ -48,8 +56,9 @@ __device__ __forceinline__ int perm32(int r) {
     return ((r >> 2) & 1) * 16 + (r >> 3) * 4 + (r & 3);
 }
 
-// LDS bank swizzles (XOR on the 16-byte chunk index within a row).
-// K tile [64 keys][D], D=128: rows of 16 chunks; D=64: rows of 8 chunks.
+// LDS bank swizzles: XOR on the 16-byte chunk index within a row of the K or V tile.
+// K (read by ds_read_b128, 8 lanes on rows {0..3, 16..19} + 4g): D=128 rows are 16 chunks,
+// D=64 rows are 8 chunks.
 template <int D>
 __device__ __forceinline__ int k_swz(int row) {
     if constexpr (D == 128) {
@@ -58,18 +67,12 @@ __device__ __forceinline__ int k_swz(int row) {
         return ((row & 3) ^ ((row >> 2) & 1)) | (((row >> 4) & 1) << 2);
     }
 }
-// V^T tile [D][64 keys]: rows of 8 chunks; conflict-free for both the transposing writes
-// (8 lanes on rows 8 apart) and the MFMA reads (8 lanes on rows {0..3, 16..19} + 4g).
-__device__ __forceinline__ int v_swz(int d) {
-    return (((d & 3) | (((d >> 4) & 1) << 2)) ^ ((d >> 3) & 7) ^ ((d >> 2) & 1)) & 7;
-}
-
-__device__ __forceinline__ uint32_t perm_b32(uint32_t hi, uint32_t lo, uint32_t sel) {
-    return __builtin_amdgcn_perm(hi, lo, sel);
-}
+// V (read by ds_read_b64_tr_b16, a 16-lane group touching chunks {c, c+2} of 4 consecutive
+// rows): rows 4k..4k+3 go to XOR patterns {0, 1, 4, 5}.
+__device__ __forceinline__ int v_swz(int row) { return (row & 1) | ((row & 2) << 1); }
 
 __device__ __forceinline__ float partner_max(float x) {
-    // value of lane l ^ 32 (the other half of the wave)
+    // max of this lane and lane l ^ 32 (the other half of the wave)
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
@@ -81,29 +84,26 @@ __device__ __forceinline__ float partner_sum(float x) {
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
     bf16x2 r;
     r[0] = (__bf16)lo;
     r[1] = (__bf16)hi;
     return __builtin_bit_cast(uint32_t, r);
 }
 
+__device__ __forceinline__ s16x4 lds_read_tr(const uint16_t* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+}
+
 template <int D, int MASK, int BIAS, bool OUT_F32>
 __global__ __launch_bounds__(kThreads, 2) void sdpa_fwd_bf16_kernel(const FwdParams p) {
-    constexpr int KCH = D / 8;          // 16-byte chunks per K row
+    constexpr int CH = D / 8;           // 16-byte chunks per K/V row
     constexpr int KS = D / 16;          // k-steps of Q.K^T
     constexpr int DB = D / 32;          // 32-wide d blocks of O^T
-    constexpr int K_TILE = kBN * D;     // bf16 elements per K buffer
-    constexpr int V_TILE = D * kBN;     // bf16 elements per V^T buffer
-    // Global->LDS staging: K by threads [0, 128) (NK 16-byte chunks each); V by 8x8 blocks,
-    // one per thread in [128, 128 + NVB).
-    constexpr int K_THREADS = 128;
-    constexpr int NK = (kBN * KCH) / K_THREADS;
-    constexpr int NVB = (kBN / 8) * (D / 8);
-    static_assert(NK * K_THREADS == kBN * KCH, "K staging");
-    static_assert(K_THREADS + NVB <= kThreads, "V staging");
+    constexpr int TILE = kBN * D;       // bf16 elements per K (or V) buffer
+    constexpr int NST = kBN * CH / kThreads;   // staged 16-byte chunks per thread per tensor
+    static_assert(NST * kThreads == kBN * CH, "staging");
 
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (K_TILE + V_TILE)];
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * 2 * TILE];
     __shared__ float t5s[BIAS == BIAS_T5 ? 2 * kT5Sat + 1 : 1];
 
     const int tid = threadIdx.x;
@@ -138,7 +138,6 @@ __global__ __launch_bounds__(kThreads, 2) void sdpa_fwd_bf16_kernel(const FwdPar
     const int pwa = wq0 + off;
     const int pwb = min(wq0 + 31, Sq - 1) + off;
 
-    // ---- output helpers --------------------------------------------------------------------
     float* lse_row = p.lse + ((size_t)b * p.Hq + hq) * Sq;
     auto out_ptr = [&](int i) -> char* {
         const size_t e = ((size_t)b * Sq + i) * q_row + (size_t)hq * D;
@@ -151,13 +150,10 @@ __global__ __launch_bounds__(kThreads, 2) void sdpa_fwd_bf16_kernel(const FwdPar
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
                 const int d0 = db * 32 + hh * 16;
-                if constexpr (OUT_F32) {
+                constexpr int NV = OUT_F32 ? 4 : 2;
 #pragma unroll
-                    for (int c = 0; c < 4; ++c) *(u32x4*)(o + (d0 + 4 * c) * 4) = u32x4{0, 0, 0, 0};
-                } else {
-#pragma unroll
-                    for (int c = 0; c < 2; ++c) *(u32x4*)(o + (d0 + 8 * c) * 2) = u32x4{0, 0, 0, 0};
-                }
+                for (int c = 0; c < NV; ++c)
+                    *(u32x4*)(o + (d0 * (OUT_F32 ? 4 : 2)) + 16 * c) = u32x4{0, 0, 0, 0};
             }
             if (hh == 0) lse_row[my_i] = -INFINITY;
         }
@@ -173,73 +169,68 @@ __global__ __launch_bounds__(kThreads, 2) void sdpa_fwd_bf16_kernel(const FwdPar
     // ---- Q fragment: lane holds row my_i, dims 16ks + 8hh .. +7 ----------------------------
     bf16x8 qf[KS];
     {
-        const uint16_t* qr = qg + (size_t)my_i * q_row + hh * 8;
+        const uint16_t* qr = qg + (size_t)(row_ok ? my_i : 0) * q_row + hh * 8;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            u32x4 x = row_ok ? *(const u32x4*)(qr + ks * 16) : u32x4{0, 0, 0, 0};
+            u32x4 x = *(const u32x4*)(qr + ks * 16);
+            if (!row_ok) x = u32x4{0, 0, 0, 0};
             qf[ks] = __builtin_bit_cast(bf16x8, x);
         }
     }
 
-    // ---- global -> register staging of one K/V tile ----------------------------------------
-    u32x4 stage[8];
-    const bool is_k_thread = tid < K_THREADS;
-    const bool is_v_thread = !is_k_thread && (tid - K_THREADS) < NVB;
-    // V block of this thread: key rows 8*vjo .. +7, dims 8*vdc .. +7
-    const int vu = tid - K_THREADS;
-    const int vdc = vu % (D / 8), vjo = vu / (D / 8);
-
+    // ---- global -> register -> LDS staging of one K/V tile ---------------------------------
+    // Thread tid stages chunk c = tid % CH of rows tid / CH + i * (256 / CH), for K and V.
+    // Rows past the end of the keys are clamped to the last key: those keys are masked.
+    constexpr int ROW_STEP = kThreads / CH;
+    const int st_c = tid % CH, st_r = tid / CH;
+    uint32_t st_off[NST];      // element offset of this thread's chunks inside a key tile
+#pragma unroll
+    for (int i = 0; i < NST; ++i) st_off[i] = (uint32_t)((st_r + i * ROW_STEP) * p.Hkv * D + st_c * 8);
+    u32x4 stk[NST], stv[NST];
     auto load_tile = [&](int t) {
         const int j0 = t * kBN;
-        if (is_k_thread) {
+        const uint16_t* kt = kg + (size_t)j0 * kv_row;
+        const uint16_t* vt = vg + (size_t)j0 * kv_row;
+        if (j0 + kBN <= Sk) {
 #pragma unroll
-            for (int i = 0; i < NK; ++i) {
-                const int cid = tid + i * K_THREADS;
-                const int row = cid / KCH, c = cid % KCH;
-                const int j = j0 + row;
-                stage[i] = (j < Sk) ? *(const u32x4*)(kg + (size_t)j * kv_row + c * 8)
-                                    : u32x4{0, 0, 0, 0};
+            for (int i = 0; i < NST; ++i) {
+                stk[i] = *(const u32x4*)(kt + st_off[i]);
+                stv[i] = *(const u32x4*)(vt + st_off[i]);
             }
-        } else if (is_v_thread) {
+        } else {
+            // last, partial tile: rows past the end are clamped to the last key (masked)
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int j = j0 + vjo * 8 + i;
-                stage[i] = (j < Sk) ? *(const u32x4*)(vg + (size_t)j * kv_row + vdc * 8)
-                                    : u32x4{0, 0, 0, 0};
+            for (int i = 0; i < NST; ++i) {
+                const int j = min(j0 + st_r + i * ROW_STEP, Sk - 1);
+                const size_t o = (size_t)j * kv_row + st_c * 8;
+                stk[i] = *(const u32x4*)(kg + o);
+                stv[i] = *(const u32x4*)(vg + o);
             }
         }
     };
     auto store_tile = [&](int buf) {
-        uint16_t* kb = smem + buf * (K_TILE + V_TILE);
-        uint16_t* vb = kb + K_TILE;
-        if (is_k_thread) {
+        uint16_t* kb = smem + buf * (2 * TILE);
+        uint16_t* vb = kb + TILE;
 #pragma unroll
-            for (int i = 0; i < NK; ++i) {
-                const int cid = tid + i * K_THREADS;
-                const int row = cid / KCH, c = cid % KCH;
-                *(u32x4*)(kb + row * D + ((c ^ k_swz<D>(row)) * 8)) = stage[i];
-            }
-        } else if (is_v_thread) {
-            // transpose the 8x8 block: output row d = 8*vdc + e holds keys 8*vjo .. +7
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-                u32x4 o;
-#pragma unroll
-                for (int m = 0; m < 4; ++m)
-                    o[m] = perm_b32(stage[2 * m + 1][e >> 1], stage[2 * m][e >> 1], sel);
-                const int d = vdc * 8 + e;
-                *(u32x4*)(vb + d * kBN + ((vjo ^ v_swz(d)) * 8)) = o;
-            }
+        for (int i = 0; i < NST; ++i) {
+            const int row = st_r + i * ROW_STEP;
+            *(u32x4*)(kb + row * D + ((st_c ^ k_swz<D>(row)) * 8)) = stk[i];
+            *(u32x4*)(vb + row * D + ((st_c ^ v_swz(row)) * 8)) = stv[i];
         }
     };
 
-    // ---- per-lane LDS read offsets (in bf16 elements) --------------------------------------
+    // ---- per-lane LDS read offsets (bf16 elements) -----------------------------------------
     // K: A operand row (lane % 32) -> key perm32(r32) (+32 for the second key block).
     const int krow = perm32(r32);
     const int k_sw = k_swz<D>(krow);          // identical for krow + 32
-    // V^T: A operand row -> head dim 32*db + perm32(r32).
-    const int vrow = perm32(r32);
+    // V^T via transposing reads: within 16-lane group gg = lane / 16, source lane i = lane % 16
+    // points at key 16*hh + (i >> 2) (+ 32 jb + 8 s + 4 half) and head dims
+    // 32 db + 16 (a & 1) + 8 (gg & 1) + 4 (a >> 1) .. +3 with a = i & 3; the read hands lane
+    // (gg, a, c) the 4 keys of head dim 32 db + perm32(16 (gg & 1) + 4 a + c).
+    const int gg = lane >> 4, li = lane & 15, la = li & 3;
+    const int v_key = 16 * hh + (li >> 2);
+    const int v_dlo = 16 * (la & 1) + 8 * (gg & 1) + 4 * (la >> 1);   // within a 32-d block
+    const int v_sw = v_swz(v_key);                                     // same for key + 4n
 
     f32x16 o_acc[DB];
 #pragma unroll
@@ -249,12 +240,208 @@ __global__ __launch_bounds__(kThreads, 2) void sdpa_fwd_bf16_kernel(const FwdPar
     float m_ref = -INFINITY;     // reference max (log2 units) of this lane's row
     float l_part = 0.f;          // sum of p over this lane's keys, relative to m_ref
 
-    const float c_scale = p.scale_log2;
+    // The tile loop assumes a positive scale. A negative scale flips the sign of the Q
+    // fragment and of the scale together (exact in bf16, same products); a zero scale uses the
+    // smallest normal float instead (the exponents change by < 1e-35).
+    float c_scale = p.scale_log2;
+    if (c_scale < 0.f) {
+        c_scale = -c_scale;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            qf[ks] = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, qf[ks]) ^ 0x80008000u);
+    } else if (c_scale == 0.f) {
+        c_scale = 1.17549435e-38f;
+    }
+
+    // One key tile for this wave. MASKED: apply per-key masks (edge tiles only).
+    auto compute_tile = [&](auto masked_tag, int buf, int j0) {
+        constexpr bool MASKED = decltype(masked_tag)::value;
+        const uint16_t* kb = smem + buf * (2 * TILE);
+        const uint16_t* vb = kb + TILE;
+
+        // full bias: issue this tile's bias loads first (consumed after the MFMAs)
+        u32x4 fb[4];
+        const uint16_t* br = nullptr;
+        const int jl = j0 + 16 * hh;   // key of register 0 of this lane
+        bool fb_vec = false;
+        if constexpr (BIAS == BIAS_FULL) {
+            br = (const uint16_t*)p.bias +
+                 (((size_t)b * p.Hq + hq) * Sq + (row_ok ? my_i : 0)) * (size_t)Sk;
+            fb_vec = (j0 + kBN <= Sk) && ((Sk & 7) == 0);
+            if (fb_vec) {
+#pragma unroll
+                for (int jb = 0; jb < 2; ++jb) {
+                    fb[2 * jb] = *(const u32x4*)(br + jl + 32 * jb);
+                    fb[2 * jb + 1] = *(const u32x4*)(br + jl + 32 * jb + 8);
+                }
+            }
+        }
+
+        // ---- S^T = K . Q^T (two 32-key blocks) ----
+        f32x16 s0, s1;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) { s0[v] = 0.f; s1[v] = 0.f; }
+        // K fragments are read two k-steps ahead of their MFMAs; the scheduling barriers
+        // keep the compiler from hoisting all of them (64 VGPRs) to the top.
+        bf16x8 ka[2][2];
+        auto read_k = [&](int ks, bf16x8* dst) {
+            const int ch = ((2 * ks + hh) ^ k_sw) * 8;
+            dst[0] = *(const bf16x8*)(kb + krow * D + ch);
+            dst[1] = *(const bf16x8*)(kb + (krow + 32) * D + ch);
+        };
+        read_k(0, ka[0]);
+        read_k(1, ka[1]);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const bf16x8 a0 = ka[ks & 1][0], a1 = ka[ks & 1][1];
+            if (ks + 2 < KS) read_k(ks + 2, ka[ks & 1]);
+            s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[ks], s0, 0, 0, 0);
+            s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[ks], s1, 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        float x[32];    // x[16*jb + v] belongs to key jl + 32*jb + v
+#pragma unroll
+        for (int v = 0; v < 16; ++v) { x[v] = s0[v]; x[16 + v] = s1[v]; }
+
+        auto visible = [&](int e) {
+            const int j = jl + (e >> 4) * 32 + (e & 15);
+            bool vis = j < Sk;
+            if constexpr (MASK != MASK_NONE) vis = vis && (j <= my_pos);
+            if constexpr (MASK == MASK_SLIDING) vis = vis && (my_pos - j < p.window);
+            return vis;
+        };
+
+        // Per-element path: full bias, or T5 near the diagonal. Otherwise
+        // the bias is constant over the tile (none, or T5 far from the diagonal) and the scale
+        // is folded into the exponent's FMA after a max over the raw scores.
+        bool per_elem = (BIAS == BIAS_FULL);
+        bool t5_near = false;
+        float bconst = 0.f;
+        if constexpr (BIAS == BIAS_T5) {
+            const int rmin = j0 - pwb, rmax = j0 + kBN - 1 - pwa;
+            if (rmin >= kT5Sat) bconst = t5s[2 * kT5Sat];
+            else if (rmax <= -kT5Sat) bconst = t5s[0];
+            else t5_near = per_elem = true;
+        }
+
+        float mt;     // row max of the log2-domain scores of this tile
+        if (per_elem) {
+            if constexpr (BIAS == BIAS_T5) {
+                if (t5_near) {
+                    const int rel0 = jl - my_pos;
+#pragma unroll
+                    for (int e = 0; e < 32; ++e) {
+                        const int rel = rel0 + (e >> 4) * 32 + (e & 15);
+                        const int idx = min(max(rel, -kT5Sat), kT5Sat) + kT5Sat;
+                        x[e] = fmaf(x[e], c_scale, t5s[idx]);
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 32; ++e) x[e] = fmaf(x[e], c_scale, bconst);
+                }
+            } else if constexpr (BIAS == BIAS_FULL) {
+                if (fb_vec) {
+#pragma unroll
+                    for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+                        for (int c = 0; c < 4; ++c)
+#pragma unroll
+                            for (int hv = 0; hv < 2; ++hv) {
+                                const uint32_t lo = fb[2 * jb][c], hi = fb[2 * jb + 1][c];
+                                const int e0 = 16 * jb + 2 * c + hv;
+                                x[e0] = fmaf(x[e0], c_scale,
+                                             bf16_to_f32(hv ? (lo >> 16) : (lo & 0xffffu)) * kLog2e);
+                                x[e0 + 8] = fmaf(x[e0 + 8], c_scale,
+                                                 bf16_to_f32(hv ? (hi >> 16) : (hi & 0xffffu)) * kLog2e);
+                            }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 32; ++e) {
+                        const int j = jl + (e >> 4) * 32 + (e & 15);
+                        const float bv = (row_ok && j < Sk) ? bf16_to_f32(br[j]) : 0.f;
+                        x[e] = fmaf(x[e], c_scale, bv * kLog2e);
+                    }
+                }
+            }
+            if constexpr (MASKED) {
+#pragma unroll
+                for (int e = 0; e < 32; ++e) x[e] = visible(e) ? x[e] : -INFINITY;
+            }
+            mt = x[0];
+#pragma unroll
+            for (int e = 1; e < 32; ++e) mt = fmaxf(mt, x[e]);
+            mt = partner_max(mt);
+        } else {
+            // max over the raw scores (scale > 0); hidden keys stay -inf through the FMA below
+            if constexpr (MASKED) {
+#pragma unroll
+                for (int e = 0; e < 32; ++e) x[e] = visible(e) ? x[e] : -INFINITY;
+            }
+            float ext = x[0];
+#pragma unroll
+            for (int e = 1; e < 32; ++e) ext = fmaxf(ext, x[e]);
+            ext = partner_max(ext);
+            mt = (ext == -INFINITY) ? -INFINITY : fmaf(ext, c_scale, bconst);
+        }
+
+        // ---- online softmax (log2 domain, lazy rescale) ----
+        if (__builtin_amdgcn_ballot_w64(mt > m_ref + kRescaleSlack) != 0) {
+            const float m_new = fmaxf(m_ref, mt);
+            const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
+            m_ref = m_new;
+            l_part *= alpha;
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) o_acc[db][v] *= alpha;
+        }
+        const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
+        if (per_elem) {
+#pragma unroll
+            for (int e = 0; e < 32; ++e) x[e] = __builtin_amdgcn_exp2f(x[e] - m_use);
+        } else {
+            const float nb = bconst - m_use;
+#pragma unroll
+            for (int e = 0; e < 32; ++e) x[e] = __builtin_amdgcn_exp2f(fmaf(x[e], c_scale, nb));
+        }
+
+        // ---- O^T += V^T . P^T ----
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb) {
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                u32x4 pk;
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    pk[c] = pack_bf16x2(x[16 * jb + 8 * s + 2 * c], x[16 * jb + 8 * s + 2 * c + 1]);
+                    l_part += x[16 * jb + 8 * s + 2 * c] + x[16 * jb + 8 * s + 2 * c + 1];
+                }
+                const bf16x8 pb = __builtin_bit_cast(bf16x8, pk);
+                __builtin_amdgcn_sched_barrier(0);
+                const int key = v_key + 32 * jb + 8 * s;
+#pragma unroll
+                for (int db = 0; db < DB; ++db) {
+                    const int d = 32 * db + v_dlo;
+                    const int coff = (((d >> 3) ^ v_sw) << 3) + (d & 7);
+                    const s16x4 lo = lds_read_tr(vb + key * D + coff);
+                    const s16x4 hi = lds_read_tr(vb + (key + 4) * D + coff);
+                    u32x4 av;
+                    av[0] = __builtin_bit_cast(u32x2, lo)[0];
+                    av[1] = __builtin_bit_cast(u32x2, lo)[1];
+                    av[2] = __builtin_bit_cast(u32x2, hi)[0];
+                    av[3] = __builtin_bit_cast(u32x2, hi)[1];
+                    o_acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        __builtin_bit_cast(bf16x8, av), pb, o_acc[db], 0, 0, 0);
+                }
+            }
+        }
+    };
 
     load_tile(t_begin);
     store_tile(0);
     __syncthreads();
 
+#pragma unroll 1
     for (int t = t_begin; t < t_end; ++t) {
         const int buf = (t - t_begin) & 1;
         const bool has_next = t + 1 < t_end;
@@ -265,132 +452,15 @@ __global__ __launch_bounds__(kThreads, 2) void sdpa_fwd_bf16_kernel(const FwdPar
         bool skip = !wave_ok;
         if constexpr (MASK != MASK_NONE) skip = skip || (j0 > pwb);
         if constexpr (MASK == MASK_SLIDING) skip = skip || (j0 + kBN - 1 <= pwa - p.window);
+        bool need_mask = (j0 + kBN > Sk);
+        if constexpr (MASK != MASK_NONE) need_mask = need_mask || (j0 + kBN - 1 > pwa);
+        if constexpr (MASK == MASK_SLIDING) need_mask = need_mask || (j0 <= pwb - p.window);
 
         if (!skip) {
-            const uint16_t* kb = smem + buf * (K_TILE + V_TILE);
-            const uint16_t* vb = kb + K_TILE;
-
-            // ---- S^T = K . Q^T (two 32-key blocks) ----
-            f32x16 s0, s1;
-#pragma unroll
-            for (int v = 0; v < 16; ++v) { s0[v] = 0.f; s1[v] = 0.f; }
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const int ch = ((2 * ks + hh) ^ k_sw) * 8;
-                const bf16x8 a0 = *(const bf16x8*)(kb + krow * D + ch);
-                const bf16x8 a1 = *(const bf16x8*)(kb + (krow + 32) * D + ch);
-                s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[ks], s0, 0, 0, 0);
-                s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[ks], s1, 0, 0, 0);
-            }
-
-            // ---- scores in log2 units, bias, mask.  x[16*jb + v] is key j0 + 32jb + 16hh + v
-            float x[32];
-#pragma unroll
-            for (int v = 0; v < 16; ++v) { x[v] = s0[v]; x[16 + v] = s1[v]; }
-
-            const int jl = j0 + 16 * hh;   // key of x[0] in this lane
-            if constexpr (BIAS == BIAS_T5) {
-                const int rmin = j0 - pwb, rmax = j0 + kBN - 1 - pwa;
-                if (rmin >= kT5Sat || rmax <= -kT5Sat) {
-                    const float bc = t5s[rmin >= kT5Sat ? 2 * kT5Sat : 0];
-#pragma unroll
-                    for (int e = 0; e < 32; ++e) x[e] = fmaf(x[e], c_scale, bc);
-                } else {
-                    const int rel0 = jl - my_pos;
-#pragma unroll
-                    for (int e = 0; e < 32; ++e) {
-                        const int rel = rel0 + (e >> 4) * 32 + (e & 15);
-                        const int idx = min(max(rel, -kT5Sat), kT5Sat) + kT5Sat;
-                        x[e] = fmaf(x[e], c_scale, t5s[idx]);
-                    }
-                }
-            } else if constexpr (BIAS == BIAS_FULL) {
-                const uint16_t* br = (const uint16_t*)p.bias +
-                                     (((size_t)b * p.Hq + hq) * Sq + (row_ok ? my_i : 0)) * (size_t)Sk;
-                const bool vec_ok = row_ok && (j0 + kBN <= Sk) && ((Sk & 7) == 0);
-                if (vec_ok) {
-#pragma unroll
-                    for (int jb = 0; jb < 2; ++jb) {
-                        const u32x4 lo = *(const u32x4*)(br + jl + 32 * jb);
-                        const u32x4 hi = *(const u32x4*)(br + jl + 32 * jb + 8);
-#pragma unroll
-                        for (int c = 0; c < 4; ++c) {
-                            x[16 * jb + 2 * c] = fmaf(x[16 * jb + 2 * c], c_scale, bf16_to_f32(lo[c] & 0xffffu) * kLog2e);
-                            x[16 * jb + 2 * c + 1] = fmaf(x[16 * jb + 2 * c + 1], c_scale, bf16_to_f32(lo[c] >> 16) * kLog2e);
-                            x[16 * jb + 8 + 2 * c] = fmaf(x[16 * jb + 8 + 2 * c], c_scale, bf16_to_f32(hi[c] & 0xffffu) * kLog2e);
-                            x[16 * jb + 9 + 2 * c] = fmaf(x[16 * jb + 9 + 2 * c], c_scale, bf16_to_f32(hi[c] >> 16) * kLog2e);
-                        }
-                    }
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 32; ++e) {
-                        const int j = jl + (e >> 4) * 32 + (e & 15);
-                        const float bv = (row_ok && j < Sk) ? bf16_to_f32(br[j]) : 0.f;
-                        x[e] = fmaf(x[e], c_scale, bv * kLog2e);
-                    }
-                }
-            } else {
-#pragma unroll
-                for (int e = 0; e < 32; ++e) x[e] = x[e] * c_scale;
-            }
-
-            bool need_mask = (j0 + kBN > Sk);
-            if constexpr (MASK != MASK_NONE) need_mask = need_mask || (j0 + kBN - 1 > pwa);
-            if constexpr (MASK == MASK_SLIDING) need_mask = need_mask || (j0 <= pwb - p.window);
-            if (need_mask) {
-#pragma unroll
-                for (int e = 0; e < 32; ++e) {
-                    const int j = jl + (e >> 4) * 32 + (e & 15);
-                    bool vis = j < Sk;
-                    if constexpr (MASK != MASK_NONE) vis = vis && (j <= my_pos);
-                    if constexpr (MASK == MASK_SLIDING) vis = vis && (my_pos - j < p.window);
-                    x[e] = vis ? x[e] : -INFINITY;
-                }
-            }
-
-            // ---- online softmax (log2 domain, lazy rescale) ----
-            float mt = x[0];
-#pragma unroll
-            for (int e = 1; e < 32; ++e) mt = fmaxf(mt, x[e]);
-            mt = partner_max(mt);
-            if (__builtin_amdgcn_ballot_w64(mt > m_ref + kRescaleSlack) != 0) {
-                const float m_new = fmaxf(m_ref, mt);
-                const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
-                m_ref = m_new;
-                l_part *= alpha;
-#pragma unroll
-                for (int db = 0; db < DB; ++db)
-#pragma unroll
-                    for (int v = 0; v < 16; ++v) o_acc[db][v] *= alpha;
-            }
-            const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
-            float psum = 0.f;
-#pragma unroll
-            for (int e = 0; e < 32; ++e) {
-                x[e] = __builtin_amdgcn_exp2f(x[e] - m_use);
-                psum += x[e];
-            }
-            l_part += psum;
-
-            // ---- O^T += V^T . P^T ----
-#pragma unroll
-            for (int jb = 0; jb < 2; ++jb) {
-#pragma unroll
-                for (int s = 0; s < 2; ++s) {
-                    u32x4 pk;
-#pragma unroll
-                    for (int c = 0; c < 4; ++c)
-                        pk[c] = pack_bf16x2(x[16 * jb + 8 * s + 2 * c], x[16 * jb + 8 * s + 2 * c + 1]);
-                    const bf16x8 pb = __builtin_bit_cast(bf16x8, pk);
-                    const int vch = 4 * jb + 2 * hh + s;
-#pragma unroll
-                    for (int db = 0; db < DB; ++db) {
-                        const int d = 32 * db + vrow;
-                        const bf16x8 a = *(const bf16x8*)(vb + d * kBN + ((vch ^ v_swz(d)) * 8));
-                        o_acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, o_acc[db], 0, 0, 0);
-                    }
-                }
-            }
+            if (need_mask)
+                compute_tile(std::true_type{}, buf, j0);
+            else
+                compute_tile(std::false_type{}, buf, j0);
         }
 
         if (has_next) store_tile(buf ^ 1);
@@ -408,19 +478,19 @@ __global__ __launch_bounds__(kThreads, 2) void sdpa_fwd_bf16_kernel(const FwdPar
             if constexpr (OUT_F32) {
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
-                    u32x4 x;
+                    u32x4 xo;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) x[e] = __float_as_uint(o_acc[db][4 * c + e] * inv);
-                    *(u32x4*)(o + (d0 + 4 * c) * 4) = x;
+                    for (int e = 0; e < 4; ++e) xo[e] = __float_as_uint(o_acc[db][4 * c + e] * inv);
+                    *(u32x4*)(o + (d0 + 4 * c) * 4) = xo;
                 }
             } else {
 #pragma unroll
                 for (int c = 0; c < 2; ++c) {
-                    u32x4 x;
+                    u32x4 xo;
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        x[e] = pack_bf16x2(o_acc[db][8 * c + 2 * e] * inv, o_acc[db][8 * c + 2 * e + 1] * inv);
-                    *(u32x4*)(o + (d0 + 8 * c) * 2) = x;
+                        xo[e] = pack_bf16x2(o_acc[db][8 * c + 2 * e] * inv, o_acc[db][8 * c + 2 * e + 1] * inv);
+                    *(u32x4*)(o + (d0 + 8 * c) * 2) = xo;
                 }
             }
         }
