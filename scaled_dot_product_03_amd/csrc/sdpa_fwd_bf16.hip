@@ -42,8 +42,17 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-constexpr int kThreads = 256;
-constexpr int kBM = 128;        // query rows per workgroup
+#ifndef SDPA_PRIO
+#define SDPA_PRIO 1
+#endif
+#ifndef SDPA_VMAP
+#define SDPA_VMAP 1
+#endif
+#ifndef SDPA_WAVES
+#define SDPA_WAVES 8
+#endif
+constexpr int kThreads = 64 * SDPA_WAVES;
+constexpr int kBM = 32 * SDPA_WAVES;    // query rows per workgroup
 constexpr int kBN = 64;         // keys per tile
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -69,7 +78,13 @@ __device__ __forceinline__ int k_swz(int row) {
 }
 // V (read by ds_read_b64_tr_b16, a 16-lane group touching chunks {c, c+2} of 4 consecutive
 // rows): rows 4k..4k+3 go to XOR patterns {0, 1, 4, 5}.
-__device__ __forceinline__ int v_swz(int row) { return (row & 1) | ((row & 2) << 1); }
+__device__ __forceinline__ int v_swz(int row) {
+#if SDPA_VMAP
+    return 2 * (row & 3);
+#else
+    return (row & 1) | ((row & 2) << 1);
+#endif
+}
 
 __device__ __forceinline__ float partner_max(float x) {
     // max of this lane and lane l ^ 32 (the other half of the wave)
@@ -95,7 +110,7 @@ __device__ __forceinline__ s16x4 lds_read_tr(const uint16_t* p) {
 }
 
 template <int D, int MASK, int BIAS, bool OUT_F32>
-__global__ __launch_bounds__(kThreads, 2) void sdpa_fwd_bf16_kernel(const FwdParams p) {
+__global__ __launch_bounds__(kThreads, 8 / SDPA_WAVES) void sdpa_fwd_bf16_kernel(const FwdParams p) {
     constexpr int CH = D / 8;           // 16-byte chunks per K/V row
     constexpr int KS = D / 16;          // k-steps of Q.K^T
     constexpr int DB = D / 32;          // 32-wide d blocks of O^T
@@ -229,7 +244,14 @@ __global__ __launch_bounds__(kThreads, 2) void sdpa_fwd_bf16_kernel(const FwdPar
     // (gg, a, c) the 4 keys of head dim 32 db + perm32(16 (gg & 1) + 4 a + c).
     const int gg = lane >> 4, li = lane & 15, la = li & 3;
     const int v_key = 16 * hh + (li >> 2);
+#if SDPA_VMAP
+    // rows 0..15 of the O^T MFMA for block db hold head dims 16 db + sigma, rows 16..31 hold
+    // 16 (db + DB) + sigma: the two 16-lane halves of a transposing read touch opposite
+    // 128-byte halves of the LDS banks.
+    const int v_dlo = 16 * DB * (gg & 1) + 8 * (la & 1) + 4 * (la >> 1);
+#else
     const int v_dlo = 16 * (la & 1) + 8 * (gg & 1) + 4 * (la >> 1);   // within a 32-d block
+#endif
     const int v_sw = v_swz(v_key);                                     // same for key + 4n
 
     f32x16 o_acc[DB];
@@ -291,6 +313,9 @@ __global__ __launch_bounds__(kThreads, 2) void sdpa_fwd_bf16_kernel(const FwdPar
         };
         read_k(0, ka[0]);
         read_k(1, ka[1]);
+#if SDPA_PRIO
+        __builtin_amdgcn_s_setprio(1);
+#endif
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             const bf16x8 a0 = ka[ks & 1][0], a1 = ka[ks & 1][1];
@@ -299,6 +324,9 @@ __global__ __launch_bounds__(kThreads, 2) void sdpa_fwd_bf16_kernel(const FwdPar
             s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[ks], s1, 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
         }
+#if SDPA_PRIO
+        __builtin_amdgcn_s_setprio(0);
+#endif
         float x[32];    // x[16*jb + v] belongs to key jl + 32*jb + v
 #pragma unroll
         for (int v = 0; v < 16; ++v) { x[v] = s0[v]; x[16 + v] = s1[v]; }
@@ -406,6 +434,9 @@ __global__ __launch_bounds__(kThreads, 2) void sdpa_fwd_bf16_kernel(const FwdPar
         }
 
         // ---- O^T += V^T . P^T ----
+#if SDPA_PRIO
+        __builtin_amdgcn_s_setprio(1);
+#endif
 #pragma unroll
         for (int jb = 0; jb < 2; ++jb) {
 #pragma unroll
@@ -421,7 +452,11 @@ __global__ __launch_bounds__(kThreads, 2) void sdpa_fwd_bf16_kernel(const FwdPar
                 const int key = v_key + 32 * jb + 8 * s;
 #pragma unroll
                 for (int db = 0; db < DB; ++db) {
+#if SDPA_VMAP
+                    const int d = 16 * db + v_dlo;
+#else
                     const int d = 32 * db + v_dlo;
+#endif
                     const int coff = (((d >> 3) ^ v_sw) << 3) + (d & 7);
                     const s16x4 lo = lds_read_tr(vb + key * D + coff);
                     const s16x4 hi = lds_read_tr(vb + (key + 4) * D + coff);
@@ -435,6 +470,9 @@ __global__ __launch_bounds__(kThreads, 2) void sdpa_fwd_bf16_kernel(const FwdPar
                 }
             }
         }
+#if SDPA_PRIO
+        __builtin_amdgcn_s_setprio(0);
+#endif
     };
 
     load_tile(t_begin);
@@ -474,23 +512,28 @@ __global__ __launch_bounds__(kThreads, 2) void sdpa_fwd_bf16_kernel(const FwdPar
         char* o = out_ptr(my_i);
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-            const int d0 = db * 32 + hh * 16;
-            if constexpr (OUT_F32) {
+            // registers 8c .. 8c+7 of block db hold 8 consecutive head dims starting at d0[c]
+#if SDPA_VMAP
+            const int d0[2] = {16 * db + 8 * hh, 16 * (db + DB) + 8 * hh};
+#else
+            const int d0[2] = {32 * db + 16 * hh, 32 * db + 16 * hh + 8};
+#endif
 #pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    u32x4 xo;
+            for (int c = 0; c < 2; ++c) {
+                if constexpr (OUT_F32) {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) xo[e] = __float_as_uint(o_acc[db][4 * c + e] * inv);
-                    *(u32x4*)(o + (d0 + 4 * c) * 4) = xo;
-                }
-            } else {
+                    for (int hv = 0; hv < 2; ++hv) {
+                        u32x4 xo;
 #pragma unroll
-                for (int c = 0; c < 2; ++c) {
+                        for (int e = 0; e < 4; ++e) xo[e] = __float_as_uint(o_acc[db][8 * c + 4 * hv + e] * inv);
+                        *(u32x4*)(o + (d0[c] + 4 * hv) * 4) = xo;
+                    }
+                } else {
                     u32x4 xo;
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
                         xo[e] = pack_bf16x2(o_acc[db][8 * c + 2 * e] * inv, o_acc[db][8 * c + 2 * e + 1] * inv);
-                    *(u32x4*)(o + (d0 + 8 * c) * 2) = xo;
+                    *(u32x4*)(o + d0[c] * 2) = xo;
                 }
             }
         }
