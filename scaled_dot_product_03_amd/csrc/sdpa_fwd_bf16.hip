@@ -48,6 +48,12 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 #ifndef SDPA_VMAP
 #define SDPA_VMAP 1
 #endif
+#ifndef SDPA_DMA
+#define SDPA_DMA 1
+#endif
+#ifndef SDPA_STAGES
+#define SDPA_STAGES 2
+#endif
 #ifndef SDPA_WAVES
 #define SDPA_WAVES 8
 #endif
@@ -118,7 +124,8 @@ __global__ __launch_bounds__(kThreads, 8 / SDPA_WAVES) void sdpa_fwd_bf16_kernel
     constexpr int NST = kBN * CH / kThreads;   // staged 16-byte chunks per thread per tensor
     static_assert(NST * kThreads == kBN * CH, "staging");
 
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * 2 * TILE];
+    constexpr int NBUF = SDPA_DMA ? SDPA_STAGES : 2;   // K/V ring depth
+    __shared__ __attribute__((aligned(16))) uint16_t smem[NBUF * 2 * TILE];
     __shared__ float t5s[BIAS == BIAS_T5 ? 2 * kT5Sat + 1 : 1];
 
     const int tid = threadIdx.x;
@@ -223,6 +230,42 @@ __global__ __launch_bounds__(kThreads, 8 / SDPA_WAVES) void sdpa_fwd_bf16_kernel
             }
         }
     };
+    // LDS-DMA staging: each wave issues 1 KB global_load_lds_dwordx4 transfers (lane i lands at
+    // M0 + 16 i). Lane i of a transfer fetches the global chunk whose swizzled LDS slot is
+    // 16 i, so the XOR layout is produced on the global side. Issued through inline asm: the
+    // compiler would otherwise wait for every outstanding DMA before any LDS read. The waits
+    // are explicit: vmcnt(0) before the barrier that publishes the tile.
+    constexpr int ROWS_PER_XFER = 1024 / (D * 2);              // rows of one 1 KB transfer
+    constexpr int XFERS = (kBN * D * 2) / 1024;                // per tensor per tile
+    constexpr int XPW = XFERS / (kThreads / 64);               // per wave per tensor
+    static_assert(XPW * (kThreads / 64) == XFERS, "dma split");
+    const uint32_t lds_base = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint16_t*)smem);
+    auto dma_tile = [&](int t, int buf) {
+        const int j0 = t * kBN;
+#pragma unroll
+        for (int n = 0; n < XPW; ++n) {
+            const int xi = wave * XPW + n;                      // transfer index in the tile
+            const int row = xi * ROWS_PER_XFER + lane / CH;     // tile row this lane fills
+            const int pc = lane % CH;                           // physical chunk in the row
+            const int j = min(j0 + row, Sk - 1);
+            const uint16_t* ksrc = kg + (size_t)j * kv_row + ((pc ^ k_swz<D>(row)) * 8);
+            const uint16_t* vsrc = vg + (size_t)j * kv_row + ((pc ^ v_swz(row)) * 8);
+            const uint32_t kdst = __builtin_amdgcn_readfirstlane(
+                lds_base + (uint32_t)((buf * 2 * TILE) * 2 + xi * 1024));
+            const uint32_t vdst = kdst + (uint32_t)(TILE * 2);
+            asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                         :: "v"(ksrc), "s"(kdst) : "memory");
+            asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                         :: "v"(vsrc), "s"(vdst) : "memory");
+        }
+    };
+    auto dma_wait = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
+    // wait until at most this wave's transfers of one tile are still in flight
+    auto dma_wait_one_behind = [&]() {
+        static_assert(2 * XPW <= 15, "vmcnt field");
+        asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * XPW) : "memory");
+    };
+
     auto store_tile = [&](int buf) {
         uint16_t* kb = smem + buf * (2 * TILE);
         uint16_t* vb = kb + TILE;
@@ -475,15 +518,33 @@ __global__ __launch_bounds__(kThreads, 8 / SDPA_WAVES) void sdpa_fwd_bf16_kernel
 #endif
     };
 
+#if SDPA_DMA
+    dma_tile(t_begin, 0);
+    if (NBUF > 2 && t_begin + 1 < t_end) {
+        dma_tile(t_begin + 1, 1);
+        dma_wait_one_behind();
+    } else {
+        dma_wait();
+    }
+#else
     load_tile(t_begin);
     store_tile(0);
+#endif
     __syncthreads();
 
 #pragma unroll 1
     for (int t = t_begin; t < t_end; ++t) {
-        const int buf = (t - t_begin) & 1;
+        const int buf = (t - t_begin) % NBUF;
         const bool has_next = t + 1 < t_end;
+#if SDPA_DMA
+        if (NBUF > 2) {
+            if (t + 2 < t_end) dma_tile(t + 2, (t + 2 - t_begin) % NBUF);
+        } else {
+            if (has_next) dma_tile(t + 1, buf ^ 1);
+        }
+#else
         if (has_next) load_tile(t + 1);
+#endif
 
         const int j0 = t * kBN;
         // wave-level classification of this tile
@@ -501,7 +562,16 @@ __global__ __launch_bounds__(kThreads, 8 / SDPA_WAVES) void sdpa_fwd_bf16_kernel
                 compute_tile(std::false_type{}, buf, j0);
         }
 
+#if SDPA_DMA
+        if (NBUF > 2) {
+            if (t + 2 < t_end) dma_wait_one_behind();
+            else if (has_next) dma_wait();
+        } else {
+            if (has_next) dma_wait();
+        }
+#else
         if (has_next) store_tile(buf ^ 1);
+#endif
         __syncthreads();
     }
 
