@@ -9,10 +9,11 @@ D=128, bf16, sliding window 4096 (= seqlen, i.e. exactly causal).
 
 Prints ONE JSON line on stdout. `value` is effective TFLOP/s: 4*D flop per visible
 (query, key) pair (Q.K^T and P.V), masked pairs excluded, exps not counted. Timing: W untimed
-warmup launches, then K launches bracketed by device synchronisation, each launch also
-bracketed by HIP events on the stream it runs on (the median-of-repeats-with-device-sync
-method of the "jax-gpu-05-attention-gpu" codelab, section 8). The CPU baseline is the fp64
-oracle timed on a bounded sample of the same workload on this host's cores.
+warmup launches, then exactly K launches bracketed by device synchronisation (wall clock, plus
+one HIP event pair on the launch stream); then K more launches each bracketed by HIP events on
+that stream give the per-launch kernel duration used for the roofline (the
+repeat-with-device-sync method of the "jax-gpu-05-attention-gpu" codelab, section 8). The CPU
+baseline is the fp64 oracle timed on the same workload on this host's cores.
 
 --sweep additionally times every other workload and prints one JSON line per workload on
 stderr.
@@ -95,20 +96,33 @@ def time_workload(sdpa, wl: si.Workload, steps: int, warmup: int):
     for _ in range(warmup):
         launch()
     torch.cuda.synchronize()
+    # timed region: exactly `steps` launches between two device synchronisations, plus one
+    # event pair on the launch stream around them
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(steps):
+        launch()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    region_ms = ev0.elapsed_time(ev1)
+    # per-launch durations (separate pass, events bracketing each launch on the same stream)
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    t0 = time.perf_counter()
     for i in range(steps):
         starts[i].record(stream)
         launch()
         ends[i].record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     ev = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
     del q, k, v, bias, out, lse
     torch.cuda.empty_cache()
-    return dict(ms_per_step=1e3 * wall / steps, kernel_ms_avg=float(ev.mean()),
-                kernel_ms_median=float(np.median(ev)), kernel_ms_min=float(ev.min()))
+    return dict(ms_per_step=1e3 * wall / steps, region_ms_per_step=region_ms / steps,
+                kernel_ms_avg=float(ev.mean()), kernel_ms_median=float(np.median(ev)),
+                kernel_ms_min=float(ev.min()))
 
 
 def cpu_baseline(wl: si.Workload, budget_s: float = 12.0):
@@ -171,8 +185,8 @@ def report(wl: si.Workload, t: dict):
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="c2", choices=sorted(si.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", action="store_true")
@@ -226,6 +240,7 @@ def main(argv=None):
         "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "config": {**wl.describe(), "effective_gflop": round(flops / 1e9, 2),
                    "kernel_ms_median": round(t["kernel_ms_median"], 4),
+                   "event_ms_per_step": round(t["region_ms_per_step"], 4),
                    "hbm_gbs_algorithmic": round(si.algorithmic_bytes(wl) /
                                                 (t["kernel_ms_avg"] * 1e-3) / 1e9, 1)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,

@@ -370,15 +370,52 @@ __global__ __launch_bounds__(kThreads, 8 / SDPA_WAVES) void sdpa_fwd_bf16_kernel
 #if SDPA_PRIO
         __builtin_amdgcn_s_setprio(0);
 #endif
+        // V^T fragments of key group g = (jb, s): 4 keys from each of two transposing reads
+        bf16x8 vfr[2][DB];
+        auto read_v = [&](int g, bf16x8* dst) {
+            const int key = v_key + 32 * (g >> 1) + 8 * (g & 1);
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+#if SDPA_VMAP
+                const int d = 16 * db + v_dlo;
+#else
+                const int d = 32 * db + v_dlo;
+#endif
+                const int coff = (((d >> 3) ^ v_sw) << 3) + (d & 7);
+                const s16x4 lo = lds_read_tr(vb + key * D + coff);
+                const s16x4 hi = lds_read_tr(vb + (key + 4) * D + coff);
+                u32x4 av;
+                av[0] = __builtin_bit_cast(u32x2, lo)[0];
+                av[1] = __builtin_bit_cast(u32x2, lo)[1];
+                av[2] = __builtin_bit_cast(u32x2, hi)[0];
+                av[3] = __builtin_bit_cast(u32x2, hi)[1];
+                dst[db] = __builtin_bit_cast(bf16x8, av);
+            }
+        };
+        read_v(0, vfr[0]);
         float x[32];    // x[16*jb + v] belongs to key jl + 32*jb + v
 #pragma unroll
         for (int v = 0; v < 16; ++v) { x[v] = s0[v]; x[16 + v] = s1[v]; }
 
+        // Visible keys of this lane's row form one interval [lo, hi]; register e of key block
+        // jb holds key jl + 32 jb + (e & 15), so visibility is a compare of the compile-time
+        // index e & 15 against per-lane bounds.
+        int vis_hi[2], vis_lo[2];
+        if constexpr (MASKED) {
+            int hi = Sk - 1;
+            if constexpr (MASK != MASK_NONE) hi = min(hi, my_pos);
+            int lo = 0;
+            if constexpr (MASK == MASK_SLIDING) lo = max(0, my_pos - p.window + 1);
+#pragma unroll
+            for (int jb = 0; jb < 2; ++jb) {
+                vis_hi[jb] = hi - (jl + 32 * jb);
+                vis_lo[jb] = lo - (jl + 32 * jb);
+            }
+        }
         auto visible = [&](int e) {
-            const int j = jl + (e >> 4) * 32 + (e & 15);
-            bool vis = j < Sk;
-            if constexpr (MASK != MASK_NONE) vis = vis && (j <= my_pos);
-            if constexpr (MASK == MASK_SLIDING) vis = vis && (my_pos - j < p.window);
+            const int v = e & 15, jb = e >> 4;
+            bool vis = v <= vis_hi[jb];
+            if constexpr (MASK == MASK_SLIDING) vis = vis && (v >= vis_lo[jb]);
             return vis;
         };
 
@@ -477,41 +514,26 @@ __global__ __launch_bounds__(kThreads, 8 / SDPA_WAVES) void sdpa_fwd_bf16_kernel
         }
 
         // ---- O^T += V^T . P^T ----
+        // Four key groups g = (jb, s) of 8 keys per lane half; the V^T fragments of group g+1
+        // are read while the MFMAs of group g run (group 0 was read before the softmax).
 #if SDPA_PRIO
         __builtin_amdgcn_s_setprio(1);
 #endif
 #pragma unroll
-        for (int jb = 0; jb < 2; ++jb) {
+        for (int g = 0; g < 4; ++g) {
+            const int jb = g >> 1, s = g & 1;
+            u32x4 pk;
 #pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                u32x4 pk;
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    pk[c] = pack_bf16x2(x[16 * jb + 8 * s + 2 * c], x[16 * jb + 8 * s + 2 * c + 1]);
-                    l_part += x[16 * jb + 8 * s + 2 * c] + x[16 * jb + 8 * s + 2 * c + 1];
-                }
-                const bf16x8 pb = __builtin_bit_cast(bf16x8, pk);
-                __builtin_amdgcn_sched_barrier(0);
-                const int key = v_key + 32 * jb + 8 * s;
-#pragma unroll
-                for (int db = 0; db < DB; ++db) {
-#if SDPA_VMAP
-                    const int d = 16 * db + v_dlo;
-#else
-                    const int d = 32 * db + v_dlo;
-#endif
-                    const int coff = (((d >> 3) ^ v_sw) << 3) + (d & 7);
-                    const s16x4 lo = lds_read_tr(vb + key * D + coff);
-                    const s16x4 hi = lds_read_tr(vb + (key + 4) * D + coff);
-                    u32x4 av;
-                    av[0] = __builtin_bit_cast(u32x2, lo)[0];
-                    av[1] = __builtin_bit_cast(u32x2, lo)[1];
-                    av[2] = __builtin_bit_cast(u32x2, hi)[0];
-                    av[3] = __builtin_bit_cast(u32x2, hi)[1];
-                    o_acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        __builtin_bit_cast(bf16x8, av), pb, o_acc[db], 0, 0, 0);
-                }
+            for (int c = 0; c < 4; ++c) {
+                pk[c] = pack_bf16x2(x[16 * jb + 8 * s + 2 * c], x[16 * jb + 8 * s + 2 * c + 1]);
+                l_part += x[16 * jb + 8 * s + 2 * c] + x[16 * jb + 8 * s + 2 * c + 1];
             }
+            const bf16x8 pb = __builtin_bit_cast(bf16x8, pk);
+            if (g + 1 < 4) read_v(g + 1, vfr[(g + 1) & 1]);
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+                o_acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfr[g & 1][db], pb, o_acc[db], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
         }
 #if SDPA_PRIO
         __builtin_amdgcn_s_setprio(0);
