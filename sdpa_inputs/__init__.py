@@ -50,9 +50,12 @@ class Workload:
     seed: int = 0         # base seed; q = seed, k = seed+1, v = seed+2, t5 table = seed+3, bias = seed+4
     kv_seed: Optional[int] = None   # overrides the k/v seed base (k = kv_seed+1, v = kv_seed+2)
     bias_std: float = 0.5
+    scale_override: Optional[float] = None   # softmax scale; default 1/sqrt(D)
 
     @property
     def scale(self) -> float:
+        if self.scale_override is not None:
+            return float(np.float32(self.scale_override))
         return float(np.float32(1.0 / np.sqrt(self.D)))
 
     def replace(self, **kw) -> "Workload":

@@ -46,6 +46,24 @@ SMALL_BF16 = [
         bias_kind=si.BIAS_T5, mask_kind=si.MASK_NONE),
     si.small(W["c2"], B=1, Hq=2, Hkv=2, Sq=1, Sk=1, name_suffix="single"),
     si.small(W["c2"], B=1, Hq=2, Hkv=1, Sq=5, Sk=3, window=1, name_suffix="window1"),
+    # bidirectional D = 128 without bias; T5 and sliding with Sq != Sk
+    si.small(W["c2"], B=2, Hq=4, Hkv=2, Sq=300, Sk=300, name_suffix="none_d128").replace(
+        mask_kind=si.MASK_NONE),
+    si.small(W["c4t5"], B=1, Hq=3, Hkv=3, Sq=150, Sk=400, name_suffix="t5_q150_k400"),
+    si.small(W["c2"], B=1, Hq=4, Hkv=1, Sq=200, Sk=520, window=150, name_suffix="q200_k520_w150"),
+    # negative and zero softmax scale (sign flip of the Q fragment; smallest normal float)
+    si.small(W["c2"], B=1, Hq=4, Hkv=2, Sq=260, Sk=260, window=100,
+             name_suffix="neg_scale").replace(scale_override=-0.07),
+    si.small(W["c3c"], B=1, Hq=2, Hkv=1, Sq=200, Sk=200, name_suffix="neg_scale").replace(
+        scale_override=-0.2),
+    si.small(W["c4t5"], B=1, Hq=2, Hkv=2, Sq=140, Sk=140, name_suffix="neg_scale").replace(
+        scale_override=-0.1),
+    si.small(W["c4full"], B=1, Hq=2, Hkv=2, Sq=136, Sk=136, name_suffix="neg_scale").replace(
+        scale_override=-0.1),
+    si.small(W["c3c"], B=1, Hq=2, Hkv=1, Sq=200, Sk=200, name_suffix="zero_scale").replace(
+        scale_override=0.0),
+    si.small(W["c4t5"], B=1, Hq=2, Hkv=2, Sq=140, Sk=140, name_suffix="zero_scale").replace(
+        scale_override=0.0),
 ]
 
 SMALL_F32 = [
@@ -57,6 +75,8 @@ SMALL_F32 = [
     W["c1"].replace(name="c1_full_causal_q_lt_k", B=2, Hq=2, Hkv=1, Sq=90, Sk=170,
                     bias_kind=si.BIAS_FULL),
     W["c1"].replace(name="c1_q_gt_k", Sq=170, Sk=90),
+    W["c1"].replace(name="c1_neg_scale_none", mask_kind=si.MASK_NONE, scale_override=-0.1),
+    W["c1"].replace(name="c1_zero_scale", scale_override=0.0),
 ]
 
 
