@@ -51,9 +51,6 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 #ifndef SDPA_DMA
 #define SDPA_DMA 1
 #endif
-#ifndef SDPA_STAGES
-#define SDPA_STAGES 2
-#endif
 #ifndef SDPA_WAVES
 #define SDPA_WAVES 8
 #endif
@@ -124,8 +121,14 @@ __global__ __launch_bounds__(kThreads, 8 / SDPA_WAVES) void sdpa_fwd_bf16_kernel
     constexpr int NST = kBN * CH / kThreads;   // staged 16-byte chunks per thread per tensor
     static_assert(NST * kThreads == kBN * CH, "staging");
 
-    constexpr int NBUF = SDPA_DMA ? SDPA_STAGES : 2;   // K/V ring depth
-    __shared__ __attribute__((aligned(16))) uint16_t smem[NBUF * 2 * TILE];
+    // Ring depth: 3 for the full-bias D = 64 kernel (the bias stream needs the latency
+    // cover; 144 KB of LDS), 2 otherwise. Each stage holds K, V and, for a full bias, the
+    // [256 rows][64 keys] bias tile.
+    constexpr bool FB_LDS = SDPA_DMA && BIAS == BIAS_FULL;
+    constexpr int NBUF = (FB_LDS && D == 64) ? 3 : 2;
+    constexpr int BTILE = FB_LDS ? kBM * kBN : 0;      // bf16 elements of a bias buffer
+    constexpr int STAGE = 2 * TILE + BTILE;
+    __shared__ __attribute__((aligned(16))) uint16_t smem[NBUF * STAGE];
     __shared__ float t5s[BIAS == BIAS_T5 ? 2 * kT5Sat + 1 : 1];
 
     const int tid = threadIdx.x;
@@ -240,6 +243,11 @@ __global__ __launch_bounds__(kThreads, 8 / SDPA_WAVES) void sdpa_fwd_bf16_kernel
     constexpr int XPW = XFERS / (kThreads / 64);               // per wave per tensor
     static_assert(XPW * (kThreads / 64) == XFERS, "dma split");
     const uint32_t lds_base = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint16_t*)smem);
+    // full bias through the LDS ring when rows split into whole 16-byte chunks
+    constexpr int XPB = FB_LDS ? (kBM * kBN * 2 / 1024) / (kThreads / 64) : 0;
+    const bool fb_dma = FB_LDS && ((Sk & 7) == 0);
+    const uint16_t* fbg = (BIAS == BIAS_FULL)
+        ? (const uint16_t*)p.bias + ((size_t)b * p.Hq + hq) * (size_t)Sq * Sk : nullptr;
     auto dma_tile = [&](int t, int buf) {
         const int j0 = t * kBN;
 #pragma unroll
@@ -251,23 +259,45 @@ __global__ __launch_bounds__(kThreads, 8 / SDPA_WAVES) void sdpa_fwd_bf16_kernel
             const uint16_t* ksrc = kg + (size_t)j * kv_row + ((pc ^ k_swz<D>(row)) * 8);
             const uint16_t* vsrc = vg + (size_t)j * kv_row + ((pc ^ v_swz(row)) * 8);
             const uint32_t kdst = __builtin_amdgcn_readfirstlane(
-                lds_base + (uint32_t)((buf * 2 * TILE) * 2 + xi * 1024));
+                lds_base + (uint32_t)((buf * STAGE) * 2 + xi * 1024));
             const uint32_t vdst = kdst + (uint32_t)(TILE * 2);
             asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
                          :: "v"(ksrc), "s"(kdst) : "memory");
             asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
                          :: "v"(vsrc), "s"(vdst) : "memory");
         }
+        if constexpr (FB_LDS) {
+            if (fb_dma) {
+                // bias tile [kBM rows][kBN keys], 128-byte rows, chunk swizzle (row >> 1) & 7;
+                // keys past the end of a partial last tile re-read the last whole chunk
+                const int nchunk = min(kBN, Sk - j0) / 8;
+#pragma unroll
+                for (int n = 0; n < XPB; ++n) {
+                    const int xi = wave * XPB + n;
+                    const int row = xi * 8 + (lane >> 3);
+                    const int c = min((lane & 7) ^ ((row >> 1) & 7), nchunk - 1);
+                    const uint16_t* bsrc = fbg + (size_t)min(q0 + row, Sq - 1) * Sk + j0 + 8 * c;
+                    const uint32_t bdst = __builtin_amdgcn_readfirstlane(
+                        lds_base + (uint32_t)((buf * STAGE + 2 * TILE) * 2 + xi * 1024));
+                    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                                 :: "v"(bsrc), "s"(bdst) : "memory");
+                }
+            }
+        }
     };
     auto dma_wait = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
     // wait until at most this wave's transfers of one tile are still in flight
+    // wait until at most one tile's transfers of this wave are still in flight
     auto dma_wait_one_behind = [&]() {
-        static_assert(2 * XPW <= 15, "vmcnt field");
-        asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * XPW) : "memory");
+        static_assert(2 * XPW + XPB <= 63, "vmcnt field");
+        if (fb_dma)
+            asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * XPW + XPB) : "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * XPW) : "memory");
     };
 
     auto store_tile = [&](int buf) {
-        uint16_t* kb = smem + buf * (2 * TILE);
+        uint16_t* kb = smem + buf * STAGE;
         uint16_t* vb = kb + TILE;
 #pragma unroll
         for (int i = 0; i < NST; ++i) {
@@ -321,7 +351,7 @@ __global__ __launch_bounds__(kThreads, 8 / SDPA_WAVES) void sdpa_fwd_bf16_kernel
     // One key tile for this wave. MASKED: apply per-key masks (edge tiles only).
     auto compute_tile = [&](auto masked_tag, int buf, int j0) {
         constexpr bool MASKED = decltype(masked_tag)::value;
-        const uint16_t* kb = smem + buf * (2 * TILE);
+        const uint16_t* kb = smem + buf * STAGE;
         const uint16_t* vb = kb + TILE;
 
         // full bias: issue this tile's bias loads first (consumed after the MFMAs)
@@ -333,7 +363,19 @@ __global__ __launch_bounds__(kThreads, 8 / SDPA_WAVES) void sdpa_fwd_bf16_kernel
             br = (const uint16_t*)p.bias +
                  (((size_t)b * p.Hq + hq) * Sq + (row_ok ? my_i : 0)) * (size_t)Sk;
             fb_vec = (j0 + kBN <= Sk) && ((Sk & 7) == 0);
-            if (fb_vec) {
+            if (fb_dma) {
+                // this tile's bias rows from the LDS ring: row (wave*32 + r32), chunks
+                // 4 jb + 2 hh + {0, 1}
+                fb_vec = true;
+                const int ir = wave * 32 + r32;
+                const uint16_t* bt = smem + buf * STAGE + 2 * TILE + ir * kBN;
+                const int sw = (ir >> 1) & 7;
+#pragma unroll
+                for (int jb = 0; jb < 2; ++jb) {
+                    fb[2 * jb] = *(const u32x4*)(bt + (((4 * jb + 2 * hh) ^ sw) * 8));
+                    fb[2 * jb + 1] = *(const u32x4*)(bt + (((4 * jb + 2 * hh + 1) ^ sw) * 8));
+                }
+            } else if (fb_vec) {
 #pragma unroll
                 for (int jb = 0; jb < 2; ++jb) {
                     fb[2 * jb] = *(const u32x4*)(br + jl + 32 * jb);
@@ -540,62 +582,82 @@ __global__ __launch_bounds__(kThreads, 8 / SDPA_WAVES) void sdpa_fwd_bf16_kernel
 #endif
     };
 
-#if SDPA_DMA
-    dma_tile(t_begin, 0);
-    if (NBUF > 2 && t_begin + 1 < t_end) {
-        dma_tile(t_begin + 1, 1);
-        dma_wait_one_behind();
-    } else {
-        dma_wait();
-    }
-#else
-    load_tile(t_begin);
-    store_tile(0);
-#endif
-    __syncthreads();
-
-#pragma unroll 1
-    for (int t = t_begin; t < t_end; ++t) {
-        const int buf = (t - t_begin) % NBUF;
-        const bool has_next = t + 1 < t_end;
-#if SDPA_DMA
-        if (NBUF > 2) {
-            if (t + 2 < t_end) dma_tile(t + 2, (t + 2 - t_begin) % NBUF);
-        } else {
-            if (has_next) dma_tile(t + 1, buf ^ 1);
-        }
-#else
-        if (has_next) load_tile(t + 1);
-#endif
-
+    // wave-level classification of tile t and its computation on ring buffer `buf`
+    auto run_tile = [&](int t, int buf) {
         const int j0 = t * kBN;
-        // wave-level classification of this tile
         bool skip = !wave_ok;
         if constexpr (MASK != MASK_NONE) skip = skip || (j0 > pwb);
         if constexpr (MASK == MASK_SLIDING) skip = skip || (j0 + kBN - 1 <= pwa - p.window);
         bool need_mask = (j0 + kBN > Sk);
         if constexpr (MASK != MASK_NONE) need_mask = need_mask || (j0 + kBN - 1 > pwa);
         if constexpr (MASK == MASK_SLIDING) need_mask = need_mask || (j0 <= pwb - p.window);
-
         if (!skip) {
             if (need_mask)
                 compute_tile(std::true_type{}, buf, j0);
             else
                 compute_tile(std::false_type{}, buf, j0);
         }
+    };
 
 #if SDPA_DMA
-        if (NBUF > 2) {
-            if (t + 2 < t_end) dma_wait_one_behind();
-            else if (has_next) dma_wait();
-        } else {
+    if constexpr (NBUF == 2) {
+        // tile t+1 is fetched while tile t is computed
+        dma_tile(t_begin, 0);
+        dma_wait();
+        __syncthreads();
+#pragma unroll 1
+        for (int t = t_begin; t < t_end; ++t) {
+            const int buf = (t - t_begin) & 1;
+            const bool has_next = t + 1 < t_end;
+            if (has_next) dma_tile(t + 1, buf ^ 1);
+            run_tile(t, buf);
             if (has_next) dma_wait();
+            __syncthreads();
         }
+    } else {
+        // tiles t+1 .. t+NBUF-1 in flight; the wait before each barrier leaves only the
+        // transfers of tiles beyond the next one outstanding
+        int fetch_t = t_begin, fetch_buf = 0;
+        for (int n = 0; n < NBUF - 1 && fetch_t < t_end; ++n) {
+            dma_tile(fetch_t, fetch_buf);
+            ++fetch_t;
+            fetch_buf = (fetch_buf + 1 == NBUF) ? 0 : fetch_buf + 1;
+        }
+        if (fetch_t > t_begin + 1) dma_wait_one_behind();
+        else dma_wait();
+        __syncthreads();
+        int buf = 0;
+#pragma unroll 1
+        for (int t = t_begin; t < t_end; ++t) {
+            const bool has_next = t + 1 < t_end;
+            if (fetch_t < t_end) {
+                dma_tile(fetch_t, fetch_buf);
+                ++fetch_t;
+                fetch_buf = (fetch_buf + 1 == NBUF) ? 0 : fetch_buf + 1;
+            }
+            run_tile(t, buf);
+            if (has_next) {
+                if (fetch_t > t + 2) dma_wait_one_behind();   // tile t+2 is also in flight
+                else dma_wait();
+            }
+            buf = (buf + 1 == NBUF) ? 0 : buf + 1;
+            __syncthreads();
+        }
+    }
 #else
+    load_tile(t_begin);
+    store_tile(0);
+    __syncthreads();
+#pragma unroll 1
+    for (int t = t_begin; t < t_end; ++t) {
+        const int buf = (t - t_begin) & 1;
+        const bool has_next = t + 1 < t_end;
+        if (has_next) load_tile(t + 1);
+        run_tile(t, buf);
         if (has_next) store_tile(buf ^ 1);
-#endif
         __syncthreads();
     }
+#endif
 
     // ---- epilogue: O = O_acc / l, LSE = ln2 * (m + log2 l) ---------------------------------
     const float l_tot = partner_sum(l_part);
