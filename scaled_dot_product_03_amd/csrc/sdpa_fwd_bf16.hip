@@ -46,7 +46,7 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 
-constexpr int kWaves = 8;
+constexpr int kWaves = 8;           // one workgroup per CU, two waves per SIMD
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBM = 32 * kWaves;    // query rows per workgroup
 constexpr int kBN = 64;             // keys per tile
@@ -117,14 +117,20 @@ __global__ __launch_bounds__(kThreads, 1) void sdpa_fwd_bf16_kernel(const FwdPar
     // LDS: K ring (NKS slots, each a K tile followed, for a full bias, by the [256 rows][64 keys]
     // bias tile of the same keys), then the V ring (NVS slots).
     constexpr bool FB = BIAS == BIAS_FULL;
-    constexpr int NKS = 2;
+    // A full bias streams from HBM with the K tiles: for D = 64 the K ring is 3 deep (K tiles
+    // are fetched two iterations before use), which the LDS holds; otherwise 2 deep.
+    constexpr int NKS = (FB && D == 64) ? 3 : 2;
     constexpr int NVS = 2;
     constexpr int BTILE = FB ? kBM * kBN : 0;
     constexpr int KSTAGE = TILE + BTILE;
     constexpr int VRING = NKS * KSTAGE;
     static_assert((NKS * KSTAGE + NVS * TILE) * 2 <= 160 * 1024, "LDS");
     __shared__ __attribute__((aligned(16))) uint16_t smem[NKS * KSTAGE + NVS * TILE];
-    __shared__ float t5s[BIAS == BIAS_T5 ? 2 * kT5Sat + 1 : 1];
+    // T5 bias by relative position rel = key - query, log2 units, at t5s[kT5Pad + rel]. Padded
+    // so that every rel of a tile near the diagonal indexes it without clamping: such a tile has
+    // j0 - pwb < kT5Sat and j0 + 63 - pwa > -kT5Sat, and pwb - pwa <= 31, so |rel| < kT5Pad.
+    constexpr int kT5Pad = kT5Sat + kBN + 31;
+    __shared__ float t5s[BIAS == BIAS_T5 ? 2 * kT5Pad + 1 : 1];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -183,7 +189,7 @@ __global__ __launch_bounds__(kThreads, 1) void sdpa_fwd_bf16_kernel(const FwdPar
     // ---- T5: expanded bias by relative position, already in log2 units --------------------
     if constexpr (BIAS == BIAS_T5) {
         const float* tbl = (const float*)p.bias + (size_t)hq * kT5Buckets;
-        if (tid < 2 * kT5Sat + 1) t5s[tid] = tbl[t5_bucket(tid - kT5Sat)] * kLog2e;
+        for (int i = tid; i < 2 * kT5Pad + 1; i += kThreads) t5s[i] = tbl[t5_bucket(i - kT5Pad)] * kLog2e;
     }
 
     // ---- Q fragment: lane holds row my_i, dims 16ks + 8hh .. +7 ----------------------------
@@ -209,6 +215,8 @@ __global__ __launch_bounds__(kThreads, 1) void sdpa_fwd_bf16_kernel(const FwdPar
     } else if (c_scale == 0.f) {
         c_scale = 1.17549435e-38f;
     }
+    // the same positive scale in natural-log units (a full bias is added in those units)
+    const float n_scale = (p.scale == 0.f) ? 1.17549435e-38f : fabsf(p.scale);
 
     // ---- LDS-DMA staging -------------------------------------------------------------------
     // Each wave issues 1 KB global_load_lds_dwordx4 transfers (lane i lands at M0 + 16 i).
@@ -299,16 +307,29 @@ __global__ __launch_bounds__(kThreads, 1) void sdpa_fwd_bf16_kernel(const FwdPar
     // 0 .. NXF-1; in a fused iteration they are issued one or two per k-step of phase A
     // instead of back to back.
     constexpr int NXF = 2 * XPW + XPB;
+    // transfer i of iteration t: V(t+1) first, then K and bias of tile t + NKS
     auto dma_xfer = [&](int t, int i) {
         if (i < XPW) {
-            if (t + 2 < t_end) dma_k_x(t + 2, i);
+            dma_v_x(t + 1, i);
         } else if (i < 2 * XPW) {
-            dma_v_x(t + 1, i - XPW);
+            if (t + NKS < t_end) dma_k_x(t + NKS, i - XPW);
         } else {
-            if (t + 2 < t_end) dma_b_x(t + 2, i - 2 * XPW);
+            if (t + NKS < t_end) dma_b_x(t + NKS, i - 2 * XPW);
         }
     };
     auto dma_wait = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
+    // with a 3-deep K ring: wait for everything but the K (and bias) transfers of tile u,
+    // issued last, when tile u exists
+    auto dma_wait_but_k = [&](int u) {
+        if constexpr (NKS == 3) {
+            if (u < t_end) {
+                if (fb_dma) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(XPW + XPB) : "memory");
+                else asm volatile("s_waitcnt vmcnt(%0)" :: "n"(XPW) : "memory");
+                return;
+            }
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    };
 
     // ---- per-lane LDS read offsets (bf16 elements) -----------------------------------------
     // K: A operand row (lane % 32) -> key perm32(r32) (+32 for the second key block).
@@ -454,7 +475,7 @@ __global__ __launch_bounds__(kThreads, 1) void sdpa_fwd_bf16_kernel(const FwdPar
             msk = needs_mask(tn);
             if constexpr (BIAS == BIAS_T5) {
                 const int rmin = j0 - pwb, rmax = j0 + kBN - 1 - pwa;
-                if (rmin >= kT5Sat) bconst = t5s[2 * kT5Sat];
+                if (rmin >= kT5Sat) bconst = t5s[2 * kT5Pad];
                 else if (rmax <= -kT5Sat) bconst = t5s[0];
                 else per_elem = true;
             }
@@ -499,13 +520,13 @@ __global__ __launch_bounds__(kThreads, 1) void sdpa_fwd_bf16_kernel(const FwdPar
                 } else if (g == 1) {
                     if (per_elem) {
                         if constexpr (BIAS == BIAS_T5) {
-                            const int rel0 = jl - my_pos;
+                            // register e holds key jl + 32 (e >> 4) + (e & 15): one base per
+                            // lane, compile-time offsets (rows past the end of the queries use
+                            // the wave's last row, so the index stays in the table)
+                            const float* trow = t5s + kT5Pad + (jl - min(my_pos, pwb));
 #pragma unroll
-                            for (int e = 0; e < 32; ++e) {
-                                const int rel = rel0 + (e >> 4) * 32 + (e & 15);
-                                const int idx = min(max(rel, -kT5Sat), kT5Sat) + kT5Sat;
-                                ns[e >> 4][e & 15] = fmaf(ns[e >> 4][e & 15], c_scale, t5s[idx]);
-                            }
+                            for (int e = 0; e < 32; ++e)
+                                ns[e >> 4][e & 15] = fmaf(ns[e >> 4][e & 15], c_scale, trow[(e >> 4) * 32 + (e & 15)]);
                         } else if constexpr (FB) {
                             if (fb_dma) {
 #pragma unroll
@@ -516,10 +537,10 @@ __global__ __launch_bounds__(kThreads, 1) void sdpa_fwd_bf16_kernel(const FwdPar
                                         for (int hv = 0; hv < 2; ++hv) {
                                             const uint32_t lo = fb[2 * jb][c], hi = fb[2 * jb + 1][c];
                                             const int v0 = 2 * c + hv;
-                                            ns[jb][v0] = fmaf(ns[jb][v0], c_scale,
-                                                bf16_to_f32(hv ? (lo >> 16) : (lo & 0xffffu)) * kLog2e);
-                                            ns[jb][v0 + 8] = fmaf(ns[jb][v0 + 8], c_scale,
-                                                bf16_to_f32(hv ? (hi >> 16) : (hi & 0xffffu)) * kLog2e);
+                                            ns[jb][v0] = fmaf(ns[jb][v0], n_scale,
+                                                bf16_to_f32(hv ? (lo >> 16) : (lo & 0xffffu)));
+                                            ns[jb][v0 + 8] = fmaf(ns[jb][v0 + 8], n_scale,
+                                                bf16_to_f32(hv ? (hi >> 16) : (hi & 0xffffu)));
                                         }
                             } else {
                                 const uint16_t* br = fbg + (size_t)(row_ok ? my_i : 0) * Sk;
@@ -527,7 +548,7 @@ __global__ __launch_bounds__(kThreads, 1) void sdpa_fwd_bf16_kernel(const FwdPar
                                 for (int e = 0; e < 32; ++e) {
                                     const int j = jl + (e >> 4) * 32 + (e & 15);
                                     const float bv = (row_ok && j < Sk) ? bf16_to_f32(br[j]) : 0.f;
-                                    ns[e >> 4][e & 15] = fmaf(ns[e >> 4][e & 15], c_scale, bv * kLog2e);
+                                    ns[e >> 4][e & 15] = fmaf(ns[e >> 4][e & 15], n_scale, bv);
                                 }
                             }
                         }
@@ -562,7 +583,13 @@ __global__ __launch_bounds__(kThreads, 1) void sdpa_fwd_bf16_kernel(const FwdPar
         }
         if constexpr (DO_PREP) {
             ext = partner_max(ext);
-            if (per_elem) {
+            if constexpr (FB) {
+                // scores plus bias in natural-log units: the exponent's FMA applies log2(e)
+                mt_c = ext * kLog2e;
+                cc_c = kLog2e;
+                bc_c = 0.f;
+            } else if (per_elem) {
+                // T5 near the diagonal: scores already in the log2 domain
                 mt_c = ext;
                 cc_c = 1.f;
                 bc_c = 0.f;
@@ -576,21 +603,22 @@ __global__ __launch_bounds__(kThreads, 1) void sdpa_fwd_bf16_kernel(const FwdPar
     };
 
     // ---- main loop ---------------------------------------------------------------------------
-    // Rings: K(t) (with its bias tile) in K slot (t - t_begin) & 1, V(t) in V slot
-    // (t - t_begin) & 1. Iteration t reads K(t+1) and V(t) while K(t+2) and V(t+1) are in
-    // flight; the barrier at its end publishes them and frees the slots of K(t+1) and V(t).
+    // Rings: K(t) (with its bias tile) in K slot (t - t_begin) % NKS, V(t) in V slot
+    // (t - t_begin) & 1. Iteration t reads K(t+1) and V(t) while V(t+1) and K(t+NKS) are in
+    // flight; the wait and barrier at its end publish V(t+1) and K(t+2) and free the slots of
+    // V(t) and K(t+1).
     auto none = [](int) {};
     f32x16 sa[2], sb[2];
     dma_k(t_begin);
     dma_wait();
     __syncthreads();
     dma_v(t_begin);
-    if (t_begin + 1 < t_end) dma_k(t_begin + 1);
+    for (int u = t_begin + 1; u < t_begin + NKS && u < t_end; ++u) dma_k(u);
     if (active(t_begin)) {
         phase_a(True{}, False{}, sb, sa, kptr(t_begin), nullptr, none);
         phase_b(False{}, True{}, sb, sa, nullptr, kptr(t_begin), t_begin);
     }
-    dma_wait();
+    dma_wait_but_k(t_begin + 2);
     __syncthreads();
 
     // cs: prepared score registers of tile t; ns: receives S^T of tile t+1
@@ -599,8 +627,8 @@ __global__ __launch_bounds__(kThreads, 1) void sdpa_fwd_bf16_kernel(const FwdPar
         const bool cur = active(t);
         const bool nxt = has_next && active(t + 1);
         if (!(cur && nxt)) {
-            if (t + 2 < t_end) dma_k(t + 2);
             if (has_next) dma_v(t + 1);
+            if (t + NKS < t_end) dma_k(t + NKS);
         }
         const uint16_t* kbn = kptr(t + 1);
         const uint16_t* vb = vptr(t);
@@ -618,7 +646,7 @@ __global__ __launch_bounds__(kThreads, 1) void sdpa_fwd_bf16_kernel(const FwdPar
             phase_a(True{}, False{}, cs, ns, kbn, vb, none);
             phase_b(False{}, True{}, cs, ns, vb, kbn, t + 1);
         }
-        if (has_next) dma_wait();
+        if (has_next) dma_wait_but_k(t + NKS);
         __syncthreads();
     };
     // unrolled by two so that the two score register sets swap roles without copies
