@@ -176,6 +176,36 @@ def cpu_baseline(wl: si.Workload, budget_s: float = 12.0):
                       f"{secs:.1f} s"}
 
 
+def tile_flops(wl: si.Workload) -> float:
+    """FLOP of the matrix work the bf16 kernel performs: 4*D per (row, key) slot of every block
+    of 32 query rows x 64 keys it computes, masked slots included. Follows the kernel's tile
+    plan: the key range of each 256-row work item, minus the 64-key tiles that a 32-row wave
+    skips because the mask hides them completely. One such block is 32*D/8 MFMAs of
+    v_mfma_f32_32x32x16_bf16 (32768 flop each), so rocprofv3's SQ_INSTS_MFMA times 32768 must
+    equal this count (the profile summary checks it)."""
+    off = wl.Sk - wl.Sq
+    blocks = 0
+    for q0 in range(0, wl.Sq, 256):
+        pa, pb = q0 + off, min(q0 + 256, wl.Sq) - 1 + off
+        khi, klo = wl.Sk - 1, 0
+        if wl.mask_kind != si.MASK_NONE:
+            khi = min(khi, pb)
+        if wl.mask_kind == si.MASK_SLIDING:
+            klo = max(0, pa - wl.window + 1)
+        if khi < klo:
+            continue
+        for wq0 in range(q0, min(q0 + 256, wl.Sq), 32):
+            pwa, pwb = wq0 + off, min(wq0 + 31, wl.Sq - 1) + off
+            for t in range(klo // 64, khi // 64 + 1):
+                j0 = 64 * t
+                if wl.mask_kind != si.MASK_NONE and j0 > pwb:
+                    continue
+                if wl.mask_kind == si.MASK_SLIDING and j0 + 63 <= pwa - wl.window:
+                    continue
+                blocks += 1
+    return 4.0 * wl.D * 32 * 64 * blocks * wl.B * wl.Hq
+
+
 def report(wl: si.Workload, t: dict):
     flops = si.effective_flops(wl)
     achieved = flops / (t["kernel_ms_avg"] * 1e-3) / 1e12
@@ -239,6 +269,8 @@ def main(argv=None):
         "data": "synthetic",
         "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "config": {**wl.describe(), "effective_gflop": round(flops / 1e9, 2),
+                   "tile_gflop": round(tile_flops(wl) / 1e9, 2),
+                   "tile_tflops": round(tile_flops(wl) / (t["kernel_ms_avg"] * 1e-3) / 1e12, 2),
                    "kernel_ms_median": round(t["kernel_ms_median"], 4),
                    "event_ms_per_step": round(t["region_ms_per_step"], 4),
                    "hbm_gbs_algorithmic": round(si.algorithmic_bytes(wl) /
@@ -252,17 +284,28 @@ def main(argv=None):
     print(json.dumps(line), flush=True)
 
     if args.sweep:
-        for key in ["c2", "c3", "c3c", "c4t5", "c4full", "c5mha", "c5gqa", "c5mqa"]:
+        ms = {}
+        for key in ["c2", "c2c", "c3", "c3c", "c4t5", "c4full", "c5mha", "c5gqa", "c5mqa"]:
             w2 = si.WORKLOADS[key]
             t2 = time_workload(sdpa, w2, max(5, args.steps // 2), args.warmup)
             f2, a2 = report(w2, t2)
+            ms[key] = t2["kernel_ms_median"]
             rec = {"workload": key, **w2.describe(), "kernel_ms_avg": round(t2["kernel_ms_avg"], 4),
                    "kernel_ms_median": round(t2["kernel_ms_median"], 4),
                    "effective_tflops": round(a2, 2),
                    "pct_of_bf16_peak": round(100 * a2 / PEAK_BF16_TFLOPS, 2),
+                   "tile_tflops": round(tile_flops(w2) / (t2["kernel_ms_avg"] * 1e-3) / 1e12, 2),
                    "hbm_gbs_algorithmic": round(si.algorithmic_bytes(w2) /
                                                 (t2["kernel_ms_avg"] * 1e-3) / 1e9, 1)}
             print(json.dumps(rec), file=sys.stderr, flush=True)
+        # sliding window 4096 at S = 4096 is exactly causal: same work, same time expected;
+        # at S = 8192 the window keeps 0.750 of the causal pairs
+        for a, b, note in [("c2", "c2c", "sliding(4096) / causal at S=4096, expect 1.0"),
+                           ("c3", "c3c", "sliding(4096) / causal at S=8192; visible pairs 0.750")]:
+            print(json.dumps({"comparison": note, "time_ratio": round(ms[a] / ms[b], 4),
+                              "pairs_ratio": round(si.effective_flops(si.WORKLOADS[a]) /
+                                                   si.effective_flops(si.WORKLOADS[b]), 4)}),
+                  file=sys.stderr, flush=True)
     return 0
 
 

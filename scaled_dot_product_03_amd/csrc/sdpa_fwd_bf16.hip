@@ -12,8 +12,9 @@
 // two waves per SIMD):
 //   * each wave owns 32 query rows; its Q fragment stays in VGPRs for the whole kernel;
 //   * keys are visited in tiles of 64, ascending. K and V tiles are copied global -> LDS by
-//     the DMA path of the load unit (global_load_lds_dwordx4) into two 2-slot rings, stored
-//     row-major ([key][d]) with XOR-swizzled 16-byte chunks; K runs one tile ahead of V;
+//     the DMA path of the load unit (global_load_lds_dwordx4) into a K ring (2 slots; 3 for
+//     D = 64 with a full bias) and a 2-slot V ring, stored row-major ([key][d]) with
+//     XOR-swizzled 16-byte chunks; K runs one tile ahead of V;
 //   * scores are computed transposed, S^T = K . Q^T, with v_mfma_f32_32x32x16_bf16: each lane
 //     then holds one query row (lane % 32) and 32 of the tile's keys, so the row max/sum are
 //     in-lane plus one permlane32 exchange with the lane holding the other 32 keys;

@@ -75,8 +75,9 @@ def _c5(hkv: int) -> Workload:
                     MASK_CAUSAL, seed=5000, kv_seed=5000 + 10 * hkv)
 
 
-# The five workloads (c1..c5); c3c is the full-causal comparison run of c3, c4f the full-bias
-# variant of c4, c5 is swept over Hkv in {32, 8, 1}.
+# The five workloads (c1..c5); c3c is the full-causal comparison run of c3 and c2c the causal
+# twin of c2 (window 4096 = S), c4full the full-bias variant of c4, c5 is swept over Hkv in
+# {32, 8, 1}.
 WORKLOADS = {
     "c1": Workload("tiny_causal_f32_b1_h2_s128_d64", 1, 2, 2, 128, 128, 64, "f32", MASK_CAUSAL,
                    seed=1000),
@@ -86,6 +87,8 @@ WORKLOADS = {
                    MASK_SLIDING, window=4096, seed=3000),
     "c3c": Workload("mistral_gqa_causal_b4_s8192", 4, 32, 8, 8192, 8192, 128, "bf16",
                     MASK_CAUSAL, seed=3000),
+    "c2c": Workload("mistral_gqa_causal_b4_s4096", 4, 32, 8, 4096, 4096, 128, "bf16",
+                    MASK_CAUSAL, seed=2000),
     "c4t5": Workload("t5_encoder_rpe_b8_h12_s2048_d64", 8, 12, 12, 2048, 2048, 64, "bf16",
                      MASK_NONE, bias_kind=BIAS_T5, seed=4000),
     "c4full": Workload("t5_encoder_fullbias_b8_h12_s2048_d64", 8, 12, 12, 2048, 2048, 64, "bf16",

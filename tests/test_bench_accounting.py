@@ -1,0 +1,64 @@
+"""Work accounting of bench.py (CPU): the tile-granular FLOP count against closed forms.
+
+The count is the matrix work the bf16 kernel performs (32-row x 64-key blocks, masked slots
+included); the profile summary checks it against the MFMA instruction counter.
+"""
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+import sdpa_inputs as si  # noqa: E402
+
+BLOCK = 32 * 64
+
+
+def blocks(wl):
+    return bench.tile_flops(wl) / (4.0 * wl.D * BLOCK * wl.B * wl.Hq)
+
+
+def test_unmasked_is_dense_rounded_to_tiles():
+    wl = si.WORKLOADS["c4t5"]
+    assert blocks(wl) == (wl.Sq // 32) * (wl.Sk // 64)
+    ragged = wl.replace(Sq=100, Sk=130, B=1, Hq=1, Hkv=1)
+    assert blocks(ragged) == 4 * 3          # ceil(100/32) waves x ceil(130/64) tiles
+
+
+def test_causal_closed_form():
+    # rows 32w..32w+31 need key tiles 0 .. floor((32w+31)/64): w = 2k and 2k+1 both need k+1
+    for S in (256, 4096, 8192):
+        wl = si.WORKLOADS["c2c"].replace(Sq=S, Sk=S, B=1, Hq=1, Hkv=1)
+        n = S // 64
+        assert blocks(wl) == 2 * n * (n + 1) // 2
+
+
+def test_window_equal_to_seqlen_is_causal():
+    assert bench.tile_flops(si.WORKLOADS["c2"]) == bench.tile_flops(si.WORKLOADS["c2c"])
+
+
+def test_tile_count_bounds_effective_work():
+    for key in ("c2", "c3", "c3c", "c4t5", "c5mqa"):
+        wl = si.WORKLOADS[key]
+        assert si.effective_flops(wl) <= bench.tile_flops(wl) <= 1.05 * si.effective_flops(wl)
+
+
+@pytest.mark.parametrize("mask,w,sq,sk", [
+    (si.MASK_SLIDING, 1, 300, 333), (si.MASK_SLIDING, 63, 300, 333),
+    (si.MASK_SLIDING, 64, 300, 333), (si.MASK_SLIDING, 65, 257, 257),
+    (si.MASK_SLIDING, 200, 300, 333), (si.MASK_CAUSAL, 0, 300, 333), (si.MASK_CAUSAL, 0, 70, 500)])
+def test_blocks_are_exactly_those_with_a_visible_pair(mask, w, sq, sk):
+    # brute force: with Sq <= Sk the kernel computes a 32-row x 64-key block iff some row of
+    # it sees some key of it
+    wl = si.WORKLOADS["c3"].replace(Sq=sq, Sk=sk, B=1, Hq=1, Hkv=1, window=w, mask_kind=mask)
+    off = wl.Sk - wl.Sq
+    need = set()
+    for i in range(wl.Sq):
+        p = i + off
+        lo = 0 if mask == si.MASK_CAUSAL else max(0, p - w + 1)
+        for j in range(lo, min(p, wl.Sk - 1) + 1):
+            need.add((i // 32, j // 64))
+    assert blocks(wl) == len(need)
