@@ -287,7 +287,8 @@ def main(argv=None):
         ms = {}
         for key in ["c2", "c2c", "c3", "c3c", "c4t5", "c4full", "c5mha", "c5gqa", "c5mqa"]:
             w2 = si.WORKLOADS[key]
-            t2 = time_workload(sdpa, w2, max(5, args.steps // 2), args.warmup)
+            # at least 30 warmup launches: clocks ramp up over ~15 launches after the GPU idles
+            t2 = time_workload(sdpa, w2, max(5, args.steps // 2), max(30, args.warmup))
             f2, a2 = report(w2, t2)
             ms[key] = t2["kernel_ms_median"]
             rec = {"workload": key, **w2.describe(), "kernel_ms_avg": round(t2["kernel_ms_avg"], 4),
