@@ -1,4 +1,4 @@
-"""fp64 CPU oracle for the fused attention forward.
+"""fp64 CPU oracle for the fused attention forward and its gradients.
 
 TEST INFRASTRUCTURE ONLY: used by tests/, __graft_entry__.smoke() and bench.py's cpu_baseline
 leg. The product (scaled_dot_product_03_amd) never imports it, and it imports nothing from the
@@ -12,3 +12,4 @@ from .sdpa_ref import (  # noqa: F401
     t5_bucket, visible, attend_rows, attention_weights, sdpa_rows, sdpa_forward,
     default_threads,
 )
+from .sdpa_bwd_ref import head_backward, sdpa_backward  # noqa: F401
