@@ -1,7 +1,8 @@
 /*
- * sdpa.h -- C ABI of the MI355X (gfx950) fused scaled-dot-product attention forward.
+ * sdpa.h -- C ABI of the MI355X (gfx950) fused scaled-dot-product attention forward and its
+ * gradients (sdpa_bwd, below).
  *
- * Operation (one call = one fused kernel launch):
+ * Forward operation (one call = one fused kernel launch):
  *     O   = softmax(Q.K^T * scale + bias + mask) . V
  *     LSE = log(sum_j exp(Q.K^T * scale + bias + mask))        (natural log, per query row)
  *   Definition: the four steps (score, scale + softmax, attend, output with Q's shape) of the
@@ -57,7 +58,7 @@
 extern "C" {
 #endif
 
-#define SDPA_ABI_VERSION 1
+#define SDPA_ABI_VERSION 2
 
 enum sdpa_mask_kind { SDPA_MASK_NONE = 0, SDPA_MASK_CAUSAL = 1, SDPA_MASK_SLIDING = 2 };
 enum sdpa_bias_kind { SDPA_BIAS_NONE = 0, SDPA_BIAS_T5 = 1, SDPA_BIAS_FULL = 2 };
@@ -95,6 +96,39 @@ int sdpa_fwd_bf16_f32out(const void* q, const void* k, const void* v, float* out
 int sdpa_fwd_f32(const float* q, const float* k, const float* v, float* out, float* lse,
                  int B, int Hq, int Hkv, int Sq, int Sk, int D, float scale,
                  int mask_kind, int window, int bias_kind, const void* bias_tbl, void* stream);
+
+/*
+ * bf16 backward: the gradients of L = sum(dout * out) with respect to q, k and v, where out is
+ * the forward above (same shapes, masks, biases, scale and head sharing). The pages use the
+ * backward without printing it (FAT5 README: backward TFLOPS of its biased flash kernels;
+ * transformers issue "Transformer models are not deterministic when using Flash Attention 2":
+ * run-to-run equality of a training step); the formulas are the chain rule through the
+ * forward's definition, with P the softmax weights and S the scaled, biased, masked scores:
+ *     dV = P^T dO,  dP = dO V^T,  dS = P * (dP - rowsum(dO * O)),
+ *     dQ = scale * dS K,  dK = scale * dS^T Q.
+ * A KV head shared by G query heads gets the sum of their dK and dV. The biases get no
+ * gradient.
+ *   q, k, v, out, dout : bf16 (out and lse as written by sdpa_fwd for the same arguments)
+ *   dq : [B][Sq][Hq][D]   dk, dv : [B][Sk][Hkv][D]   (bf16 here, fp32 for sdpa_bwd_f32out)
+ *   ws : caller-owned device workspace of B*Hq*Sq floats (4-byte aligned); receives
+ *        rowsum(dout * out) per query row; its contents on entry do not matter.
+ * Three launches on `stream`: the row sums, dq (one workgroup per 256 query rows), dk and dv
+ * (one workgroup per 128 keys of one KV head, looping over the query rows of its G heads).
+ * Every output element has exactly one writer and a fixed summation order (query heads
+ * ascending, query rows ascending): bitwise reproducible, no atomics. Validation as for
+ * sdpa_fwd, plus dout, dq, dk, dv 16-byte aligned and non-NULL, ws non-NULL.
+ */
+int sdpa_bwd(const void* q, const void* k, const void* v, const void* out, const float* lse,
+             const void* dout, void* dq, void* dk, void* dv, float* ws,
+             int B, int Hq, int Hkv, int Sq, int Sk, int D, float scale,
+             int mask_kind, int window, int bias_kind, const void* bias_tbl, void* stream);
+
+/* Same as sdpa_bwd, with dq, dk, dv in fp32. */
+int sdpa_bwd_f32out(const void* q, const void* k, const void* v, const void* out,
+                    const float* lse, const void* dout, float* dq, float* dk, float* dv,
+                    float* ws, int B, int Hq, int Hkv, int Sq, int Sk, int D, float scale,
+                    int mask_kind, int window, int bias_kind, const void* bias_tbl,
+                    void* stream);
 
 /* Static English text for a status code (never NULL). */
 const char* sdpa_status_str(int status);

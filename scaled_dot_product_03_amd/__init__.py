@@ -1,4 +1,4 @@
-"""MI355X (gfx950) fused scaled-dot-product attention forward.
+"""MI355X (gfx950) fused scaled-dot-product attention forward and its gradients.
 
 Thin Python binding over the C ABI in include/sdpa.h (libsdpa_mi355x.so, built in-tree by
 scaled_dot_product_03_amd.build). This module only marshals arguments: torch supplies device
@@ -6,6 +6,7 @@ memory and the current stream, every step of the attention runs in the HIP kerne
 fallback: if the library is missing, calls raise.
 
     out, lse = fwd(q, k, v, mask="causal")           # q [B,Sq,Hq,D], k/v [B,Sk,Hkv,D]
+    dq, dk, dv = bwd(q, k, v, out, lse, dout, mask="causal")
 
 Layout follows the "jax-gpu-05-attention-gpu" codelab, section 3 (batch, sequence, heads,
 head dim). lse is [B, Hq, Sq] fp32 (natural log).
@@ -32,8 +33,9 @@ STATUS_NAMES = {0: "SDPA_OK", 1: "SDPA_ERR_NULL", 2: "SDPA_ERR_SHAPE", 3: "SDPA_
                 10: "SDPA_ERR_LAUNCH"}
 
 # symbols exported by the library (must match include/sdpa.h)
-ENTRY_POINTS = ("sdpa_fwd", "sdpa_fwd_bf16_f32out", "sdpa_fwd_f32", "sdpa_status_str",
-                "sdpa_abi_version")
+ENTRY_POINTS = ("sdpa_fwd", "sdpa_fwd_bf16_f32out", "sdpa_fwd_f32", "sdpa_bwd",
+                "sdpa_bwd_f32out", "sdpa_status_str", "sdpa_abi_version")
+ABI_VERSION = 2
 
 _lib = None
 
@@ -64,6 +66,12 @@ def load():
         fn = getattr(L, name)
         fn.argtypes = fwd_args
         fn.restype = ctypes.c_int
+    bwd_args = [ctypes.c_void_p] * 10 + [ctypes.c_int] * 6 + [ctypes.c_float] + \
+               [ctypes.c_int] * 3 + [ctypes.c_void_p, ctypes.c_void_p]
+    for name in ("sdpa_bwd", "sdpa_bwd_f32out"):
+        fn = getattr(L, name)
+        fn.argtypes = bwd_args
+        fn.restype = ctypes.c_int
     L.sdpa_status_str.argtypes = [ctypes.c_int]
     L.sdpa_status_str.restype = ctypes.c_char_p
     L.sdpa_abi_version.argtypes = []
@@ -84,12 +92,54 @@ def call_raw(entry: str, q, k, v, out, lse, B, Hq, Hkv, Sq, Sk, D, scale, mask_k
               bias_kind, bias, stream)
 
 
+def call_raw_bwd(entry: str, q, k, v, out, lse, dout, dq, dk, dv, ws, B, Hq, Hkv, Sq, Sk, D,
+                 scale, mask_kind, window, bias_kind, bias, stream) -> int:
+    """Call a backward entry point with raw integer pointers; returns the status code."""
+    fn = getattr(load(), entry)
+    return fn(q, k, v, out, lse, dout, dq, dk, dv, ws, B, Hq, Hkv, Sq, Sk, D,
+              ctypes.c_float(scale), mask_kind, window, bias_kind, bias, stream)
+
+
 def _kind(val, table, what):
     if isinstance(val, str):
         if val not in table:
             raise ValueError(f"unknown {what} {val!r}")
         return table[val]
     return int(val)
+
+
+def _check_qkv(q, k, v):
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-D [B, S, H, D]")
+    B, Sq, Hq, D = q.shape
+    Bk, Sk, Hkv, Dk = k.shape
+    if (Bk, Dk) != (B, D) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("shape mismatch between q, k, v")
+    if q.dtype != k.dtype or q.dtype != v.dtype:
+        raise ValueError("q, k, v must share a dtype")
+    for t in (q, k, v):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("q, k, v must be contiguous cuda tensors")
+    return B, Sq, Hq, D, Sk, Hkv
+
+
+def _bias_ptr(bk, bias, dtype, B, Hq, Sq, Sk):
+    import torch
+
+    if bk == BIAS_T5:
+        if bias is None or bias.dtype != torch.float32 or tuple(bias.shape) != (Hq, 32) \
+                or not bias.is_contiguous() or not bias.is_cuda:
+            raise ValueError("t5 bias must be a contiguous cuda fp32 [Hq, 32] table")
+        return bias.data_ptr()
+    if bk == BIAS_FULL:
+        if bias is None or bias.dtype != dtype or tuple(bias.shape) != (B, Hq, Sq, Sk) \
+                or not bias.is_contiguous() or not bias.is_cuda:
+            raise ValueError("full bias must be a contiguous cuda [B, Hq, Sq, Sk] tensor "
+                             "in the input dtype")
+        return bias.data_ptr()
+    if bias is not None:
+        raise ValueError("bias given with bias_kind='none'")
+    return None
 
 
 def fwd(q, k, v, *, scale: Optional[float] = None, mask="causal", window: int = 0,
@@ -104,17 +154,7 @@ def fwd(q, k, v, *, scale: Optional[float] = None, mask="causal", window: int = 
     import torch
 
     L = load()
-    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
-        raise ValueError("q, k, v must be 4-D [B, S, H, D]")
-    B, Sq, Hq, D = q.shape
-    Bk, Sk, Hkv, Dk = k.shape
-    if (Bk, Dk) != (B, D) or tuple(v.shape) != tuple(k.shape):
-        raise ValueError("shape mismatch between q, k, v")
-    if q.dtype != k.dtype or q.dtype != v.dtype:
-        raise ValueError("q, k, v must share a dtype")
-    for t in (q, k, v):
-        if not t.is_cuda or not t.is_contiguous():
-            raise ValueError("q, k, v must be contiguous cuda tensors")
+    B, Sq, Hq, D, Sk, Hkv = _check_qkv(q, k, v)
     mk = _kind(mask, _MASKS, "mask")
     bk = _kind(bias_kind, _BIASES, "bias kind")
     if scale is None:
@@ -131,20 +171,7 @@ def fwd(q, k, v, *, scale: Optional[float] = None, mask="causal", window: int = 
             raise ValueError("fp32 inputs produce fp32 output")
     else:
         raise ValueError(f"unsupported dtype {q.dtype}")
-    bias_ptr = None
-    if bk == BIAS_T5:
-        if bias is None or bias.dtype != torch.float32 or tuple(bias.shape) != (Hq, 32) \
-                or not bias.is_contiguous() or not bias.is_cuda:
-            raise ValueError("t5 bias must be a contiguous cuda fp32 [Hq, 32] table")
-        bias_ptr = bias.data_ptr()
-    elif bk == BIAS_FULL:
-        if bias is None or bias.dtype != q.dtype or tuple(bias.shape) != (B, Hq, Sq, Sk) \
-                or not bias.is_contiguous() or not bias.is_cuda:
-            raise ValueError("full bias must be a contiguous cuda [B, Hq, Sq, Sk] tensor "
-                             "in the input dtype")
-        bias_ptr = bias.data_ptr()
-    elif bias is not None:
-        raise ValueError("bias given with bias_kind='none'")
+    bias_ptr = _bias_ptr(bk, bias, q.dtype, B, Hq, Sq, Sk)
     if out is None:
         out = torch.empty((B, Sq, Hq, D), dtype=odt, device=q.device)
     if lse is None:
@@ -157,3 +184,52 @@ def fwd(q, k, v, *, scale: Optional[float] = None, mask="causal", window: int = 
     if st != SDPA_OK:
         raise SdpaError(st, L.sdpa_status_str(st).decode())
     return out, lse
+
+
+def bwd(q, k, v, out, lse, dout, *, scale: Optional[float] = None, mask="causal",
+        window: int = 0, bias_kind="none", bias=None, grad_dtype=None, ws=None, dq=None,
+        dk=None, dv=None, stream=None):
+    """Gradients (dq, dk, dv) of sum(dout * out) on the current HIP stream.
+
+    q, k, v, out, dout bf16 (out, lse from fwd with the same arguments); lse [B, Hq, Sq] fp32.
+    grad_dtype: torch.bfloat16 (default) or torch.float32 for dq, dk, dv. ws: optional fp32
+    workspace of B*Hq*Sq elements (allocated here when None).
+    """
+    import torch
+
+    L = load()
+    B, Sq, Hq, D, Sk, Hkv = _check_qkv(q, k, v)
+    if q.dtype != torch.bfloat16:
+        raise ValueError("the backward takes bf16 q, k, v")
+    for t, name in ((out, "out"), (dout, "dout")):
+        if t.dtype != torch.bfloat16 or tuple(t.shape) != (B, Sq, Hq, D) or not t.is_cuda \
+                or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous cuda bf16 [B, Sq, Hq, D] tensor")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, Sq) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous fp32 [B, Hq, Sq] tensor")
+    mk = _kind(mask, _MASKS, "mask")
+    bk = _kind(bias_kind, _BIASES, "bias kind")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    gdt = grad_dtype or torch.bfloat16
+    if gdt not in (torch.bfloat16, torch.float32):
+        raise ValueError("grad_dtype must be bf16 or fp32")
+    entry = "sdpa_bwd" if gdt == torch.bfloat16 else "sdpa_bwd_f32out"
+    bias_ptr = _bias_ptr(bk, bias, q.dtype, B, Hq, Sq, Sk)
+    if dq is None:
+        dq = torch.empty((B, Sq, Hq, D), dtype=gdt, device=q.device)
+    if dk is None:
+        dk = torch.empty((B, Sk, Hkv, D), dtype=gdt, device=q.device)
+    if dv is None:
+        dv = torch.empty((B, Sk, Hkv, D), dtype=gdt, device=q.device)
+    if ws is None:
+        ws = torch.empty((B * Hq * Sq,), dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = getattr(L, entry)(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                           lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                           dv.data_ptr(), ws.data_ptr(), B, Hq, Hkv, Sq, Sk, D,
+                           ctypes.c_float(scale), mk, int(window), bk, bias_ptr, stream)
+    if st != SDPA_OK:
+        raise SdpaError(st, L.sdpa_status_str(st).decode())
+    return dq, dk, dv

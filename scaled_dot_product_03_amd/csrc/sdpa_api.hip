@@ -1,6 +1,6 @@
-// C ABI of the fused attention forward (declared in include/sdpa.h): argument validation and
-// dispatch to the gfx950 kernels. Every check runs before any HIP call, so an invalid call
-// returns its status without touching the device.
+// C ABI of the fused attention forward and backward (declared in include/sdpa.h): argument
+// validation and dispatch to the gfx950 kernels. Every check runs before any HIP call, so an
+// invalid call returns its status without touching the device.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -11,6 +11,7 @@
 namespace sdpa {
 hipError_t launch_fwd_bf16(FwdParams p, int D, int mask, int bias, bool out_f32, hipStream_t s);
 hipError_t launch_fwd_f32(FwdParams p, int D, int mask, int bias, hipStream_t s);
+hipError_t launch_bwd_bf16(BwdParams p, int D, int mask, int bias, bool out_f32, hipStream_t s);
 }  // namespace sdpa
 
 namespace {
@@ -68,6 +69,37 @@ sdpa::FwdParams make_params(const void* q, const void* k, const void* v, void* o
     return p;
 }
 
+int validate_bwd(const void* q, const void* k, const void* v, const void* out,
+                 const float* lse, const void* dout, const void* dq, const void* dk,
+                 const void* dv, const float* ws, int B, int Hq, int Hkv, int Sq, int Sk, int D,
+                 float scale, int mask_kind, int window, int bias_kind, const void* bias_tbl) {
+    if (!dout || !dq || !dk || !dv || !ws) return SDPA_ERR_NULL;
+    int st = validate(q, k, v, out, lse, B, Hq, Hkv, Sq, Sk, D, scale, mask_kind, window,
+                      bias_kind, bias_tbl, 2);
+    if (st != SDPA_OK) return st;
+    // grid of the dK/dV kernel: one workgroup per 128 keys of each (b, KV head)
+    if ((long long)B * Hkv * ((Sk + 127) / 128) >= (1LL << 31)) return SDPA_ERR_SHAPE;
+    if (!aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
+        !aligned(ws, 4))
+        return SDPA_ERR_ALIGN;
+    return SDPA_OK;
+}
+
+sdpa::BwdParams make_bwd_params(const void* q, const void* k, const void* v, const void* out,
+                                const float* lse, const void* dout, void* dq, void* dk,
+                                void* dv, float* ws, int B, int Hq, int Hkv, int Sq, int Sk,
+                                float scale, int mask_kind, int window, const void* bias_tbl) {
+    const sdpa::FwdParams f = make_params(q, k, v, const_cast<void*>(out), const_cast<float*>(lse),
+                                          B, Hq, Hkv, Sq, Sk, scale, mask_kind, window, bias_tbl);
+    sdpa::BwdParams p{};
+    p.q = q; p.k = k; p.v = v; p.o = out; p.lse = lse; p.dout = dout;
+    p.dq = dq; p.dk = dk; p.dv = dv; p.delta = ws; p.bias = bias_tbl;
+    p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.Sq = Sq; p.Sk = Sk;
+    p.G = f.G; p.off = f.off; p.window = f.window;
+    p.scale = f.scale; p.scale_log2 = f.scale_log2;
+    return p;
+}
+
 }  // namespace
 
 extern "C" {
@@ -106,6 +138,33 @@ int sdpa_fwd_f32(const float* q, const float* k, const float* v, float* out, flo
     sdpa::FwdParams p = make_params(q, k, v, out, lse, B, Hq, Hkv, Sq, Sk, scale, mask_kind,
                                     window, bias_tbl);
     hipError_t e = sdpa::launch_fwd_f32(p, D, mask_kind, bias_kind, (hipStream_t)stream);
+    return e == hipSuccess ? SDPA_OK : SDPA_ERR_LAUNCH;
+}
+
+int sdpa_bwd(const void* q, const void* k, const void* v, const void* out, const float* lse,
+             const void* dout, void* dq, void* dk, void* dv, float* ws, int B, int Hq, int Hkv,
+             int Sq, int Sk, int D, float scale, int mask_kind, int window, int bias_kind,
+             const void* bias_tbl, void* stream) {
+    int st = validate_bwd(q, k, v, out, lse, dout, dq, dk, dv, ws, B, Hq, Hkv, Sq, Sk, D, scale,
+                          mask_kind, window, bias_kind, bias_tbl);
+    if (st != SDPA_OK) return st;
+    sdpa::BwdParams p = make_bwd_params(q, k, v, out, lse, dout, dq, dk, dv, ws, B, Hq, Hkv, Sq,
+                                        Sk, scale, mask_kind, window, bias_tbl);
+    hipError_t e = sdpa::launch_bwd_bf16(p, D, mask_kind, bias_kind, false, (hipStream_t)stream);
+    return e == hipSuccess ? SDPA_OK : SDPA_ERR_LAUNCH;
+}
+
+int sdpa_bwd_f32out(const void* q, const void* k, const void* v, const void* out,
+                    const float* lse, const void* dout, float* dq, float* dk, float* dv,
+                    float* ws, int B, int Hq, int Hkv, int Sq, int Sk, int D, float scale,
+                    int mask_kind, int window, int bias_kind, const void* bias_tbl,
+                    void* stream) {
+    int st = validate_bwd(q, k, v, out, lse, dout, dq, dk, dv, ws, B, Hq, Hkv, Sq, Sk, D, scale,
+                          mask_kind, window, bias_kind, bias_tbl);
+    if (st != SDPA_OK) return st;
+    sdpa::BwdParams p = make_bwd_params(q, k, v, out, lse, dout, dq, dk, dv, ws, B, Hq, Hkv, Sq,
+                                        Sk, scale, mask_kind, window, bias_tbl);
+    hipError_t e = sdpa::launch_bwd_bf16(p, D, mask_kind, bias_kind, true, (hipStream_t)stream);
     return e == hipSuccess ? SDPA_OK : SDPA_ERR_LAUNCH;
 }
 

@@ -1,0 +1,671 @@
+// gfx950 attention backward: gradients dQ, dK, dV of L = sum(dO * O) for the fused forward
+// O = softmax(Q.K^T * scale + bias + mask) . V (the four steps of the "jax-gpu-05-attention-gpu"
+// codelab, section 1; masks of its section 7 and of the transformers issue "Slowdown in
+// Training Speed Due to SDPA Mask Fix in Version 4.40.0"; biases of the FAT5 README; head
+// sharing of codelab section 9). With P the softmax weights (recomputed from the forward's
+// row log-sum-exp) and D_i = rowsum(dO_i * O_i):
+//     dV = P^T dO,  dP = dO V^T,  dS = P * (dP - D),  dQ = scale * dS K,  dK = scale * dS^T Q.
+// Three launches, each output element written once, fixed summation order, no atomics, so the
+// gradients are bitwise reproducible run to run (the determinism asked of a training step in
+// the transformers issue "Transformer models are not deterministic when using Flash Attention 2").
+//
+//   delta_kernel : D_i = rowsum(dO_i * O_i) for every query row, into the caller's workspace.
+//   dq_kernel    : one workgroup = 8 waves = 256 query rows of one (batch, query head), like the
+//                  forward: Q and dO fragments stay in VGPRs, K and V tiles of 64 keys stream
+//                  through 2-slot LDS rings (LDS DMA). Per 32-key half: S^T = K.Q^T and
+//                  dP^T = V.dO^T (lane = query row, 16 keys per lane half), P and dS^T in
+//                  registers, then dQ^T += K^T.dS^T with K^T from transposing LDS reads.
+//   dkdv_kernel  : one workgroup = 4 waves = 128 keys of one (batch, KV head); each wave owns 32
+//                  keys and keeps their K and V fragments in VGPRs and their dK^T, dV^T
+//                  accumulators in the accumulation registers (one wave per SIMD). Q and dO
+//                  tiles of 64 query rows stream through a 2-slot LDS ring over the rows of the
+//                  G query heads sharing the KV head (heads ascending, rows ascending). Per
+//                  32-row block: S = Q.K^T and dP = dO.V^T (lane = key, 16 rows per lane half),
+//                  then dV^T += dO^T.P and dK^T += Q^T.dS with Q^T, dO^T from transposing reads.
+// MFMA: v_mfma_f32_32x32x16_bf16 throughout; P and dS are rounded to bf16 (nearest even) as
+// MFMA operands, all sums are fp32.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "sdpa_params.h"
+
+namespace sdpa {
+namespace bwd {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kTinyScale = 1.17549435e-38f;   // stands in for a zero scale (see the forward)
+
+// Row permutation inside a 32-row MFMA operand (output register v of lane half h holds row
+// 16h + v), as in the forward kernel.
+__device__ __forceinline__ int perm32(int r) {
+    return ((r >> 2) & 1) * 16 + (r >> 3) * 4 + (r & 3);
+}
+// XOR swizzle of the 16-byte chunk index of a tile row. The backward reads each streamed tile
+// both row-wise (ds_read_b128, 8 lanes on rows {0..3, 16..19} + 4g) and through transposing
+// reads (16 lanes on 4 consecutive rows): bits 0-1 of the row spread the transposing reads,
+// bit 4 separates rows r and r + 16 for the row-wise reads.
+__device__ __forceinline__ int swz(int row) { return (2 * (row & 3)) | ((row >> 4) & 1); }
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    bf16x2 r;
+    r[0] = (__bf16)lo;
+    r[1] = (__bf16)hi;
+    return __builtin_bit_cast(uint32_t, r);
+}
+__device__ __forceinline__ s16x4 lds_read_tr(const uint16_t* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+}
+
+// Accumulators pinned to the accumulation registers (dK/dV kernel): MFMAs through inline asm
+// with "+a" operands. The compiler does not model hazards of these asm MFMAs, so the wait
+// states are explicit: 3 before every MFMA, which may read an operand a VALU instruction just
+// wrote (the packed P / dS fragment, or a fragment assembled by moves); 21 before anything
+// reads an accumulator an 8-pass MFMA wrote (acc_fence_read); 5 before an MFMA reads an
+// accumulator written by v_accvgpr_write (acc_fence_write).
+__device__ __forceinline__ void mfma_acc(f32x16& o, const bf16x8& a, const bf16x8& b) {
+    asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(o) : "v"(a), "v"(b));
+}
+template <int N>
+__device__ __forceinline__ void acc_fence_read(f32x16 (&o)[N]) {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 4" : "+a"(o[0]));
+#pragma unroll
+    for (int i = 1; i < N; ++i) asm volatile("" : "+a"(o[i]));
+}
+template <int N>
+__device__ __forceinline__ void acc_fence_write(f32x16 (&o)[N]) {
+#pragma unroll
+    for (int i = 0; i < N - 1; ++i) asm volatile("" : "+a"(o[i]));
+    asm volatile("s_nop 4" : "+a"(o[N - 1]));
+}
+
+__device__ __forceinline__ void dma16(const uint16_t* src, uint32_t lds_dst) {
+    // one 1 KB transfer: lane i's 16 bytes land at M0 + 16 i (no other instruction here reads
+    // M0); waited for explicitly with s_waitcnt vmcnt before the publishing barrier
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                 :: "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_dst)) : "memory");
+}
+__device__ __forceinline__ void dma_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Transposing read of 8 consecutive tile rows for the A operand of an MFMA whose k index runs
+// over rows: key group g holds rows 16 h + 8 (g & 1) + 32 (g >> 1) + e of lane half h, the
+// layout of the P / dS registers. Returns the DB fragments (32 head dims each) of group g;
+// rows 0..15 of fragment db are head dims 16 db + sigma, rows 16..31 are 16 (db + DB) + sigma.
+template <int D>
+__device__ __forceinline__ void read_tr(const uint16_t* tile, int g, int lane, bf16x8* dst) {
+    constexpr int DB = D / 32;
+    const int hh = lane >> 5, gg = lane >> 4, li = lane & 15, la = li & 3;
+    const int row = 16 * hh + (li >> 2) + 32 * (g >> 1) + 8 * (g & 1);
+    const int dlo = 16 * DB * (gg & 1) + 8 * (la & 1) + 4 * (la >> 1);
+    const int sw = swz(row);                // same for row + 4
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+        const int d = 16 * db + dlo;
+        const int coff = (((d >> 3) ^ sw) << 3) + (d & 7);
+        const s16x4 lo = lds_read_tr(tile + row * D + coff);
+        const s16x4 hi = lds_read_tr(tile + (row + 4) * D + coff);
+        u32x4 av;
+        av[0] = __builtin_bit_cast(u32x2, lo)[0];
+        av[1] = __builtin_bit_cast(u32x2, lo)[1];
+        av[2] = __builtin_bit_cast(u32x2, hi)[0];
+        av[3] = __builtin_bit_cast(u32x2, hi)[1];
+        dst[db] = __builtin_bit_cast(bf16x8, av);
+    }
+}
+
+// Row-wise read for the A operand of S (rows perm32(lane % 32) + 32 blk of the tile, head dims
+// 16 ks + 8 (lane / 32) .. + 7).
+template <int D>
+__device__ __forceinline__ bf16x8 read_rows(const uint16_t* tile, int blk, int ks, int lane) {
+    const int row = perm32(lane & 31) + 32 * blk;
+    const int ch = ((2 * ks + (lane >> 5)) ^ swz(row)) * 8;
+    return *(const bf16x8*)(tile + row * D + ch);
+}
+
+// Writes the O^T-layout accumulators of one lane (rows of head dims per block db, see read_tr)
+// times `mul` to the D-element row at `dst`.
+template <int D, bool OUT_F32>
+__device__ __forceinline__ void store_row(char* dst, const f32x16 (&acc)[D / 32], float mul, int hh) {
+    constexpr int DB = D / 32;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+        const int d0[2] = {16 * db + 8 * hh, 16 * (db + DB) + 8 * hh};
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            if constexpr (OUT_F32) {
+#pragma unroll
+                for (int hv = 0; hv < 2; ++hv) {
+                    u32x4 xo;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) xo[e] = __float_as_uint(acc[db][8 * c + 4 * hv + e] * mul);
+                    *(u32x4*)(dst + (d0[c] + 4 * hv) * 4) = xo;
+                }
+            } else {
+                u32x4 xo;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    xo[e] = pack_bf16x2(acc[db][8 * c + 2 * e] * mul, acc[db][8 * c + 2 * e + 1] * mul);
+                *(u32x4*)(dst + d0[c] * 2) = xo;
+            }
+        }
+    }
+}
+
+template <int D, bool OUT_F32>
+__device__ __forceinline__ void store_zero_row(char* dst, int hh) {
+    f32x16 z[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) z[db][v] = 0.f;
+    store_row<D, OUT_F32>(dst, z, 0.f, hh);
+}
+
+// ------------------------------------------------------------------------------------------
+// D_i = rowsum(dO_i * O_i): one thread per query row, head dims ascending
+// ------------------------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void delta_kernel(const BwdParams p) {
+    const long long r = (long long)blockIdx.x * 256 + threadIdx.x;   // (b * Sq + i) * Hq + h
+    if (r >= (long long)p.B * p.Sq * p.Hq) return;
+    const int h = (int)(r % p.Hq);
+    const long long bi = r / p.Hq;
+    const int i = (int)(bi % p.Sq), b = (int)(bi / p.Sq);
+    const uint16_t* o = (const uint16_t*)p.o + r * D;
+    const uint16_t* g = (const uint16_t*)p.dout + r * D;
+    float acc = 0.f;
+#pragma unroll
+    for (int c = 0; c < D; c += 8) {
+        const u32x4 a = *(const u32x4*)(o + c), x = *(const u32x4*)(g + c);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            acc = fmaf(bf16_to_f32(a[e] & 0xffffu), bf16_to_f32(x[e] & 0xffffu), acc);
+            acc = fmaf(bf16_to_f32(a[e] >> 16), bf16_to_f32(x[e] >> 16), acc);
+        }
+    }
+    p.delta[((size_t)b * p.Hq + h) * p.Sq + i] = acc;
+}
+
+// ------------------------------------------------------------------------------------------
+// dQ: 256 query rows per workgroup, 64-key tiles
+// ------------------------------------------------------------------------------------------
+template <int D, int MASK, int BIAS, bool OUT_F32>
+__global__ __launch_bounds__(512, 1) void dq_kernel(const BwdParams p) {
+    constexpr int kWaves = 8, kThreads = 512, kBM = 256, kBN = 64;
+    constexpr int CH = D / 8, KS = D / 16, DB = D / 32, TILE = kBN * D;
+    constexpr bool FB = BIAS == BIAS_FULL;
+    constexpr int kT5Pad = kT5Sat + kBN + 31;
+    __shared__ __attribute__((aligned(16))) uint16_t smem[4 * TILE];   // K slots 0-1, V slots 2-3
+    __shared__ float t5s[BIAS == BIAS_T5 ? 2 * kT5Pad + 1 : 1];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int hh = lane >> 5, r32 = lane & 31;
+    const WorkItem w = decode_work(p, blockIdx.x);
+    const int b = w.b, hq = w.hq, kvh = hq / p.G;
+    const int Sq = p.Sq, Sk = p.Sk, off = p.off;
+    const int q0 = w.qt * kBM;
+
+    const int pa = q0 + off, pb = min(q0 + kBM, Sq) - 1 + off;
+    int khi = Sk - 1, klo = 0;
+    if constexpr (MASK != MASK_NONE) khi = min(khi, pb);
+    if constexpr (MASK == MASK_SLIDING) klo = max(0, pa - p.window + 1);
+    const int t_begin = klo / kBN;
+    const int t_end = (khi < klo) ? t_begin : khi / kBN + 1;
+
+    const size_t q_row = (size_t)p.Hq * D, kv_row = (size_t)p.Hkv * D;
+    const uint16_t* qg = (const uint16_t*)p.q + ((size_t)b * Sq * p.Hq + hq) * D;
+    const uint16_t* dog = (const uint16_t*)p.dout + ((size_t)b * Sq * p.Hq + hq) * D;
+    const uint16_t* kg = (const uint16_t*)p.k + ((size_t)b * Sk * p.Hkv + kvh) * D;
+    const uint16_t* vg = (const uint16_t*)p.v + ((size_t)b * Sk * p.Hkv + kvh) * D;
+
+    const int wq0 = q0 + wave * 32, my_i = wq0 + r32;
+    const bool row_ok = my_i < Sq, wave_ok = wq0 < Sq;
+    const int my_pos = my_i + off;
+    const int pwa = wq0 + off, pwb = min(wq0 + 31, Sq - 1) + off;
+    char* dq_row = (char*)p.dq + (((size_t)b * Sq + (row_ok ? my_i : 0)) * q_row + (size_t)hq * D) * (OUT_F32 ? 4 : 2);
+
+    if (t_end == t_begin) {   // no row of the tile sees a key: dQ = 0
+        if (row_ok) store_zero_row<D, OUT_F32>(dq_row, hh);
+        return;
+    }
+    if constexpr (BIAS == BIAS_T5) {
+        const float* tbl = (const float*)p.bias + (size_t)hq * kT5Buckets;
+        for (int i = tid; i < 2 * kT5Pad + 1; i += kThreads) t5s[i] = tbl[t5_bucket(i - kT5Pad)] * kLog2e;
+    }
+
+    // A negative scale flips the sign of the Q fragment (S is unchanged); dQ = scale * dS K
+    // uses the signed scale. A zero scale computes P with the smallest normal float.
+    const bool neg = p.scale_log2 < 0.f;
+    const float c_scale = neg ? -p.scale_log2 : (p.scale_log2 == 0.f ? kTinyScale : p.scale_log2);
+    const float n_scale = neg ? -p.scale : (p.scale == 0.f ? kTinyScale : p.scale);
+    bf16x8 qf[KS], dof[KS];
+    {
+        const size_t ro = (size_t)(row_ok ? my_i : 0) * q_row + hh * 8;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            u32x4 x = *(const u32x4*)(qg + ro + ks * 16);
+            u32x4 y = *(const u32x4*)(dog + ro + ks * 16);
+            if (!row_ok) { x = u32x4{0, 0, 0, 0}; y = u32x4{0, 0, 0, 0}; }
+            if (neg) x ^= 0x80008000u;
+            qf[ks] = __builtin_bit_cast(bf16x8, x);
+            dof[ks] = __builtin_bit_cast(bf16x8, y);
+        }
+    }
+    // row constants: log-sum-exp in log2 units (+inf for a row with no visible key, so that
+    // its P is 0) and D_i
+    float lse2 = INFINITY, drow = 0.f;
+    if (row_ok) {
+        const float l = p.lse[((size_t)b * p.Hq + hq) * Sq + my_i];
+        lse2 = (l == -INFINITY) ? INFINITY : l * kLog2e;
+        drow = p.delta[((size_t)b * p.Hq + hq) * Sq + my_i];
+    }
+
+    // K and V tiles: 64 keys x D, row-major, swizzled chunks; 2 slots each
+    constexpr int ROWS_PER_XFER = 1024 / (D * 2), XFERS = (kBN * D * 2) / 1024, XPW = XFERS / kWaves;
+    static_assert(XPW * kWaves == XFERS, "dma split");
+    const uint32_t lds_base = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint16_t*)smem);
+    auto dma_tile = [&](int t) {
+        const int sl = (t - t_begin) & 1, j0 = t * kBN;
+#pragma unroll
+        for (int n = 0; n < XPW; ++n) {
+            const int xi = wave * XPW + n;
+            const int row = xi * ROWS_PER_XFER + lane / CH;
+            const int j = min(j0 + row, Sk - 1);
+            const int ch = ((lane % CH) ^ swz(row)) * 8;
+            dma16(kg + (size_t)j * kv_row + ch, lds_base + (uint32_t)((sl * TILE) * 2 + xi * 1024));
+            dma16(vg + (size_t)j * kv_row + ch, lds_base + (uint32_t)(((2 + sl) * TILE) * 2 + xi * 1024));
+        }
+    };
+
+    f32x16 dq_acc[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) dq_acc[db][v] = 0.f;
+
+    auto active = [&](int t) {
+        const int j0 = t * kBN;
+        bool skip = !wave_ok;
+        if constexpr (MASK != MASK_NONE) skip = skip || (j0 > pwb);
+        if constexpr (MASK == MASK_SLIDING) skip = skip || (j0 + kBN - 1 <= pwa - p.window);
+        return !skip;
+    };
+    auto needs_mask = [&](int t) {
+        const int j0 = t * kBN;
+        bool m = (j0 + kBN > Sk);
+        if constexpr (MASK != MASK_NONE) m = m || (j0 + kBN - 1 > pwa);
+        if constexpr (MASK == MASK_SLIDING) m = m || (j0 <= pwb - p.window);
+        return m;
+    };
+
+    auto compute_tile = [&](int t) {
+        const int sl = (t - t_begin) & 1, j0 = t * kBN;
+        const uint16_t* kb = smem + sl * TILE;
+        const uint16_t* vb = smem + (2 + sl) * TILE;
+        const bool msk = needs_mask(t);
+        // bias of the tile: constant for T5 far from the diagonal
+        bool per_elem = FB;
+        float bconst = 0.f;
+        if constexpr (BIAS == BIAS_T5) {
+            const int rmin = j0 - pwb, rmax = j0 + kBN - 1 - pwa;
+            if (rmin >= kT5Sat) bconst = t5s[2 * kT5Pad];
+            else if (rmax <= -kT5Sat) bconst = t5s[0];
+            else per_elem = true;
+        }
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb) {
+            const int jl = j0 + 32 * jb + 16 * hh;     // key of register 0 of this lane
+            f32x16 s, dp;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) { s[v] = 0.f; dp[v] = 0.f; }
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const bf16x8 ak = read_rows<D>(kb, jb, ks, lane);
+                const bf16x8 av = read_rows<D>(vb, jb, ks, lane);
+                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qf[ks], s, 0, 0, 0);
+                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, dof[ks], dp, 0, 0, 0);
+            }
+            // x = scores in log2 units including the bias, minus the row's log-sum-exp
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                float x;
+                if constexpr (BIAS == BIAS_T5) {
+                    if (per_elem) {
+                        const float* trow = t5s + kT5Pad + (jl - min(my_pos, pwb));
+                        x = fmaf(s[v], c_scale, trow[v]);
+                    } else {
+                        x = fmaf(s[v], c_scale, bconst);
+                    }
+                } else if constexpr (FB) {
+                    const int j = jl + v;
+                    const uint16_t* br = (const uint16_t*)p.bias +
+                        (((size_t)b * p.Hq + hq) * Sq + (row_ok ? my_i : 0)) * (size_t)Sk;
+                    const float bv = (row_ok && j < Sk) ? bf16_to_f32(br[j]) : 0.f;
+                    x = fmaf(bv, kLog2e, s[v] * c_scale);
+                } else {
+                    x = s[v] * c_scale;
+                }
+                if (msk) {
+                    const int j = jl + v;
+                    bool vis = j < Sk;
+                    if constexpr (MASK != MASK_NONE) vis = vis && (j <= my_pos);
+                    if constexpr (MASK == MASK_SLIDING) vis = vis && (my_pos - j < p.window);
+                    if (!vis) x = -INFINITY;
+                }
+                const float pv = __builtin_amdgcn_exp2f(x - lse2);
+                s[v] = pv * (dp[v] - drow);     // dS^T
+            }
+            // dQ^T += K^T dS^T over the two 16-key groups of this half
+#pragma unroll
+            for (int sg = 0; sg < 2; ++sg) {
+                u32x4 pk;
+#pragma unroll
+                for (int c = 0; c < 4; ++c) pk[c] = pack_bf16x2(s[8 * sg + 2 * c], s[8 * sg + 2 * c + 1]);
+                bf16x8 kt[DB];
+                read_tr<D>(kb, 2 * jb + sg, lane, kt);
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+                    dq_acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt[db], __builtin_bit_cast(bf16x8, pk), dq_acc[db], 0, 0, 0);
+            }
+        }
+    };
+
+    dma_tile(t_begin);
+    dma_wait();
+    __syncthreads();
+#pragma unroll 1
+    for (int t = t_begin; t < t_end; ++t) {
+        const bool has_next = t + 1 < t_end;
+        if (has_next) dma_tile(t + 1);
+        if (active(t)) compute_tile(t);
+        if (has_next) dma_wait();
+        __syncthreads();
+    }
+    if (row_ok) store_row<D, OUT_F32>(dq_row, dq_acc, p.scale, hh);
+}
+
+// ------------------------------------------------------------------------------------------
+// dK, dV: 128 keys of one (batch, KV head) per workgroup, query rows in steps of 64
+// ------------------------------------------------------------------------------------------
+template <int D, int MASK, int BIAS, bool OUT_F32>
+__global__ __launch_bounds__(256, 1) void dkdv_kernel(const BwdParams p) {
+    constexpr int kWaves = 4, kThreads = 256, kBK = 128, kBQ = 64;
+    constexpr int CH = D / 8, KS = D / 16, DB = D / 32, QT = kBQ * D;
+    constexpr bool FB = BIAS == BIAS_FULL;
+    constexpr int kT5Pad = kT5Sat + 64 + 31;
+    __shared__ __attribute__((aligned(16))) uint16_t smem[4 * QT];   // (Q, dO) x 2 slots
+    __shared__ __attribute__((aligned(16))) float rowc[2][2][kBQ];    // [slot][lse2, D][row]
+    __shared__ float t5s[BIAS == BIAS_T5 ? 2 * kT5Pad + 1 : 1];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int hh = lane >> 5, r32 = lane & 31;
+    const int kt_idx = blockIdx.x % p.n_kt, bk = blockIdx.x / p.n_kt;
+    const int b = bk / p.Hkv, kvh = bk - b * p.Hkv;
+    const int Sq = p.Sq, Sk = p.Sk, off = p.off, G = p.G;
+    const int k0 = kt_idx * kBK;
+    const int kw0 = k0 + 32 * wave;            // first key of this wave
+    const int my_j = kw0 + r32;                // key of this lane
+    const bool key_ok = my_j < Sk;
+    const bool wave_ok = kw0 < Sk;
+    const int kwe = min(kw0 + 31, Sk - 1);     // last valid key of the wave
+
+    const size_t q_row = (size_t)p.Hq * D, kv_row = (size_t)p.Hkv * D;
+    const size_t kv_off = ((size_t)b * Sk + (key_ok ? my_j : 0)) * kv_row + (size_t)kvh * D;
+    char* dk_row = (char*)p.dk + kv_off * (OUT_F32 ? 4 : 2);
+    char* dv_row = (char*)p.dv + kv_off * (OUT_F32 ? 4 : 2);
+
+    // query rows the workgroup's keys can see (positions of the rows: i + off)
+    const int kend = min(k0 + kBK, Sk) - 1;
+    int qlo = 0, qhi = Sq;
+    if constexpr (MASK != MASK_NONE) qlo = max(0, k0 - off);
+    if constexpr (MASK == MASK_SLIDING) qhi = min(Sq, kend + p.window - off);
+    const int s_begin = qlo / kBQ;
+    const int s_end = (qhi <= qlo) ? s_begin : (qhi + kBQ - 1) / kBQ;
+    const int nqs = s_end - s_begin;
+    const int n_steps = G * nqs;
+
+    if (n_steps == 0) {        // no query row sees these keys: dK = dV = 0
+        if (key_ok) {
+            store_zero_row<D, OUT_F32>(dk_row, hh);
+            store_zero_row<D, OUT_F32>(dv_row, hh);
+        }
+        return;
+    }
+    const bool neg = p.scale_log2 < 0.f;
+    const float c_scale = neg ? -p.scale_log2 : (p.scale_log2 == 0.f ? kTinyScale : p.scale_log2);
+    // K fragments (sign-flipped for a negative scale) and V fragments of this lane's key:
+    // dims 16 ks + 8 hh .. + 7 (B operands of S = Q.K^T and dP = dO.V^T)
+    bf16x8 kf[KS], vf[KS];
+    {
+        const uint16_t* kr = (const uint16_t*)p.k + kv_off + hh * 8;
+        const uint16_t* vr = (const uint16_t*)p.v + kv_off + hh * 8;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            u32x4 x = *(const u32x4*)(kr + ks * 16);
+            u32x4 y = *(const u32x4*)(vr + ks * 16);
+            if (!key_ok) { x = u32x4{0, 0, 0, 0}; y = u32x4{0, 0, 0, 0}; }
+            if (neg) x ^= 0x80008000u;
+            kf[ks] = __builtin_bit_cast(bf16x8, x);
+            vf[ks] = __builtin_bit_cast(bf16x8, y);
+        }
+    }
+
+    // Q / dO tiles of step n: head h = kvh * G + n / nqs, rows 64 s .. 64 s + 63 (clamped)
+    constexpr int ROWS_PER_XFER = 1024 / (D * 2), XFERS = (kBQ * D * 2) / 1024, XPW = XFERS / kWaves;
+    static_assert(XPW * kWaves == XFERS, "dma split");
+    const uint32_t lds_base = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint16_t*)smem);
+    auto issue_step = [&](int n) {
+        const int sl = n & 1;
+        const int h = kvh * G + n / nqs;
+        const int i0 = (s_begin + n % nqs) * kBQ;
+        const uint16_t* qg = (const uint16_t*)p.q + ((size_t)b * Sq * p.Hq + h) * D;
+        const uint16_t* dg = (const uint16_t*)p.dout + ((size_t)b * Sq * p.Hq + h) * D;
+#pragma unroll
+        for (int x = 0; x < XPW; ++x) {
+            const int xi = wave * XPW + x;
+            const int row = xi * ROWS_PER_XFER + lane / CH;
+            const int i = min(i0 + row, Sq - 1);
+            const int ch = ((lane % CH) ^ swz(row)) * 8;
+            dma16(qg + (size_t)i * q_row + ch, lds_base + (uint32_t)((2 * sl) * QT * 2 + xi * 1024));
+            dma16(dg + (size_t)i * q_row + ch, lds_base + (uint32_t)((2 * sl + 1) * QT * 2 + xi * 1024));
+        }
+        if (tid < kBQ) {
+            const int i = i0 + tid;
+            float l2 = INFINITY, dd = 0.f;
+            if (i < Sq) {
+                const size_t ri = ((size_t)b * p.Hq + h) * Sq + i;
+                const float l = p.lse[ri];
+                l2 = (l == -INFINITY) ? INFINITY : l * kLog2e;
+                dd = p.delta[ri];
+            }
+            rowc[sl][0][tid] = l2;
+            rowc[sl][1][tid] = dd;
+        }
+    };
+
+    f32x16 dk_acc[DB], dv_acc[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) { dk_acc[db][v] = 0.f; dv_acc[db][v] = 0.f; }
+    acc_fence_write(dk_acc);
+    acc_fence_write(dv_acc);
+
+    // one 32-row block (rows i0 + 32 qb ..) of step n against this wave's 32 keys
+    auto compute_block = [&](int n, int qb) {
+        const int sl = n & 1;
+        const int h = kvh * G + n / nqs;
+        const int r0 = (s_begin + n % nqs) * kBQ + 32 * qb;    // first query row of the block
+        const int pa = r0 + off, pb = min(r0 + 31, Sq - 1) + off;
+        if (!wave_ok || r0 >= Sq) return;
+        if constexpr (MASK != MASK_NONE) { if (pb < kw0) return; }
+        if constexpr (MASK == MASK_SLIDING) { if (pa - kwe >= p.window) return; }
+        bool msk = (r0 + 31 >= Sq) || (kw0 + 31 >= Sk);
+        if constexpr (MASK != MASK_NONE) msk = msk || (pa < kwe);
+        if constexpr (MASK == MASK_SLIDING) msk = msk || (pb - kw0 >= p.window);
+        bool per_elem = FB;
+        float bconst = 0.f;
+        if constexpr (BIAS == BIAS_T5) {
+            const int rmin = kw0 - pb, rmax = kwe - pa;
+            if (rmin >= kT5Sat) bconst = t5s[2 * kT5Pad];
+            else if (rmax <= -kT5Sat) bconst = t5s[0];
+            else per_elem = true;
+        }
+        const uint16_t* qt = smem + (2 * sl) * QT;
+        const uint16_t* dt = smem + (2 * sl + 1) * QT;
+        f32x16 s, dp;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) { s[v] = 0.f; dp[v] = 0.f; }
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const bf16x8 aq = read_rows<D>(qt, qb, ks, lane);
+            const bf16x8 ad = read_rows<D>(dt, qb, ks, lane);
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kf[ks], s, 0, 0, 0);
+            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, vf[ks], dp, 0, 0, 0);
+        }
+        // register v of lane half hh: query row r0 + 16 hh + v, key my_j
+        const int rl = 32 * qb + 16 * hh;                      // row of register 0 in the tile
+        const int pos0 = r0 + 16 * hh + off;                   // its position
+        float lrow[16], drow[16];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const u32x4 a = *(const u32x4*)(&rowc[sl][0][rl + 4 * c]);
+            const u32x4 d = *(const u32x4*)(&rowc[sl][1][rl + 4 * c]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) { lrow[4 * c + e] = __uint_as_float(a[e]); drow[4 * c + e] = __uint_as_float(d[e]); }
+        }
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            float x;
+            if constexpr (BIAS == BIAS_T5) {
+                if (per_elem) {
+                    // rel = my_j - position of row v; stays inside the padded table
+                    const float* trow = t5s + kT5Pad + (my_j - pos0);
+                    x = fmaf(s[v], c_scale, trow[-v]);
+                } else {
+                    x = fmaf(s[v], c_scale, bconst);
+                }
+            } else if constexpr (FB) {
+                const int i = r0 + 16 * hh + v;
+                const uint16_t* br = (const uint16_t*)p.bias + ((size_t)b * p.Hq + h) * Sq * (size_t)Sk;
+                const float bv = (i < Sq && key_ok) ? bf16_to_f32(br[(size_t)i * Sk + my_j]) : 0.f;
+                x = fmaf(bv, kLog2e, s[v] * c_scale);
+            } else {
+                x = s[v] * c_scale;
+            }
+            if (msk) {
+                const int pos = pos0 + v;
+                bool vis = key_ok && (pos - off < Sq);
+                if constexpr (MASK != MASK_NONE) vis = vis && (my_j <= pos);
+                if constexpr (MASK == MASK_SLIDING) vis = vis && (pos - my_j < p.window);
+                if (!vis) x = -INFINITY;
+            }
+            const float pv = __builtin_amdgcn_exp2f(x - lrow[v]);
+            dp[v] = pv * (dp[v] - drow[v]);      // dS
+            s[v] = pv;                            // P
+        }
+        // dV^T += dO^T P and dK^T += Q^T dS over the two 16-row groups of the block
+#pragma unroll
+        for (int sg = 0; sg < 2; ++sg) {
+            u32x4 pp, pd;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                pp[c] = pack_bf16x2(s[8 * sg + 2 * c], s[8 * sg + 2 * c + 1]);
+                pd[c] = pack_bf16x2(dp[8 * sg + 2 * c], dp[8 * sg + 2 * c + 1]);
+            }
+            bf16x8 at[DB];
+            read_tr<D>(dt, 2 * qb + sg, lane, at);
+            const bf16x8 bp = __builtin_bit_cast(bf16x8, pp), bd = __builtin_bit_cast(bf16x8, pd);
+#pragma unroll
+            for (int db = 0; db < DB; ++db) mfma_acc(dv_acc[db], at[db], bp);
+            read_tr<D>(qt, 2 * qb + sg, lane, at);
+#pragma unroll
+            for (int db = 0; db < DB; ++db) mfma_acc(dk_acc[db], at[db], bd);
+        }
+    };
+
+    issue_step(0);
+    dma_wait();
+    __syncthreads();
+    int cur_h = -1;
+#pragma unroll 1
+    for (int n = 0; n < n_steps; ++n) {
+        const int h = kvh * G + n / nqs;
+        if constexpr (BIAS == BIAS_T5) {
+            if (h != cur_h) {
+                // table of head h (no reader of the previous table is still running: the
+                // barrier ending the previous step, and one after the writes)
+                const float* tbl = (const float*)p.bias + (size_t)h * kT5Buckets;
+                for (int i = tid; i < 2 * kT5Pad + 1; i += kThreads) t5s[i] = tbl[t5_bucket(i - kT5Pad)] * kLog2e;
+                __syncthreads();
+            }
+        }
+        cur_h = h;
+        const bool has_next = n + 1 < n_steps;
+        if (has_next) issue_step(n + 1);
+        compute_block(n, 0);
+        compute_block(n, 1);
+        if (has_next) dma_wait();
+        __syncthreads();
+    }
+    acc_fence_read(dk_acc);
+    acc_fence_read(dv_acc);
+    if (key_ok) {
+        store_row<D, OUT_F32>(dk_row, dk_acc, p.scale, hh);
+        store_row<D, OUT_F32>(dv_row, dv_acc, 1.f, hh);
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// host-side launch
+// ------------------------------------------------------------------------------------------
+template <int D, int MASK, int BIAS, bool OUT_F32>
+static hipError_t launch_grads(const BwdParams& p, hipStream_t s) {
+    const unsigned gq = (unsigned)((size_t)p.B * p.Hq * p.n_qt);
+    hipLaunchKernelGGL((dq_kernel<D, MASK, BIAS, OUT_F32>), dim3(gq), dim3(512), 0, s, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const unsigned gk = (unsigned)((size_t)p.B * p.Hkv * p.n_kt);
+    hipLaunchKernelGGL((dkdv_kernel<D, MASK, BIAS, OUT_F32>), dim3(gk), dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
+template <int D, bool OUT_F32>
+static hipError_t launch_d(const BwdParams& p, int mask, int bias, hipStream_t s) {
+#define SDPA_CASE(M, Bk) \
+    if (mask == M && bias == Bk) return launch_grads<D, M, Bk, OUT_F32>(p, s);
+    SDPA_CASE(MASK_NONE, BIAS_NONE) SDPA_CASE(MASK_NONE, BIAS_T5) SDPA_CASE(MASK_NONE, BIAS_FULL)
+    SDPA_CASE(MASK_CAUSAL, BIAS_NONE) SDPA_CASE(MASK_CAUSAL, BIAS_T5) SDPA_CASE(MASK_CAUSAL, BIAS_FULL)
+    SDPA_CASE(MASK_SLIDING, BIAS_NONE) SDPA_CASE(MASK_SLIDING, BIAS_T5) SDPA_CASE(MASK_SLIDING, BIAS_FULL)
+#undef SDPA_CASE
+    return hipErrorInvalidValue;
+}
+
+}  // namespace bwd
+
+hipError_t launch_bwd_bf16(BwdParams p, int D, int mask, int bias, bool out_f32, hipStream_t s) {
+    p.n_qt = (p.Sq + 255) / 256;
+    p.n_kt = (p.Sk + 127) / 128;
+    p.xcd_remap = ((p.B * p.Hkv) % 8 == 0) ? 1 : 0;
+    const long long rows = (long long)p.B * p.Sq * p.Hq;
+    const unsigned gd = (unsigned)((rows + 255) / 256);
+    if (D == 128) hipLaunchKernelGGL((bwd::delta_kernel<128>), dim3(gd), dim3(256), 0, s, p);
+    else if (D == 64) hipLaunchKernelGGL((bwd::delta_kernel<64>), dim3(gd), dim3(256), 0, s, p);
+    else return hipErrorInvalidValue;
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (D == 128) return out_f32 ? bwd::launch_d<128, true>(p, mask, bias, s) : bwd::launch_d<128, false>(p, mask, bias, s);
+    return out_f32 ? bwd::launch_d<64, true>(p, mask, bias, s) : bwd::launch_d<64, false>(p, mask, bias, s);
+}
+
+}  // namespace sdpa

@@ -31,6 +31,30 @@ struct FwdParams {
     float scale_log2;    // scale * log2(e)
 };
 
+// Backward: gradients of L = sum(dO * O) for the forward above.
+struct BwdParams {
+    const void* q;       // [B][Sq][Hq][D] bf16
+    const void* k;       // [B][Sk][Hkv][D] bf16
+    const void* v;       // [B][Sk][Hkv][D] bf16
+    const void* o;       // [B][Sq][Hq][D] bf16: the forward's output
+    const float* lse;    // [B][Hq][Sq]: the forward's row log-sum-exp
+    const void* dout;    // [B][Sq][Hq][D] bf16: dL/dO
+    void* dq;            // [B][Sq][Hq][D]  bf16 or fp32
+    void* dk;            // [B][Sk][Hkv][D] bf16 or fp32
+    void* dv;            // [B][Sk][Hkv][D] bf16 or fp32
+    float* delta;        // [B][Hq][Sq] workspace: rowsum(dO * O)
+    const void* bias;    // T5 table [Hq][32] fp32, or full bias [B][Hq][Sq][Sk] bf16
+    int B, Hq, Hkv, Sq, Sk;
+    int G;               // Hq / Hkv
+    int off;             // Sk - Sq
+    int window;
+    int n_qt;            // 256-row query tiles per (batch, query head)   (dQ kernel)
+    int n_kt;            // 128-key tiles per (batch, KV head)            (dK/dV kernel)
+    int xcd_remap;
+    float scale;
+    float scale_log2;
+};
+
 // T5 bidirectional bucket of rel = key position - query position (integer form of the T5 log
 // spacing: for 8 <= n < 91 the bucket 8 + floor(8 log(n/8) / log 16) equals 1 + bitlen(n^2)).
 __host__ __device__ inline int t5_bucket(int rel) {
@@ -54,7 +78,8 @@ __host__ __device__ inline int t5_bucket(int rel) {
 // whole (batch, KV head) groups so the G query heads sharing K/V hit the same L2.
 struct WorkItem { int b, hq, qt; };
 
-__host__ __device__ inline WorkItem decode_work(const FwdParams& p, int x) {
+template <class Params>
+__host__ __device__ inline WorkItem decode_work(const Params& p, int x) {
     const int per_group = p.G * p.n_qt;
     int group, r;
     if (p.xcd_remap) {

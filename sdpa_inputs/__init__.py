@@ -47,7 +47,8 @@ class Workload:
     mask_kind: int
     window: int = 0
     bias_kind: int = BIAS_NONE
-    seed: int = 0         # base seed; q = seed, k = seed+1, v = seed+2, t5 table = seed+3, bias = seed+4
+    seed: int = 0         # base seed; q = seed, k = seed+1, v = seed+2, t5 table = seed+3,
+    #                       bias = seed+4, dO (backward) = seed+5
     kv_seed: Optional[int] = None   # overrides the k/v seed base (k = kv_seed+1, v = kv_seed+2)
     bias_std: float = 0.5
     scale_override: Optional[float] = None   # softmax scale; default 1/sqrt(D)
@@ -177,6 +178,12 @@ def make_inputs(wl: Workload) -> Inputs:
         inp.bias = _store(normal_f32(wl.seed + 4, (wl.B, wl.Hq, wl.Sq, wl.Sk), wl.bias_std),
                           wl.dtype)
     return inp
+
+
+def make_dout(wl: Workload) -> np.ndarray:
+    """The output gradient dL/dO [B, Sq, Hq, D] for the backward, in the workload's dtype:
+    N(0, 1) draws from seed + 5 (the weights of an arbitrary linear loss sum(dO * O))."""
+    return _store(normal_f32(wl.seed + 5, (wl.B, wl.Sq, wl.Hq, wl.D)), wl.dtype)
 
 
 def small(wl: Workload, *, B=None, Hq=None, Hkv=None, Sq=None, Sk=None, window=None,

@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.sdpa_abi_version() == 1
+    assert lib.sdpa_abi_version() == sdpa.ABI_VERSION == 2
     for code in range(0, 11):
         s = sdpa.status_str(code)
         assert s and s != "unknown status"
@@ -105,3 +105,45 @@ def test_binding_rejects_before_launch(lib):
     q = torch.zeros(1, 8, 2, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         sdpa.fwd(q, q, q)            # cpu tensors are refused by the binding
+
+
+# backward: same validation as the forward, plus its own pointers
+GOOD_BWD = dict(GOOD, dout=P, dq=P, dk=P, dv=P, ws=P)
+
+
+def call_bwd(entry="sdpa_bwd", **kw):
+    a = dict(GOOD_BWD)
+    a.update(kw)
+    return sdpa.call_raw_bwd(entry, a["q"], a["k"], a["v"], a["out"], a["lse"], a["dout"],
+                             a["dq"], a["dk"], a["dv"], a["ws"], a["B"], a["Hq"], a["Hkv"],
+                             a["Sq"], a["Sk"], a["D"], a["scale"], a["mask_kind"], a["window"],
+                             a["bias_kind"], a["bias"], a["stream"])
+
+
+BWD_CASES = BAD_CASES + [
+    ("null dout", dict(dout=None), 1),
+    ("null dq", dict(dq=None), 1),
+    ("null dk", dict(dk=None), 1),
+    ("null dv", dict(dv=None), 1),
+    ("null ws", dict(ws=None), 1),
+    ("misaligned dout", dict(dout=P + 2), 9),
+    ("misaligned dq", dict(dq=P + 8), 9),
+    ("misaligned dk", dict(dk=P + 4), 9),
+    ("misaligned dv", dict(dv=P + 2), 9),
+    ("misaligned ws", dict(ws=P + 2), 9),
+]
+
+
+@pytest.mark.parametrize("entry", ["sdpa_bwd", "sdpa_bwd_f32out"])
+@pytest.mark.parametrize("name,kw,code", BWD_CASES, ids=[c[0] for c in BWD_CASES])
+def test_backward_invalid_arguments_return_status(lib, entry, name, kw, code):
+    assert call_bwd(entry, **kw) == code
+
+
+def test_backward_binding_rejects_before_launch(lib):
+    torch = pytest.importorskip("torch")
+    q = torch.zeros(1, 8, 2, 64, dtype=torch.bfloat16)
+    lse = torch.zeros(1, 2, 8)
+    with pytest.raises(ValueError):
+        sdpa.bwd(q, q, q, q, lse, q)  # cpu tensors are refused by the binding
+

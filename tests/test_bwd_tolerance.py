@@ -1,0 +1,113 @@
+"""CPU checks of the gradient error bars in bwd_check.py (no GPU).
+
+An fp32 / bf16 emulation of the gradient kernels' rounding (scores and sums in fp32, P and dS
+rounded to bf16 before their products, the row constant from a bf16 forward output, P from an
+fp32 LSE) must pass both bars against the fp64 oracle; the same emulation with a planted
+mistake must fail at least one of them. This pins the bars from both sides: not tighter than
+the arithmetic allows, not so loose that a wrong gradient passes.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import sdpa_inputs as si
+from bwd_check import check_grad, pair_reference
+
+LOG2E = np.float32(1.4426950408889634)
+
+
+def bf16(x):
+    return si.bf16_bits_to_f32(si.f32_to_bf16_bits(np.asarray(x, np.float32)))
+
+
+def emulate(q, k, v, dout, o16, lse32, b, kvh, scale, mask, window, bias_kind, bias, plant=None):
+    """fp32 emulation of the kernels for one (b, KV head): returns dq [Sq, G, D], dk, dv."""
+    B, Sq, Hq, D = q.shape
+    Sk, Hkv = k.shape[1], k.shape[2]
+    G = Hq // Hkv
+    q_pos = np.arange(Sq) + (Sk - Sq)
+    vis = oracle.visible(q_pos, Sk, mask, window + (1 if plant == "window_off_by_one" else 0))
+    k_h = k[b, :, kvh].astype(np.float32)
+    v_h = v[b, :, kvh].astype(np.float32)
+    dq = np.zeros((Sq, G, D), np.float32)
+    dk = np.zeros((Sk, D), np.float32)
+    dv = np.zeros((Sk, D), np.float32)
+    sl2 = np.float32(scale) * LOG2E
+    for g in range(G):
+        h = kvh * G + g
+        q_h = q[b, :, h].astype(np.float32)
+        do_h = dout[b, :, h].astype(np.float32)
+        x = (q_h @ k_h.T) * sl2
+        if bias_kind == oracle.BIAS_T5:
+            rel = np.arange(Sk)[None, :] - q_pos[:, None]
+            x = x + bias[h][oracle.t5_bucket(rel)].astype(np.float32) * LOG2E
+        elif bias_kind == oracle.BIAS_FULL:
+            x = x + bias[b, h].astype(np.float32) * LOG2E
+        x = np.where(vis, x, -np.inf).astype(np.float32)
+        l2 = lse32[b, h] * LOG2E
+        l2 = np.where(np.isfinite(l2), l2, np.inf).astype(np.float32)
+        with np.errstate(invalid="ignore"):
+            p = np.exp2(x - l2[:, None]).astype(np.float32)
+        p = np.where(np.isnan(p), 0, p).astype(np.float32)
+        delta = np.sum(do_h * o16[b, :, h].astype(np.float32), axis=1, dtype=np.float32)
+        if plant == "no_row_constant":
+            delta = np.zeros_like(delta)
+        dp = do_h @ v_h.T
+        ds = p * (dp - delta[:, None])
+        pb, dsb = bf16(p), bf16(ds)
+        kk = np.roll(k_h, 1, axis=0) if plant == "dq_key_shift" else k_h
+        dq[:, g] = np.float32(scale) * (dsb @ kk)
+        dk += (np.float32(1.0) if plant == "dk_no_scale" else np.float32(scale)) * (dsb.T @ q_h)
+        dv += pb.T @ (do_h if plant != "dv_uses_q" else q_h)
+    return dq, dk, dv
+
+
+CASES = [  # B, Sq, Sk, Hq, Hkv, D, mask, window, bias_kind
+    (1, 150, 150, 4, 2, 64, oracle.MASK_CAUSAL, 0, oracle.BIAS_NONE),
+    (1, 130, 190, 2, 1, 128, oracle.MASK_SLIDING, 40, oracle.BIAS_NONE),
+    (1, 120, 120, 2, 2, 64, oracle.MASK_NONE, 0, oracle.BIAS_T5),
+    (1, 96, 96, 2, 2, 64, oracle.MASK_NONE, 0, oracle.BIAS_FULL),
+]
+
+
+def _case(c, seed):
+    B, Sq, Sk, Hq, Hkv, D, mask, window, bk = c
+    wl = si.Workload("tol", B, Hq, Hkv, Sq, Sk, D, "bf16", mask, window=window, bias_kind=bk,
+                     seed=seed)
+    inp = si.make_inputs(wl)
+    q, k, v, extra = inp.as_f64()
+    do = si.bf16_bits_to_f64(si.make_dout(wl))
+    o, lse = oracle.sdpa_forward(q, k, v, scale=wl.scale, mask_kind=mask, window=window,
+                                 bias_kind=bk, bias=extra)
+    o16 = bf16(o.astype(np.float32)).astype(np.float64)           # the forward's bf16 output
+    lse32 = lse.astype(np.float32)                                  # and its fp32 LSE
+    return wl, q, k, v, extra, do, o16, lse32
+
+
+def _verdict(c, seed, plant):
+    wl, q, k, v, extra, do, o16, lse32 = _case(c, seed)
+    G = wl.Hq // wl.Hkv
+    for kvh in range(wl.Hkv):
+        ref = pair_reference(q, k, v, do, o16, lse32.astype(np.float64), 0, kvh, scale=wl.scale,
+                             mask_kind=wl.mask_kind, window=wl.window, bias_kind=wl.bias_kind,
+                             bias=extra)
+        got = emulate(q, k, v, do, o16, lse32, 0, kvh, wl.scale, wl.mask_kind, wl.window,
+                      wl.bias_kind, extra, plant)
+        assert got[0].shape == (wl.Sq, G, wl.D)
+        for name, g, r, bd in (("dq", got[0], ref["dq"], ref["bound_dq"]),
+                               ("dk", got[1], ref["dk"], ref["bound_dk"]),
+                               ("dv", got[2], ref["dv"], ref["bound_dv"])):
+            check_grad(name, g.astype(np.float64), r, bd)
+
+
+@pytest.mark.parametrize("c", CASES, ids=[f"case{i}" for i in range(len(CASES))])
+def test_emulated_kernel_rounding_passes(c):
+    _verdict(c, 77, None)
+
+
+@pytest.mark.parametrize("plant", ["no_row_constant", "dq_key_shift", "dk_no_scale", "dv_uses_q",
+                                   "window_off_by_one"])
+def test_planted_mistakes_fail(plant):
+    c = CASES[1] if plant == "window_off_by_one" else CASES[0]
+    with pytest.raises(AssertionError):
+        _verdict(c, 78, plant)
