@@ -5,13 +5,14 @@
 // sharing of codelab section 9). With P the softmax weights (recomputed from the forward's
 // row log-sum-exp) and D_i = rowsum(dO_i * O_i):
 //     dV = P^T dO,  dP = dO V^T,  dS = P * (dP - D),  dQ = scale * dS K,  dK = scale * dS^T Q.
-// Three launches, each output element written once, fixed summation order, no atomics, so the
+// Two launches, each output element written once, fixed summation order, no atomics, so the
 // gradients are bitwise reproducible run to run (the determinism asked of a training step in
 // the transformers issue "Transformer models are not deterministic when using Flash Attention 2").
 //
-//   delta_kernel : D_i = rowsum(dO_i * O_i) for every query row, into the caller's workspace.
 //   dq_kernel    : one workgroup = 8 waves = 256 query rows of one (batch, query head), like the
-//                  forward: Q and dO fragments stay in VGPRs, K and V tiles of 64 keys stream
+//                  forward. It first forms D_i = rowsum(dO_i * O_i) for its rows and stores it
+//                  in the caller's workspace for the second launch. Q and dO fragments stay in
+//                  VGPRs, K and V tiles of 64 keys stream
 //                  through 2-slot LDS rings (LDS DMA). Per 32-key half: S^T = K.Q^T and
 //                  dP^T = V.dO^T (lane = query row, 16 keys per lane half), P and dS^T in
 //                  registers, then dQ^T += K^T.dS^T with K^T from transposing LDS reads.
@@ -51,10 +52,24 @@ __device__ __forceinline__ int perm32(int r) {
     return ((r >> 2) & 1) * 16 + (r >> 3) * 4 + (r & 3);
 }
 // XOR swizzle of the 16-byte chunk index of a tile row. The backward reads each streamed tile
-// both row-wise (ds_read_b128, 8 lanes on rows {0..3, 16..19} + 4g) and through transposing
-// reads (16 lanes on 4 consecutive rows): bits 0-1 of the row spread the transposing reads,
-// bit 4 separates rows r and r + 16 for the row-wise reads.
-__device__ __forceinline__ int swz(int row) { return (2 * (row & 3)) | ((row >> 4) & 1); }
+// both row-wise (ds_read_b128: 16 lanes per LDS cycle on rows {0..3, 16..19, 4..7, 20..23}
+// + 8m, one chunk each) and through transposing reads (ds_read_b64_tr_b16: 32 lanes per
+// cycle on 4 consecutive rows, chunks c + {0, 1, 2DB, 2DB + 1}). Row bits 0-1 (D = 128) or bit
+// 1 (D = 64, two rows per 256-byte bank line) pick distinct chunk pairs for the transposing
+// reads; row bits 2 and 4 fill the remaining swizzle bits so the 16 rows of a row-wise read
+// land on 16 distinct chunks of the bank line.
+template <int D>
+__device__ __forceinline__ int swz(int row) {
+    if constexpr (D == 128)
+        return (2 * (row & 3)) | ((row >> 4) & 1) | (((row >> 2) & 1) << 3);
+    else
+        return (row & 2) | ((row >> 4) & 1) | (((row >> 2) & 1) << 2);
+}
+
+// A value the caller knows to be equal in every lane of the wave, made visibly uniform to the
+// compiler so that branches on it stay scalar.
+__device__ __forceinline__ bool uniform(bool b) { return __builtin_amdgcn_readfirstlane((int)b) != 0; }
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
@@ -62,6 +77,11 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     r[0] = (__bf16)lo;
     r[1] = (__bf16)hi;
     return __builtin_bit_cast(uint32_t, r);
+}
+__device__ __forceinline__ float partner_sum(float x) {
+    // this lane's value plus that of lane l ^ 32 (same result in both lanes)
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 __device__ __forceinline__ s16x4 lds_read_tr(const uint16_t* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
@@ -107,13 +127,12 @@ __device__ __forceinline__ void read_tr(const uint16_t* tile, int g, int lane, b
     const int hh = lane >> 5, gg = lane >> 4, li = lane & 15, la = li & 3;
     const int row = 16 * hh + (li >> 2) + 32 * (g >> 1) + 8 * (g & 1);
     const int dlo = 16 * DB * (gg & 1) + 8 * (la & 1) + 4 * (la >> 1);
-    const int sw = swz(row);                // same for row + 4
+    const int sw0 = swz<D>(row), sw1 = swz<D>(row + 4);
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
         const int d = 16 * db + dlo;
-        const int coff = (((d >> 3) ^ sw) << 3) + (d & 7);
-        const s16x4 lo = lds_read_tr(tile + row * D + coff);
-        const s16x4 hi = lds_read_tr(tile + (row + 4) * D + coff);
+        const s16x4 lo = lds_read_tr(tile + row * D + ((((d >> 3) ^ sw0) << 3) | (d & 7)));
+        const s16x4 hi = lds_read_tr(tile + (row + 4) * D + ((((d >> 3) ^ sw1) << 3) | (d & 7)));
         u32x4 av;
         av[0] = __builtin_bit_cast(u32x2, lo)[0];
         av[1] = __builtin_bit_cast(u32x2, lo)[1];
@@ -128,7 +147,7 @@ __device__ __forceinline__ void read_tr(const uint16_t* tile, int g, int lane, b
 template <int D>
 __device__ __forceinline__ bf16x8 read_rows(const uint16_t* tile, int blk, int ks, int lane) {
     const int row = perm32(lane & 31) + 32 * blk;
-    const int ch = ((2 * ks + (lane >> 5)) ^ swz(row)) * 8;
+    const int ch = ((2 * ks + (lane >> 5)) ^ swz<D>(row)) * 8;
     return *(const bf16x8*)(tile + row * D + ch);
 }
 
@@ -172,31 +191,6 @@ __device__ __forceinline__ void store_zero_row(char* dst, int hh) {
 }
 
 // ------------------------------------------------------------------------------------------
-// D_i = rowsum(dO_i * O_i): one thread per query row, head dims ascending
-// ------------------------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(256) void delta_kernel(const BwdParams p) {
-    const long long r = (long long)blockIdx.x * 256 + threadIdx.x;   // (b * Sq + i) * Hq + h
-    if (r >= (long long)p.B * p.Sq * p.Hq) return;
-    const int h = (int)(r % p.Hq);
-    const long long bi = r / p.Hq;
-    const int i = (int)(bi % p.Sq), b = (int)(bi / p.Sq);
-    const uint16_t* o = (const uint16_t*)p.o + r * D;
-    const uint16_t* g = (const uint16_t*)p.dout + r * D;
-    float acc = 0.f;
-#pragma unroll
-    for (int c = 0; c < D; c += 8) {
-        const u32x4 a = *(const u32x4*)(o + c), x = *(const u32x4*)(g + c);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            acc = fmaf(bf16_to_f32(a[e] & 0xffffu), bf16_to_f32(x[e] & 0xffffu), acc);
-            acc = fmaf(bf16_to_f32(a[e] >> 16), bf16_to_f32(x[e] >> 16), acc);
-        }
-    }
-    p.delta[((size_t)b * p.Hq + h) * p.Sq + i] = acc;
-}
-
-// ------------------------------------------------------------------------------------------
 // dQ: 256 query rows per workgroup, 64-key tiles
 // ------------------------------------------------------------------------------------------
 template <int D, int MASK, int BIAS, bool OUT_F32>
@@ -234,6 +228,32 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(const BwdParams p) {
     const int pwa = wq0 + off, pwb = min(wq0 + 31, Sq - 1) + off;
     char* dq_row = (char*)p.dq + (((size_t)b * Sq + (row_ok ? my_i : 0)) * q_row + (size_t)hq * D) * (OUT_F32 ? 4 : 2);
 
+    // dO fragment of this lane's row (dims 16 ks + 8 hh .. + 7, the B operand of dP^T) and the
+    // row constant D_i = rowsum(dO_i * O_i): each lane half sums its 64 (or 32) dims in
+    // ascending order, then the halves are added. Written to the workspace for the dK/dV
+    // kernel, which runs after this one on the same stream.
+    const size_t ro = (size_t)(row_ok ? my_i : 0) * q_row + hh * 8;
+    bf16x8 dof[KS];
+    float drow;
+    {
+        const uint16_t* og = (const uint16_t*)p.o + ((size_t)b * Sq * p.Hq + hq) * D;
+        float part = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            u32x4 y = *(const u32x4*)(dog + ro + ks * 16);
+            u32x4 o = *(const u32x4*)(og + ro + ks * 16);
+            if (!row_ok) { y = u32x4{0, 0, 0, 0}; o = u32x4{0, 0, 0, 0}; }
+            dof[ks] = __builtin_bit_cast(bf16x8, y);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                part = fmaf(bf16_to_f32(y[e] & 0xffffu), bf16_to_f32(o[e] & 0xffffu), part);
+                part = fmaf(bf16_to_f32(y[e] >> 16), bf16_to_f32(o[e] >> 16), part);
+            }
+        }
+        drow = partner_sum(part);
+        if (row_ok && hh == 0) p.delta[((size_t)b * p.Hq + hq) * Sq + my_i] = drow;
+    }
+
     if (t_end == t_begin) {   // no row of the tile sees a key: dQ = 0
         if (row_ok) store_zero_row<D, OUT_F32>(dq_row, hh);
         return;
@@ -247,27 +267,20 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(const BwdParams p) {
     // uses the signed scale. A zero scale computes P with the smallest normal float.
     const bool neg = p.scale_log2 < 0.f;
     const float c_scale = neg ? -p.scale_log2 : (p.scale_log2 == 0.f ? kTinyScale : p.scale_log2);
-    const float n_scale = neg ? -p.scale : (p.scale == 0.f ? kTinyScale : p.scale);
-    bf16x8 qf[KS], dof[KS];
-    {
-        const size_t ro = (size_t)(row_ok ? my_i : 0) * q_row + hh * 8;
+    bf16x8 qf[KS];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            u32x4 x = *(const u32x4*)(qg + ro + ks * 16);
-            u32x4 y = *(const u32x4*)(dog + ro + ks * 16);
-            if (!row_ok) { x = u32x4{0, 0, 0, 0}; y = u32x4{0, 0, 0, 0}; }
-            if (neg) x ^= 0x80008000u;
-            qf[ks] = __builtin_bit_cast(bf16x8, x);
-            dof[ks] = __builtin_bit_cast(bf16x8, y);
-        }
+    for (int ks = 0; ks < KS; ++ks) {
+        u32x4 x = *(const u32x4*)(qg + ro + ks * 16);
+        if (!row_ok) x = u32x4{0, 0, 0, 0};
+        if (neg) x ^= 0x80008000u;
+        qf[ks] = __builtin_bit_cast(bf16x8, x);
     }
-    // row constants: log-sum-exp in log2 units (+inf for a row with no visible key, so that
-    // its P is 0) and D_i
-    float lse2 = INFINITY, drow = 0.f;
+    // log-sum-exp of the row in log2 units (+inf for a row with no visible key, so that its
+    // P is 0)
+    float lse2 = INFINITY;
     if (row_ok) {
         const float l = p.lse[((size_t)b * p.Hq + hq) * Sq + my_i];
         lse2 = (l == -INFINITY) ? INFINITY : l * kLog2e;
-        drow = p.delta[((size_t)b * p.Hq + hq) * Sq + my_i];
     }
 
     // K and V tiles: 64 keys x D, row-major, swizzled chunks; 2 slots each
@@ -281,7 +294,7 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(const BwdParams p) {
             const int xi = wave * XPW + n;
             const int row = xi * ROWS_PER_XFER + lane / CH;
             const int j = min(j0 + row, Sk - 1);
-            const int ch = ((lane % CH) ^ swz(row)) * 8;
+            const int ch = ((lane % CH) ^ swz<D>(row)) * 8;
             dma16(kg + (size_t)j * kv_row + ch, lds_base + (uint32_t)((sl * TILE) * 2 + xi * 1024));
             dma16(vg + (size_t)j * kv_row + ch, lds_base + (uint32_t)(((2 + sl) * TILE) * 2 + xi * 1024));
         }
@@ -312,14 +325,15 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(const BwdParams p) {
         const int sl = (t - t_begin) & 1, j0 = t * kBN;
         const uint16_t* kb = smem + sl * TILE;
         const uint16_t* vb = smem + (2 + sl) * TILE;
-        const bool msk = needs_mask(t);
+        const bool msk = uniform(needs_mask(t));
         // bias of the tile: constant for T5 far from the diagonal
         bool per_elem = FB;
         float bconst = 0.f;
         if constexpr (BIAS == BIAS_T5) {
             const int rmin = j0 - pwb, rmax = j0 + kBN - 1 - pwa;
-            if (rmin >= kT5Sat) bconst = t5s[2 * kT5Pad];
-            else if (rmax <= -kT5Sat) bconst = t5s[0];
+            const int side = uniform(rmin >= kT5Sat ? 1 : (rmax <= -kT5Sat ? -1 : 0));
+            if (side > 0) bconst = t5s[2 * kT5Pad];
+            else if (side < 0) bconst = t5s[0];
             else per_elem = true;
         }
 #pragma unroll
@@ -387,7 +401,7 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(const BwdParams p) {
     for (int t = t_begin; t < t_end; ++t) {
         const bool has_next = t + 1 < t_end;
         if (has_next) dma_tile(t + 1);
-        if (active(t)) compute_tile(t);
+        if (uniform(active(t))) compute_tile(t);
         if (has_next) dma_wait();
         __syncthreads();
     }
@@ -395,25 +409,44 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(const BwdParams p) {
 }
 
 // ------------------------------------------------------------------------------------------
-// dK, dV: 128 keys of one (batch, KV head) per workgroup, query rows in steps of 64
+// dK, dV: 128 keys of one (batch, KV head) per workgroup, query rows in steps of 128.
+// Waves 0-3 accumulate dV and waves 4-7 dK for the same four 32-key groups, so each wave holds
+// one 32 x D accumulator and two waves share every SIMD. Both roles form S = Q.K^T with the
+// same instructions (so their P agree bit for bit); the dK waves also form dP = dO.V^T.
 // ------------------------------------------------------------------------------------------
 template <int D, int MASK, int BIAS, bool OUT_F32>
-__global__ __launch_bounds__(256, 1) void dkdv_kernel(const BwdParams p) {
-    constexpr int kWaves = 4, kThreads = 256, kBK = 128, kBQ = 64;
+__global__ __launch_bounds__(512, 1) void dkdv_kernel(const BwdParams p) {
+    constexpr int kWaves = 8, kThreads = 512, kBK = 128, kBQ = 128, NB = kBQ / 32;
     constexpr int CH = D / 8, KS = D / 16, DB = D / 32, QT = kBQ * D;
     constexpr bool FB = BIAS == BIAS_FULL;
     constexpr int kT5Pad = kT5Sat + 64 + 31;
-    __shared__ __attribute__((aligned(16))) uint16_t smem[4 * QT];   // (Q, dO) x 2 slots
+    // LDS: slot sl holds the Q tile at [2 sl] and the dO tile at [2 sl + 1] (kBQ rows each)
+    __shared__ __attribute__((aligned(16))) uint16_t smem[4 * QT];
     __shared__ __attribute__((aligned(16))) float rowc[2][2][kBQ];    // [slot][lse2, D][row]
     __shared__ float t5s[BIAS == BIAS_T5 ? 2 * kT5Pad + 1 : 1];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int hh = lane >> 5, r32 = lane & 31;
-    const int kt_idx = blockIdx.x % p.n_kt, bk = blockIdx.x / p.n_kt;
-    const int b = bk / p.Hkv, kvh = bk - b * p.Hkv;
+    const bool role_dk = uniform(wave >= 4);
+    // workgroup -> (batch, KV head, key tile); with xcd_remap all key tiles of one (batch,
+    // KV head) run on one XCD (workgroup x is dispatched to XCD x % 8), where they share the
+    // Q / dO rows in that XCD's L2
+    int group, kt_idx;
+    {
+        const int x = blockIdx.x;
+        if (p.xcd_remap) {
+            const int slot = x >> 3, gl = slot / p.n_kt;
+            kt_idx = slot - gl * p.n_kt;
+            group = gl * 8 + (x & 7);
+        } else {
+            group = x / p.n_kt;
+            kt_idx = x - group * p.n_kt;
+        }
+    }
+    const int b = group / p.Hkv, kvh = group - b * p.Hkv;
     const int Sq = p.Sq, Sk = p.Sk, off = p.off, G = p.G;
     const int k0 = kt_idx * kBK;
-    const int kw0 = k0 + 32 * wave;            // first key of this wave
+    const int kw0 = k0 + 32 * (wave & 3);      // first key of this wave
     const int my_j = kw0 + r32;                // key of this lane
     const bool key_ok = my_j < Sk;
     const bool wave_ok = kw0 < Sk;
@@ -421,8 +454,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(const BwdParams p) {
 
     const size_t q_row = (size_t)p.Hq * D, kv_row = (size_t)p.Hkv * D;
     const size_t kv_off = ((size_t)b * Sk + (key_ok ? my_j : 0)) * kv_row + (size_t)kvh * D;
-    char* dk_row = (char*)p.dk + kv_off * (OUT_F32 ? 4 : 2);
-    char* dv_row = (char*)p.dv + kv_off * (OUT_F32 ? 4 : 2);
+    char* out_row = (char*)(role_dk ? p.dk : p.dv) + kv_off * (OUT_F32 ? 4 : 2);
 
     // query rows the workgroup's keys can see (positions of the rows: i + off)
     const int kend = min(k0 + kBK, Sk) - 1;
@@ -435,32 +467,13 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(const BwdParams p) {
     const int n_steps = G * nqs;
 
     if (n_steps == 0) {        // no query row sees these keys: dK = dV = 0
-        if (key_ok) {
-            store_zero_row<D, OUT_F32>(dk_row, hh);
-            store_zero_row<D, OUT_F32>(dv_row, hh);
-        }
+        if (key_ok) store_zero_row<D, OUT_F32>(out_row, hh);
         return;
     }
     const bool neg = p.scale_log2 < 0.f;
     const float c_scale = neg ? -p.scale_log2 : (p.scale_log2 == 0.f ? kTinyScale : p.scale_log2);
-    // K fragments (sign-flipped for a negative scale) and V fragments of this lane's key:
-    // dims 16 ks + 8 hh .. + 7 (B operands of S = Q.K^T and dP = dO.V^T)
-    bf16x8 kf[KS], vf[KS];
-    {
-        const uint16_t* kr = (const uint16_t*)p.k + kv_off + hh * 8;
-        const uint16_t* vr = (const uint16_t*)p.v + kv_off + hh * 8;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            u32x4 x = *(const u32x4*)(kr + ks * 16);
-            u32x4 y = *(const u32x4*)(vr + ks * 16);
-            if (!key_ok) { x = u32x4{0, 0, 0, 0}; y = u32x4{0, 0, 0, 0}; }
-            if (neg) x ^= 0x80008000u;
-            kf[ks] = __builtin_bit_cast(bf16x8, x);
-            vf[ks] = __builtin_bit_cast(bf16x8, y);
-        }
-    }
 
-    // Q / dO tiles of step n: head h = kvh * G + n / nqs, rows 64 s .. 64 s + 63 (clamped)
+    // Q / dO tiles of step n: head h = kvh * G + n / nqs, rows kBQ s .. + kBQ - 1 (clamped)
     constexpr int ROWS_PER_XFER = 1024 / (D * 2), XFERS = (kBQ * D * 2) / 1024, XPW = XFERS / kWaves;
     static_assert(XPW * kWaves == XFERS, "dma split");
     const uint32_t lds_base = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint16_t*)smem);
@@ -475,7 +488,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(const BwdParams p) {
             const int xi = wave * XPW + x;
             const int row = xi * ROWS_PER_XFER + lane / CH;
             const int i = min(i0 + row, Sq - 1);
-            const int ch = ((lane % CH) ^ swz(row)) * 8;
+            const int ch = ((lane % CH) ^ swz<D>(row)) * 8;
             dma16(qg + (size_t)i * q_row + ch, lds_base + (uint32_t)((2 * sl) * QT * 2 + xi * 1024));
             dma16(dg + (size_t)i * q_row + ch, lds_base + (uint32_t)((2 * sl + 1) * QT * 2 + xi * 1024));
         }
@@ -493,137 +506,199 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(const BwdParams p) {
         }
     };
 
-    f32x16 dk_acc[DB], dv_acc[DB];
+    // Lane-dependent LDS byte offsets inside a tile; block, group and slot offsets are
+    // compile-time constants added on top. Row-wise reads (A operand of S and dP): row
+    // perm32(r32) + 32 qb, chunk (2 ks + hh) ^ swz. Transposing reads (A operand of the
+    // dV / dK products): rows 16 hh + (li >> 2) (+4) + 8 sg + 32 qb, see read_tr.
+    uint32_t rr_off[KS], tr_off[2 * DB];
+    {
+        const int row = perm32(r32);
+        const int sw = swz<D>(row);
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+        for (int ks = 0; ks < KS; ++ks) rr_off[ks] = (uint32_t)(row * D + (((2 * ks + hh) ^ sw) << 3)) * 2;
+        const int li = lane & 15, la = li & 3, gg = lane >> 4;
+        const int trow = 16 * hh + (li >> 2);
+        const int dlo = 16 * DB * (gg & 1) + 8 * (la & 1) + 4 * (la >> 1);
 #pragma unroll
-        for (int v = 0; v < 16; ++v) { dk_acc[db][v] = 0.f; dv_acc[db][v] = 0.f; }
-    acc_fence_write(dk_acc);
-    acc_fence_write(dv_acc);
+        for (int half = 0; half < 2; ++half) {
+            const int r = trow + 4 * half;
+            const int sw2 = swz<D>(r);
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                const int d = 16 * db + dlo;
+                tr_off[2 * db + half] = (uint32_t)(r * D + ((((d >> 3) ^ sw2) << 3) | (d & 7))) * 2;
+            }
+        }
+    }
+    const char* lds = (const char*)smem;
 
-    // one 32-row block (rows i0 + 32 qb ..) of step n against this wave's 32 keys
-    auto compute_block = [&](int n, int qb) {
-        const int sl = n & 1;
-        const int h = kvh * G + n / nqs;
-        const int r0 = (s_begin + n % nqs) * kBQ + 32 * qb;    // first query row of the block
-        const int pa = r0 + off, pb = min(r0 + 31, Sq - 1) + off;
-        if (!wave_ok || r0 >= Sq) return;
-        if constexpr (MASK != MASK_NONE) { if (pb < kw0) return; }
-        if constexpr (MASK == MASK_SLIDING) { if (pa - kwe >= p.window) return; }
-        bool msk = (r0 + 31 >= Sq) || (kw0 + 31 >= Sk);
-        if constexpr (MASK != MASK_NONE) msk = msk || (pa < kwe);
-        if constexpr (MASK == MASK_SLIDING) msk = msk || (pb - kw0 >= p.window);
-        bool per_elem = FB;
-        float bconst = 0.f;
-        if constexpr (BIAS == BIAS_T5) {
-            const int rmin = kw0 - pb, rmax = kwe - pa;
-            if (rmin >= kT5Sat) bconst = t5s[2 * kT5Pad];
-            else if (rmax <= -kT5Sat) bconst = t5s[0];
-            else per_elem = true;
+    // The whole row loop of one role. Both roles run the same number of steps and barriers.
+    auto run = [&](auto role) {
+        constexpr bool DK = decltype(role)::value;
+        // K fragments (sign-flipped for a negative scale) and, for dK, V fragments of this
+        // lane's key: dims 16 ks + 8 hh .. + 7 (B operands of S = Q.K^T and dP = dO.V^T)
+        bf16x8 kf[KS], vf[DK ? KS : 1];
+        {
+            const uint16_t* kr = (const uint16_t*)p.k + kv_off + hh * 8;
+            const uint16_t* vr = (const uint16_t*)p.v + kv_off + hh * 8;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                u32x4 x = *(const u32x4*)(kr + ks * 16);
+                if (!key_ok) x = u32x4{0, 0, 0, 0};
+                if (neg) x ^= 0x80008000u;
+                kf[ks] = __builtin_bit_cast(bf16x8, x);
+                if constexpr (DK) {
+                    u32x4 y = *(const u32x4*)(vr + ks * 16);
+                    if (!key_ok) y = u32x4{0, 0, 0, 0};
+                    vf[ks] = __builtin_bit_cast(bf16x8, y);
+                }
+            }
         }
-        const uint16_t* qt = smem + (2 * sl) * QT;
-        const uint16_t* dt = smem + (2 * sl + 1) * QT;
-        f32x16 s, dp;
+        f32x16 acc[DB];
 #pragma unroll
-        for (int v = 0; v < 16; ++v) { s[v] = 0.f; dp[v] = 0.f; }
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const bf16x8 aq = read_rows<D>(qt, qb, ks, lane);
-            const bf16x8 ad = read_rows<D>(dt, qb, ks, lane);
-            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kf[ks], s, 0, 0, 0);
-            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, vf[ks], dp, 0, 0, 0);
-        }
-        // register v of lane half hh: query row r0 + 16 hh + v, key my_j
-        const int rl = 32 * qb + 16 * hh;                      // row of register 0 in the tile
-        const int pos0 = r0 + 16 * hh + off;                   // its position
-        float lrow[16], drow[16];
+            for (int v = 0; v < 16; ++v) acc[db][v] = 0.f;
+
+        // one 32-row block (rows r0 = kBQ s + 32 QB ..) of step n in slot SL
+        auto compute_block = [&](int n, auto sl_tag, auto qb_tag) {
+            constexpr int SL = decltype(sl_tag)::value, QB = decltype(qb_tag)::value;
+            const int h = kvh * G + n / nqs;
+            const int r0 = (s_begin + n % nqs) * kBQ + 32 * QB;
+            const int pa = r0 + off, pb = min(r0 + 31, Sq - 1) + off;
+            bool skip = !wave_ok || r0 >= Sq;
+            if constexpr (MASK != MASK_NONE) skip = skip || (pb < kw0);
+            if constexpr (MASK == MASK_SLIDING) skip = skip || (pa - kwe >= p.window);
+            if (uniform(skip)) return;
+            bool m = (r0 + 31 >= Sq) || (kw0 + 31 >= Sk);
+            if constexpr (MASK != MASK_NONE) m = m || (pa < kwe);
+            if constexpr (MASK == MASK_SLIDING) m = m || (pb - kw0 >= p.window);
+            const bool msk = uniform(m);
+            constexpr uint32_t QTB = (2 * SL) * QT * 2, DTB = (2 * SL + 1) * QT * 2;   // tile bytes
+            constexpr uint32_t BLK = 32 * QB * D * 2;
+            f32x16 s, dp;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const u32x4 a = *(const u32x4*)(&rowc[sl][0][rl + 4 * c]);
-            const u32x4 d = *(const u32x4*)(&rowc[sl][1][rl + 4 * c]);
+            for (int v = 0; v < 16; ++v) { s[v] = 0.f; dp[v] = 0.f; }
 #pragma unroll
-            for (int e = 0; e < 4; ++e) { lrow[4 * c + e] = __uint_as_float(a[e]); drow[4 * c + e] = __uint_as_float(d[e]); }
-        }
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            float x;
+            for (int ks = 0; ks < KS; ++ks) {
+                const bf16x8 aq = *(const bf16x8*)(lds + rr_off[ks] + (QTB + BLK));
+                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kf[ks], s, 0, 0, 0);
+                if constexpr (DK) {
+                    const bf16x8 ad = *(const bf16x8*)(lds + rr_off[ks] + (DTB + BLK));
+                    dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, vf[ks], dp, 0, 0, 0);
+                }
+            }
+            // register v of lane half hh: query row r0 + 16 hh + v, key my_j
+            const int rl = 32 * QB + 16 * hh;                      // row of register 0 in the tile
+            const int pos0 = r0 + 16 * hh + off;                   // its position
+            float x[16];
             if constexpr (BIAS == BIAS_T5) {
-                if (per_elem) {
+                const int rmin = kw0 - pb, rmax = kwe - pa;
+                const int side = uniform(rmin >= kT5Sat ? 1 : (rmax <= -kT5Sat ? -1 : 0));
+                if (side == 0) {
                     // rel = my_j - position of row v; stays inside the padded table
                     const float* trow = t5s + kT5Pad + (my_j - pos0);
-                    x = fmaf(s[v], c_scale, trow[-v]);
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) x[v] = fmaf(s[v], c_scale, trow[-v]);
                 } else {
-                    x = fmaf(s[v], c_scale, bconst);
+                    const float bconst = side > 0 ? t5s[2 * kT5Pad] : t5s[0];
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) x[v] = fmaf(s[v], c_scale, bconst);
                 }
             } else if constexpr (FB) {
-                const int i = r0 + 16 * hh + v;
                 const uint16_t* br = (const uint16_t*)p.bias + ((size_t)b * p.Hq + h) * Sq * (size_t)Sk;
-                const float bv = (i < Sq && key_ok) ? bf16_to_f32(br[(size_t)i * Sk + my_j]) : 0.f;
-                x = fmaf(bv, kLog2e, s[v] * c_scale);
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int i = r0 + 16 * hh + v;
+                    const float bv = (i < Sq && key_ok) ? bf16_to_f32(br[(size_t)i * Sk + my_j]) : 0.f;
+                    x[v] = fmaf(bv, kLog2e, s[v] * c_scale);
+                }
             } else {
-                x = s[v] * c_scale;
+#pragma unroll
+                for (int v = 0; v < 16; ++v) x[v] = s[v] * c_scale;
             }
             if (msk) {
-                const int pos = pos0 + v;
-                bool vis = key_ok && (pos - off < Sq);
-                if constexpr (MASK != MASK_NONE) vis = vis && (my_j <= pos);
-                if constexpr (MASK == MASK_SLIDING) vis = vis && (pos - my_j < p.window);
-                if (!vis) x = -INFINITY;
-            }
-            const float pv = __builtin_amdgcn_exp2f(x - lrow[v]);
-            dp[v] = pv * (dp[v] - drow[v]);      // dS
-            s[v] = pv;                            // P
-        }
-        // dV^T += dO^T P and dK^T += Q^T dS over the two 16-row groups of the block
 #pragma unroll
-        for (int sg = 0; sg < 2; ++sg) {
-            u32x4 pp, pd;
+                for (int v = 0; v < 16; ++v) {
+                    const int pos = pos0 + v;
+                    bool vis = key_ok & (pos - off < Sq);
+                    if constexpr (MASK != MASK_NONE) vis = vis & (my_j <= pos);
+                    if constexpr (MASK == MASK_SLIDING) vis = vis & (pos - my_j < p.window);
+                    x[v] = vis ? x[v] : -INFINITY;
+                }
+            }
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                pp[c] = pack_bf16x2(s[8 * sg + 2 * c], s[8 * sg + 2 * c + 1]);
-                pd[c] = pack_bf16x2(dp[8 * sg + 2 * c], dp[8 * sg + 2 * c + 1]);
+                const u32x4 lr = *(const u32x4*)(&rowc[SL][0][rl + 4 * c]);
+                u32x4 dr;
+                if constexpr (DK) dr = *(const u32x4*)(&rowc[SL][1][rl + 4 * c]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int v = 4 * c + e;
+                    const float pv = __builtin_amdgcn_exp2f(x[v] - __uint_as_float(lr[e]));
+                    if constexpr (DK) s[v] = pv * (dp[v] - __uint_as_float(dr[e]));   // dS
+                    else s[v] = pv;                                                     // P
+                }
             }
-            bf16x8 at[DB];
-            read_tr<D>(dt, 2 * qb + sg, lane, at);
-            const bf16x8 bp = __builtin_bit_cast(bf16x8, pp), bd = __builtin_bit_cast(bf16x8, pd);
+            // dV^T += dO^T P  or  dK^T += Q^T dS, over the two 16-row groups of the block
+            constexpr uint32_t TTB = DK ? QTB : DTB;
 #pragma unroll
-            for (int db = 0; db < DB; ++db) mfma_acc(dv_acc[db], at[db], bp);
-            read_tr<D>(qt, 2 * qb + sg, lane, at);
+            for (int sg = 0; sg < 2; ++sg) {
+                u32x4 pk;
 #pragma unroll
-            for (int db = 0; db < DB; ++db) mfma_acc(dk_acc[db], at[db], bd);
+                for (int c = 0; c < 4; ++c) pk[c] = pack_bf16x2(s[8 * sg + 2 * c], s[8 * sg + 2 * c + 1]);
+                const bf16x8 bp = __builtin_bit_cast(bf16x8, pk);
+                const uint32_t gofs = TTB + (uint32_t)((32 * QB + 8 * sg) * D * 2);
+#pragma unroll
+                for (int db = 0; db < DB; ++db) {
+                    const s16x4 lo = lds_read_tr((const uint16_t*)(lds + tr_off[2 * db] + gofs));
+                    const s16x4 hi = lds_read_tr((const uint16_t*)(lds + tr_off[2 * db + 1] + gofs));
+                    u32x4 av;
+                    av[0] = __builtin_bit_cast(u32x2, lo)[0];
+                    av[1] = __builtin_bit_cast(u32x2, lo)[1];
+                    av[2] = __builtin_bit_cast(u32x2, hi)[0];
+                    av[3] = __builtin_bit_cast(u32x2, hi)[1];
+                    acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), bp, acc[db], 0, 0, 0);
+                }
+            }
+        };
+
+        auto step = [&](int n, auto sl_tag) {
+            constexpr int SL = decltype(sl_tag)::value;
+            if constexpr (BIAS == BIAS_T5) {
+                // table of head h when the head changes (no reader of the previous table is
+                // still running: the barrier ending the previous step, and one after the writes)
+                const int h = kvh * G + n / nqs;
+                if (n == 0 || h != kvh * G + (n - 1) / nqs) {
+                    const float* tbl = (const float*)p.bias + (size_t)h * kT5Buckets;
+                    for (int i = tid; i < 2 * kT5Pad + 1; i += kThreads)
+                        t5s[i] = tbl[t5_bucket(i - kT5Pad)] * kLog2e;
+                    __syncthreads();
+                }
+            }
+            const bool has_next = n + 1 < n_steps;
+            if (has_next) issue_step(n + 1);
+            compute_block(n, sl_tag, std::integral_constant<int, 0>{});
+            compute_block(n, sl_tag, std::integral_constant<int, 1>{});
+            compute_block(n, sl_tag, std::integral_constant<int, 2>{});
+            compute_block(n, sl_tag, std::integral_constant<int, 3>{});
+            static_assert(NB == 4, "four 32-row blocks per step");
+            if (has_next) dma_wait();
+            __syncthreads();
+        };
+#pragma unroll 1
+        for (int n = 0; n < n_steps; n += 2) {
+            step(n, std::integral_constant<int, 0>{});
+            if (n + 1 < n_steps) step(n + 1, std::integral_constant<int, 1>{});
         }
+        if (key_ok) store_row<D, OUT_F32>(out_row, acc, DK ? p.scale : 1.f, hh);
     };
 
     issue_step(0);
     dma_wait();
     __syncthreads();
-    int cur_h = -1;
-#pragma unroll 1
-    for (int n = 0; n < n_steps; ++n) {
-        const int h = kvh * G + n / nqs;
-        if constexpr (BIAS == BIAS_T5) {
-            if (h != cur_h) {
-                // table of head h (no reader of the previous table is still running: the
-                // barrier ending the previous step, and one after the writes)
-                const float* tbl = (const float*)p.bias + (size_t)h * kT5Buckets;
-                for (int i = tid; i < 2 * kT5Pad + 1; i += kThreads) t5s[i] = tbl[t5_bucket(i - kT5Pad)] * kLog2e;
-                __syncthreads();
-            }
-        }
-        cur_h = h;
-        const bool has_next = n + 1 < n_steps;
-        if (has_next) issue_step(n + 1);
-        compute_block(n, 0);
-        compute_block(n, 1);
-        if (has_next) dma_wait();
-        __syncthreads();
-    }
-    acc_fence_read(dk_acc);
-    acc_fence_read(dv_acc);
-    if (key_ok) {
-        store_row<D, OUT_F32>(dk_row, dk_acc, p.scale, hh);
-        store_row<D, OUT_F32>(dv_row, dv_acc, 1.f, hh);
-    }
+    if (role_dk) run(std::true_type{});
+    else run(std::false_type{});
 }
 
 // ------------------------------------------------------------------------------------------
@@ -636,7 +711,7 @@ static hipError_t launch_grads(const BwdParams& p, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const unsigned gk = (unsigned)((size_t)p.B * p.Hkv * p.n_kt);
-    hipLaunchKernelGGL((dkdv_kernel<D, MASK, BIAS, OUT_F32>), dim3(gk), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((dkdv_kernel<D, MASK, BIAS, OUT_F32>), dim3(gk), dim3(512), 0, s, p);
     return hipGetLastError();
 }
 
@@ -656,16 +731,12 @@ static hipError_t launch_d(const BwdParams& p, int mask, int bias, hipStream_t s
 hipError_t launch_bwd_bf16(BwdParams p, int D, int mask, int bias, bool out_f32, hipStream_t s) {
     p.n_qt = (p.Sq + 255) / 256;
     p.n_kt = (p.Sk + 127) / 128;
-    p.xcd_remap = ((p.B * p.Hkv) % 8 == 0) ? 1 : 0;
-    const long long rows = (long long)p.B * p.Sq * p.Hq;
-    const unsigned gd = (unsigned)((rows + 255) / 256);
-    if (D == 128) hipLaunchKernelGGL((bwd::delta_kernel<128>), dim3(gd), dim3(256), 0, s, p);
-    else if (D == 64) hipLaunchKernelGGL((bwd::delta_kernel<64>), dim3(gd), dim3(256), 0, s, p);
-    else return hipErrorInvalidValue;
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    if (D == 128) return out_f32 ? bwd::launch_d<128, true>(p, mask, bias, s) : bwd::launch_d<128, false>(p, mask, bias, s);
-    return out_f32 ? bwd::launch_d<64, true>(p, mask, bias, s) : bwd::launch_d<64, false>(p, mask, bias, s);
+    p.xcd_remap = ((p.B * p.Hkv) % 8 == 0) ? 1 : 0;   // both kernels map (batch, KV head) groups to XCDs
+    if (D == 128)
+        return out_f32 ? bwd::launch_d<128, true>(p, mask, bias, s) : bwd::launch_d<128, false>(p, mask, bias, s);
+    if (D == 64)
+        return out_f32 ? bwd::launch_d<64, true>(p, mask, bias, s) : bwd::launch_d<64, false>(p, mask, bias, s);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace sdpa
