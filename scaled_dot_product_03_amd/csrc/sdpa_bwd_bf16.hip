@@ -199,7 +199,9 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(const BwdParams p) {
     constexpr int CH = D / 8, KS = D / 16, DB = D / 32, TILE = kBN * D;
     constexpr bool FB = BIAS == BIAS_FULL;
     constexpr int kT5Pad = kT5Sat + kBN + 31;
-    __shared__ __attribute__((aligned(16))) uint16_t smem[4 * TILE];   // K slots 0-1, V slots 2-3
+    constexpr int BTILE = kBM * kBN;                 // full-bias tile: 256 rows x 64 keys
+    // K slots 0-1, V slots 2-3, then (full bias) two bias slots
+    __shared__ __attribute__((aligned(16))) uint16_t smem[4 * TILE + (FB ? 2 * BTILE : 0)];
     __shared__ float t5s[BIAS == BIAS_T5 ? 2 * kT5Pad + 1 : 1];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -287,6 +289,13 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(const BwdParams p) {
     constexpr int ROWS_PER_XFER = 1024 / (D * 2), XFERS = (kBN * D * 2) / 1024, XPW = XFERS / kWaves;
     static_assert(XPW * kWaves == XFERS, "dma split");
     const uint32_t lds_base = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint16_t*)smem);
+    // A full bias goes through LDS when its rows split into whole 16-byte chunks: tile
+    // [256 rows][64 keys], 128-byte rows, chunk swizzle (row >> 1) & 7; keys past the end of a
+    // partial last tile re-read the last whole chunk (they are masked).
+    const bool fb_dma = FB && ((Sk & 7) == 0);
+    constexpr int XPB = FB ? (BTILE * 2 / 1024) / kWaves : 0;
+    const uint16_t* fbg = FB ? (const uint16_t*)p.bias + ((size_t)b * p.Hq + hq) * (size_t)Sq * Sk
+                             : nullptr;
     auto dma_tile = [&](int t) {
         const int sl = (t - t_begin) & 1, j0 = t * kBN;
 #pragma unroll
@@ -297,6 +306,19 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(const BwdParams p) {
             const int ch = ((lane % CH) ^ swz<D>(row)) * 8;
             dma16(kg + (size_t)j * kv_row + ch, lds_base + (uint32_t)((sl * TILE) * 2 + xi * 1024));
             dma16(vg + (size_t)j * kv_row + ch, lds_base + (uint32_t)(((2 + sl) * TILE) * 2 + xi * 1024));
+        }
+        if constexpr (FB) {
+            if (fb_dma) {
+                const int nchunk = min(kBN, Sk - j0) / 8;
+#pragma unroll
+                for (int n = 0; n < XPB; ++n) {
+                    const int xi = wave * XPB + n;
+                    const int row = xi * 8 + (lane >> 3);
+                    const int c = min((lane & 7) ^ ((row >> 1) & 7), nchunk - 1);
+                    dma16(fbg + (size_t)min(q0 + row, Sq - 1) * Sk + j0 + 8 * c,
+                          lds_base + (uint32_t)((4 * TILE + sl * BTILE) * 2 + xi * 1024));
+                }
+            }
         }
     };
 
@@ -349,35 +371,60 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(const BwdParams p) {
                 s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qf[ks], s, 0, 0, 0);
                 dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, dof[ks], dp, 0, 0, 0);
             }
-            // x = scores in log2 units including the bias, minus the row's log-sum-exp
+            // x = scores in log2 units including the bias
+            float x[16];
+            if constexpr (BIAS == BIAS_T5) {
+                if (per_elem) {
+                    const float* trow = t5s + kT5Pad + (jl - min(my_pos, pwb));
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                float x;
-                if constexpr (BIAS == BIAS_T5) {
-                    if (per_elem) {
-                        const float* trow = t5s + kT5Pad + (jl - min(my_pos, pwb));
-                        x = fmaf(s[v], c_scale, trow[v]);
-                    } else {
-                        x = fmaf(s[v], c_scale, bconst);
-                    }
-                } else if constexpr (FB) {
-                    const int j = jl + v;
-                    const uint16_t* br = (const uint16_t*)p.bias +
-                        (((size_t)b * p.Hq + hq) * Sq + (row_ok ? my_i : 0)) * (size_t)Sk;
-                    const float bv = (row_ok && j < Sk) ? bf16_to_f32(br[j]) : 0.f;
-                    x = fmaf(bv, kLog2e, s[v] * c_scale);
+                    for (int v = 0; v < 16; ++v) x[v] = fmaf(s[v], c_scale, trow[v]);
                 } else {
-                    x = s[v] * c_scale;
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) x[v] = fmaf(s[v], c_scale, bconst);
                 }
-                if (msk) {
+            } else if constexpr (FB) {
+                if (fb_dma) {
+                    // 16 keys from two chunks of this lane's bias row in LDS
+                    const int lr = wave * 32 + r32, c0 = 4 * jb + 2 * hh, sw = (lr >> 1) & 7;
+                    const uint16_t* brow = smem + 4 * TILE + sl * BTILE + lr * kBN;
+#pragma unroll
+                    for (int h2 = 0; h2 < 2; ++h2) {
+                        const u32x4 w = *(const u32x4*)(brow + (((c0 + h2) ^ sw) << 3));
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int v = 8 * h2 + 2 * e;
+                            x[v] = fmaf(__uint_as_float(w[e] << 16), kLog2e, s[v] * c_scale);
+                            x[v + 1] = fmaf(__uint_as_float(w[e] & 0xffff0000u), kLog2e, s[v + 1] * c_scale);
+                        }
+                    }
+                } else {
+                    const uint16_t* br = fbg + (size_t)(row_ok ? my_i : 0) * Sk;
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        const int j = jl + v;
+                        const float bv = (row_ok && j < Sk) ? bf16_to_f32(br[j]) : 0.f;
+                        x[v] = fmaf(bv, kLog2e, s[v] * c_scale);
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int v = 0; v < 16; ++v) x[v] = s[v] * c_scale;
+            }
+            if (msk) {
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
                     const int j = jl + v;
                     bool vis = j < Sk;
-                    if constexpr (MASK != MASK_NONE) vis = vis && (j <= my_pos);
-                    if constexpr (MASK == MASK_SLIDING) vis = vis && (my_pos - j < p.window);
-                    if (!vis) x = -INFINITY;
+                    if constexpr (MASK != MASK_NONE) vis = vis & (j <= my_pos);
+                    if constexpr (MASK == MASK_SLIDING) vis = vis & (my_pos - j < p.window);
+                    x[v] = vis ? x[v] : -INFINITY;
                 }
-                const float pv = __builtin_amdgcn_exp2f(x - lse2);
-                s[v] = pv * (dp[v] - drow);     // dS^T
+            }
+            // P from the row's log-sum-exp, then dS^T
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const float pv = __builtin_amdgcn_exp2f(x[v] - lse2);
+                s[v] = pv * (dp[v] - drow);
             }
             // dQ^T += K^T dS^T over the two 16-key groups of this half
 #pragma unroll
@@ -416,12 +463,15 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(const BwdParams p) {
 // ------------------------------------------------------------------------------------------
 template <int D, int MASK, int BIAS, bool OUT_F32>
 __global__ __launch_bounds__(512, 1) void dkdv_kernel(const BwdParams p) {
-    constexpr int kWaves = 8, kThreads = 512, kBK = 128, kBQ = 128, NB = kBQ / 32;
-    constexpr int CH = D / 8, KS = D / 16, DB = D / 32, QT = kBQ * D;
     constexpr bool FB = BIAS == BIAS_FULL;
+    // 128 query rows per step; 64 with a full bias at D = 128 (its tiles share the LDS)
+    constexpr int kWaves = 8, kThreads = 512, kBK = 128, kBQ = (FB && D == 128) ? 64 : 128;
+    constexpr int NB = kBQ / 32;
+    constexpr int CH = D / 8, KS = D / 16, DB = D / 32, QT = kBQ * D, BTILE = kBQ * kBK;
     constexpr int kT5Pad = kT5Sat + 64 + 31;
-    // LDS: slot sl holds the Q tile at [2 sl] and the dO tile at [2 sl + 1] (kBQ rows each)
-    __shared__ __attribute__((aligned(16))) uint16_t smem[4 * QT];
+    // LDS: slot sl holds the Q tile at [2 sl] and the dO tile at [2 sl + 1] (kBQ rows each),
+    // then (full bias) two bias slots of kBQ rows x 128 keys
+    __shared__ __attribute__((aligned(16))) uint16_t smem[4 * QT + (FB ? 2 * BTILE : 0)];
     __shared__ __attribute__((aligned(16))) float rowc[2][2][kBQ];    // [slot][lse2, D][row]
     __shared__ float t5s[BIAS == BIAS_T5 ? 2 * kT5Pad + 1 : 1];
 
@@ -477,6 +527,11 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(const BwdParams p) {
     constexpr int ROWS_PER_XFER = 1024 / (D * 2), XFERS = (kBQ * D * 2) / 1024, XPW = XFERS / kWaves;
     static_assert(XPW * kWaves == XFERS, "dma split");
     const uint32_t lds_base = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint16_t*)smem);
+    // A full bias goes through LDS when its rows split into whole 16-byte chunks: tile
+    // [kBQ rows][128 keys], 256-byte rows, chunk swizzle 4 * ((row >> 4) & 1); keys past the end
+    // of a partial last tile re-read the last whole chunk (they are masked).
+    const bool fb_dma = FB && ((Sk & 7) == 0);
+    constexpr int XPB = FB ? (BTILE * 2 / 1024) / kWaves : 0;
     auto issue_step = [&](int n) {
         const int sl = n & 1;
         const int h = kvh * G + n / nqs;
@@ -491,6 +546,20 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(const BwdParams p) {
             const int ch = ((lane % CH) ^ swz<D>(row)) * 8;
             dma16(qg + (size_t)i * q_row + ch, lds_base + (uint32_t)((2 * sl) * QT * 2 + xi * 1024));
             dma16(dg + (size_t)i * q_row + ch, lds_base + (uint32_t)((2 * sl + 1) * QT * 2 + xi * 1024));
+        }
+        if constexpr (FB) {
+            if (fb_dma) {
+                const uint16_t* bg = (const uint16_t*)p.bias + ((size_t)b * p.Hq + h) * (size_t)Sq * Sk;
+                const int nchunk = min(kBK, Sk - k0) / 8;
+#pragma unroll
+                for (int x = 0; x < XPB; ++x) {
+                    const int xi = wave * XPB + x;
+                    const int row = xi * 4 + (lane >> 4);
+                    const int c = min((lane & 15) ^ (4 * ((row >> 4) & 1)), nchunk - 1);
+                    dma16(bg + (size_t)min(i0 + row, Sq - 1) * Sk + k0 + 8 * c,
+                          lds_base + (uint32_t)((4 * QT + sl * BTILE) * 2 + xi * 1024));
+                }
+            }
         }
         if (tid < kBQ) {
             const int i = i0 + tid;
@@ -606,12 +675,22 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(const BwdParams p) {
                     for (int v = 0; v < 16; ++v) x[v] = fmaf(s[v], c_scale, bconst);
                 }
             } else if constexpr (FB) {
-                const uint16_t* br = (const uint16_t*)p.bias + ((size_t)b * p.Hq + h) * Sq * (size_t)Sk;
+                if (fb_dma) {
+                    // column my_j of rows rl .. rl + 15 of the bias tile (row bit 4 = hh)
+                    const int kk = my_j - k0;
+                    const uint16_t* bcol = smem + 4 * QT + SL * BTILE + rl * kBK +
+                                           ((((kk >> 3) ^ (4 * hh)) << 3) | (kk & 7));
 #pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int i = r0 + 16 * hh + v;
-                    const float bv = (i < Sq && key_ok) ? bf16_to_f32(br[(size_t)i * Sk + my_j]) : 0.f;
-                    x[v] = fmaf(bv, kLog2e, s[v] * c_scale);
+                    for (int v = 0; v < 16; ++v)
+                        x[v] = fmaf(bf16_to_f32(bcol[v * kBK]), kLog2e, s[v] * c_scale);
+                } else {
+                    const uint16_t* br = (const uint16_t*)p.bias + ((size_t)b * p.Hq + h) * Sq * (size_t)Sk;
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        const int i = r0 + 16 * hh + v;
+                        const float bv = (i < Sq && key_ok) ? bf16_to_f32(br[(size_t)i * Sk + my_j]) : 0.f;
+                        x[v] = fmaf(bv, kLog2e, s[v] * c_scale);
+                    }
                 }
             } else {
 #pragma unroll
@@ -680,9 +759,11 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(const BwdParams p) {
             if (has_next) issue_step(n + 1);
             compute_block(n, sl_tag, std::integral_constant<int, 0>{});
             compute_block(n, sl_tag, std::integral_constant<int, 1>{});
-            compute_block(n, sl_tag, std::integral_constant<int, 2>{});
-            compute_block(n, sl_tag, std::integral_constant<int, 3>{});
-            static_assert(NB == 4, "four 32-row blocks per step");
+            if constexpr (NB == 4) {
+                compute_block(n, sl_tag, std::integral_constant<int, 2>{});
+                compute_block(n, sl_tag, std::integral_constant<int, 3>{});
+            }
+            static_assert(NB == 2 || NB == 4, "two or four 32-row blocks per step");
             if (has_next) dma_wait();
             __syncthreads();
         };
