@@ -17,6 +17,13 @@ baseline is the fp64 oracle timed on the same workload on this host's cores.
 
 --sweep additionally times every other workload and prints one JSON line per workload on
 stderr.
+
+--bwd measures the gradients instead: a step is one sdpa_bwd call (dQ, dK, dV of
+sum(dO * O), two kernel launches) on the same workload, with O and the LSE produced by the
+forward once before the timed region. `value` counts 10*D flop per visible pair (the five
+products S, dP, dV, dQ, dK; the kernels recompute S and dP, which is not counted), and the
+roofline entry covers the whole call (both launches) timed with HIP events on its stream.
+The CPU baseline is the fp64 gradient oracle on whole (batch, KV head) pairs.
 """
 from __future__ import annotations
 
@@ -36,6 +43,8 @@ import numpy as np  # noqa: E402
 import sdpa_inputs as si  # noqa: E402
 
 METRIC = "attention fwd effective TFLOP/s (masked tiles excluded) + % of bf16 MFMA peak"
+METRIC_BWD = ("attention bwd (dQ, dK, dV) effective TFLOP/s, 10*D flop per visible pair "
+              "(masked tiles excluded) + % of bf16 MFMA peak")
 PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0           # MI355X HBM3E, published
 KERNEL_SOURCES = ["scaled_dot_product_03_amd/csrc/sdpa_fwd_bf16.hip",
@@ -78,8 +87,9 @@ def to_device(inp: si.Inputs):
     return dev(inp.q), dev(inp.k), dev(inp.v), bias
 
 
-def time_workload(sdpa, wl: si.Workload, steps: int, warmup: int):
-    """Returns dict with ms_per_step (wall, synchronised), kernel_ms_avg / median (events)."""
+def time_workload(sdpa, wl: si.Workload, steps: int, warmup: int, bwd: bool = False):
+    """Returns dict with ms_per_step (wall, synchronised), kernel_ms_avg / median (events).
+    With bwd, a step is one gradient call (dQ, dK, dV) instead of one forward."""
     import torch
     inp = si.make_inputs(wl)
     q, k, v, bias = to_device(inp)
@@ -87,11 +97,19 @@ def time_workload(sdpa, wl: si.Workload, steps: int, warmup: int):
     out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
     lse = torch.empty((wl.B, wl.Hq, wl.Sq), dtype=torch.float32, device=q.device)
     stream = torch.cuda.current_stream()
+    kw = dict(scale=wl.scale, mask=wl.mask_kind, window=wl.window, bias_kind=wl.bias_kind,
+              bias=bias, stream=stream.cuda_stream)
+    if bwd:
+        sdpa.fwd(q, k, v, out=out, lse=lse, **kw)
+        dout = torch.from_numpy(si.make_dout(wl).view(np.int16)).cuda().view(torch.bfloat16)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        ws = torch.empty((wl.B * wl.Hq * wl.Sq,), dtype=torch.float32, device=q.device)
 
-    def launch():
-        sdpa.fwd(q, k, v, scale=wl.scale, mask=wl.mask_kind, window=wl.window,
-                 bias_kind=wl.bias_kind, bias=bias, out=out, lse=lse,
-                 stream=stream.cuda_stream)
+        def launch():
+            sdpa.bwd(q, k, v, out, lse, dout, dq=dq, dk=dk, dv=dv, ws=ws, **kw)
+    else:
+        def launch():
+            sdpa.fwd(q, k, v, out=out, lse=lse, **kw)
 
     for _ in range(warmup):
         launch()
@@ -118,7 +136,7 @@ def time_workload(sdpa, wl: si.Workload, steps: int, warmup: int):
         ends[i].record(stream)
     torch.cuda.synchronize()
     ev = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
-    del q, k, v, bias, out, lse
+    del q, k, v, bias, out, lse, launch
     torch.cuda.empty_cache()
     return dict(ms_per_step=1e3 * wall / steps, region_ms_per_step=region_ms / steps,
                 kernel_ms_avg=float(ev.mean()), kernel_ms_median=float(np.median(ev)),
@@ -176,6 +194,36 @@ def cpu_baseline(wl: si.Workload, budget_s: float = 12.0):
                       f"{secs:.1f} s"}
 
 
+def cpu_baseline_bwd(wl: si.Workload, budget_s: float = 15.0):
+    """The fp64 gradient oracle on the same workload, timed on this host's cores: whole
+    (batch, KV head) pairs (all G query heads, all rows), one after the other with BLAS on every
+    core, until the workload is done or the budget is spent (at least one pair)."""
+    import oracle
+    threads = oracle.default_threads()
+    inp = si.make_inputs(wl)
+    q, k, v, extra = inp.as_f64()
+    del inp
+    do = si.bf16_bits_to_f64(si.make_dout(wl))
+    pairs = [(b, h) for b in range(wl.B) for h in range(wl.Hkv)]
+    done = 0
+    t0 = time.perf_counter()
+    while done < len(pairs):
+        oracle.sdpa_backward(q, k, v, do, scale=float(np.float32(wl.scale)),
+                             mask_kind=wl.mask_kind, window=wl.window, bias_kind=wl.bias_kind,
+                             bias=extra, kv_heads=[pairs[done]])
+        done += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    secs = time.perf_counter() - t0
+    G = wl.Hq // wl.Hkv
+    per_pair = 10.0 * wl.D * si.visible_pairs(wl.Sq, wl.Sk, wl.mask_kind, wl.window) * G
+    return {"value": per_pair * done / secs / 1e12, "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{done} of {len(pairs)} (batch, KV head) pairs of {wl.name} (each: "
+                      f"{G} query heads x {wl.Sq} rows, dQ, dK, dV), fp64 numpy with BLAS on "
+                      f"{threads} threads, {secs:.1f} s"}
+
+
 def tile_flops(wl: si.Workload) -> float:
     """FLOP of the matrix work the bf16 kernel performs: 4*D per (row, key) slot of every block
     of 32 query rows x 64 keys it computes, masked slots included. Follows the kernel's tile
@@ -206,8 +254,8 @@ def tile_flops(wl: si.Workload) -> float:
     return 4.0 * wl.D * 32 * 64 * blocks * wl.B * wl.Hq
 
 
-def report(wl: si.Workload, t: dict):
-    flops = si.effective_flops(wl)
+def report(wl: si.Workload, t: dict, bwd: bool = False):
+    flops = si.effective_flops(wl) * (2.5 if bwd else 1.0)
     achieved = flops / (t["kernel_ms_avg"] * 1e-3) / 1e12
     return flops, achieved
 
@@ -220,6 +268,8 @@ def main(argv=None):
     ap.add_argument("--workload", default="c2", choices=sorted(si.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", action="store_true")
+    ap.add_argument("--bwd", action="store_true",
+                    help="time the gradient call (dQ, dK, dV) instead of the forward")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of attention, run `steps` device-to-device copies of MIB "
                          "MiB (reference kernel for scaling HBM byte counters)")
@@ -250,6 +300,8 @@ def main(argv=None):
         return 0
 
     wl = si.WORKLOADS[args.workload]
+    if args.bwd:
+        return main_bwd(sdpa, wl, args)
     t = time_workload(sdpa, wl, args.steps, args.warmup)
     flops, achieved = report(wl, t)
     value = flops / (t["ms_per_step"] * 1e-3) / 1e12
@@ -307,6 +359,50 @@ def main(argv=None):
                               "pairs_ratio": round(si.effective_flops(si.WORKLOADS[a]) /
                                                    si.effective_flops(si.WORKLOADS[b]), 4)}),
                   file=sys.stderr, flush=True)
+    return 0
+
+
+def main_bwd(sdpa, wl: si.Workload, args) -> int:
+    t = time_workload(sdpa, wl, args.steps, args.warmup, bwd=True)
+    flops, achieved = report(wl, t, bwd=True)
+    value = flops / (t["ms_per_step"] * 1e-3) / 1e12
+    line = {
+        "metric": METRIC_BWD,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(t["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "config": {**wl.describe(), "pass": "backward (dQ, dK, dV)",
+                   "effective_gflop": round(flops / 1e9, 2),
+                   "call_ms_median": round(t["kernel_ms_median"], 4),
+                   "event_ms_per_step": round(t["region_ms_per_step"], 4)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "unit_of_work": "one gradient call (dQ kernel + dK/dV "
+                                                     "kernel)"},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_bwd(wl)
+    print(json.dumps(line), flush=True)
+    if args.sweep:
+        for key in ["c2", "c3", "c3c", "c4t5", "c4full", "c5mha", "c5gqa", "c5mqa"]:
+            w2 = si.WORKLOADS[key]
+            t2 = time_workload(sdpa, w2, max(5, args.steps // 2), max(30, args.warmup), bwd=True)
+            f2, a2 = report(w2, t2, bwd=True)
+            rec = {"workload": key, "pass": "backward", **w2.describe(),
+                   "call_ms_avg": round(t2["kernel_ms_avg"], 4),
+                   "call_ms_median": round(t2["kernel_ms_median"], 4),
+                   "effective_tflops": round(a2, 2),
+                   "pct_of_bf16_peak": round(100 * a2 / PEAK_BF16_TFLOPS, 2)}
+            print(json.dumps(rec), file=sys.stderr, flush=True)
     return 0
 
 
