@@ -50,24 +50,29 @@ PEAK_HBM_GBS = 8000.0           # MI355X HBM3E, published
 KERNEL_SOURCES = ["scaled_dot_product_03_amd/csrc/sdpa_fwd_bf16.hip",
                   "scaled_dot_product_03_amd/csrc/sdpa_params.h"]
 TRAFFIC_FILE = "profiles/sdpa_fwd_bf16_c2_traffic.json"
+KERNEL_SOURCES_BWD = ["scaled_dot_product_03_amd/csrc/sdpa_bwd_bf16.hip",
+                      "scaled_dot_product_03_amd/csrc/sdpa_params.h"]
+TRAFFIC_FILE_BWD = "profiles/sdpa_bwd_bf16_c2_traffic.json"
 
 
-def kernel_sha() -> str:
+def kernel_sha(sources=None) -> str:
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in sources or KERNEL_SOURCES:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def load_traffic(workload: str):
-    """HBM bytes per launch measured by rocprofv3 counters, if taken on this exact kernel."""
-    path = os.path.join(ROOT, TRAFFIC_FILE)
+def load_traffic(workload: str, bwd: bool = False):
+    """HBM bytes per launch (per gradient call with bwd) measured by rocprofv3 counters, if
+    taken on this exact kernel source."""
+    path = os.path.join(ROOT, TRAFFIC_FILE_BWD if bwd else TRAFFIC_FILE)
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_sha") != kernel_sha() or rec.get("workload") != workload:
+    sha = kernel_sha(KERNEL_SOURCES_BWD if bwd else KERNEL_SOURCES)
+    if rec.get("kernel_sha") != sha or rec.get("workload") != workload:
         return None
     return rec.get("traffic_bytes_per_launch")
 
@@ -254,6 +259,67 @@ def tile_flops(wl: si.Workload) -> float:
     return 4.0 * wl.D * 32 * 64 * blocks * wl.B * wl.Hq
 
 
+def bwd_tile_mfmas(wl: si.Workload):
+    """MFMA instructions (v_mfma_f32_32x32x16_bf16) the two gradient kernels issue, following
+    their tile plans: (dq kernel, dk/dv kernel) per launch.
+
+    dq kernel: work items of 256 query rows, 64-key tiles over the item's key range; a 32-row
+    wave computes a tile unless the mask hides it completely, issuing per 32-key half D/16
+    MFMAs for S, D/16 for dP and 2 * D/32 for dQ. dk/dv kernel: 128 keys per workgroup, steps
+    of 128 query rows (64 with a full bias at D = 128) over the G query heads; each 32-key
+    group has a dV wave (D/16 for S, 2 * D/32 for dV per 32-row block) and a dK wave (2 * D/16
+    for S and dP, 2 * D/32 for dK), which skip blocks the mask hides completely."""
+    off, D, W = wl.Sk - wl.Sq, wl.D, wl.window
+    G = wl.Hq // wl.Hkv
+    causal = wl.mask_kind != si.MASK_NONE
+    sliding = wl.mask_kind == si.MASK_SLIDING
+    per_half = 2 * (D // 16) + 2 * (D // 32)
+    dq = 0
+    for q0 in range(0, wl.Sq, 256):
+        pa, pb = q0 + off, min(q0 + 256, wl.Sq) - 1 + off
+        khi, klo = wl.Sk - 1, 0
+        if causal:
+            khi = min(khi, pb)
+        if sliding:
+            klo = max(0, pa - W + 1)
+        if khi < klo:
+            continue
+        for wq0 in range(q0, min(q0 + 256, wl.Sq), 32):
+            pwa, pwb = wq0 + off, min(wq0 + 31, wl.Sq - 1) + off
+            for t in range(klo // 64, khi // 64 + 1):
+                j0 = 64 * t
+                if causal and j0 > pwb:
+                    continue
+                if sliding and j0 + 63 <= pwa - W:
+                    continue
+                dq += 2 * per_half
+    kbq = 64 if (wl.bias_kind == si.BIAS_FULL and D == 128) else 128
+    per_dv, per_dk = D // 16 + 2 * (D // 32), 2 * (D // 16) + 2 * (D // 32)
+    dkdv = 0
+    for k0 in range(0, wl.Sk, 128):
+        kend = min(k0 + 128, wl.Sk) - 1
+        qlo, qhi = 0, wl.Sq
+        if causal:
+            qlo = max(0, k0 - off)
+        if sliding:
+            qhi = min(wl.Sq, kend + min(W, wl.Sk + 1) - off)
+        if qhi <= qlo:
+            continue
+        for kw0 in range(k0, min(k0 + 128, wl.Sk), 32):
+            kwe = min(kw0 + 31, wl.Sk - 1)
+            for s0 in range((qlo // kbq) * kbq, qhi, kbq):
+                for r0 in range(s0, s0 + kbq, 32):
+                    if r0 >= wl.Sq:
+                        continue
+                    pa, pb = r0 + off, min(r0 + 31, wl.Sq - 1) + off
+                    if causal and pb < kw0:
+                        continue
+                    if sliding and pa - kwe >= min(W, wl.Sk + 1):
+                        continue
+                    dkdv += G * (per_dv + per_dk)
+    return dq * wl.B * wl.Hq, dkdv * wl.B * wl.Hkv
+
+
 def report(wl: si.Workload, t: dict, bwd: bool = False):
     flops = si.effective_flops(wl) * (2.5 if bwd else 1.0)
     achieved = flops / (t["kernel_ms_avg"] * 1e-3) / 1e12
@@ -383,11 +449,13 @@ def main_bwd(sdpa, wl: si.Workload, args) -> int:
         "config": {**wl.describe(), "pass": "backward (dQ, dK, dV)",
                    "effective_gflop": round(flops / 1e9, 2),
                    "call_ms_median": round(t["kernel_ms_median"], 4),
-                   "event_ms_per_step": round(t["region_ms_per_step"], 4)},
+                   "event_ms_per_step": round(t["region_ms_per_step"], 4),
+                   "hbm_gbs_algorithmic": round(si.algorithmic_bytes_bwd(wl) /
+                                                (t["kernel_ms_avg"] * 1e-3) / 1e9, 1)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None, "unit_of_work": "one gradient call (dQ kernel + dK/dV "
-                                                     "kernel)"},
+                     "traffic": load_traffic(wl.name, bwd=True),
+                     "unit_of_work": "one gradient call (dQ kernel + dK/dV kernel)"},
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline_bwd(wl)

@@ -234,3 +234,16 @@ def algorithmic_bytes(wl: Workload) -> float:
     elif wl.bias_kind == BIAS_T5:
         b += 4 * wl.Hq * T5_NUM_BUCKETS
     return float(b)
+
+
+def algorithmic_bytes_bwd(wl: Workload) -> float:
+    """One gradient call (bf16): read q, k, v, out, dout, lse (and a full bias) once, write dq,
+    dk, dv once, and write then read the fp32 row sums rowsum(dout * out) once."""
+    es = 2
+    b = es * wl.B * wl.D * (4 * wl.Sq * wl.Hq + 4 * wl.Sk * wl.Hkv)
+    b += (4 + 8) * wl.B * wl.Hq * wl.Sq
+    if wl.bias_kind == BIAS_FULL:
+        b += es * wl.B * wl.Hq * wl.Sq * wl.Sk
+    elif wl.bias_kind == BIAS_T5:
+        b += 4 * wl.Hq * T5_NUM_BUCKETS
+    return float(b)
