@@ -62,3 +62,46 @@ def test_blocks_are_exactly_those_with_a_visible_pair(mask, w, sq, sk):
         for j in range(lo, min(p, wl.Sk - 1) + 1):
             need.add((i // 32, j // 64))
     assert blocks(wl) == len(need)
+
+
+# ------------------------------------------------------------------------------------------
+# gradient kernels: MFMA instructions of the tile plans (bench.bwd_tile_mfmas)
+# ------------------------------------------------------------------------------------------
+def test_bwd_unmasked_closed_form():
+    for D in (64, 128):
+        wl = si.WORKLOADS["c4t5"].replace(B=2, Hq=4, Hkv=2, Sq=512, Sk=768, D=D,
+                                          bias_kind=si.BIAS_NONE)
+        dq, dkdv = bench.bwd_tile_mfmas(wl)
+        G = wl.Hq // wl.Hkv
+        per_half = 2 * (D // 16) + 2 * (D // 32)
+        assert dq == wl.B * wl.Hq * (wl.Sq // 32) * (wl.Sk // 64) * 2 * per_half
+        per_pair = (D // 16 + 2 * (D // 32)) + (2 * (D // 16) + 2 * (D // 32))
+        assert dkdv == wl.B * wl.Hkv * (wl.Sk // 32) * (wl.Sq // 32) * G * per_pair
+
+
+@pytest.mark.parametrize("mask,w,sq,sk,bias", [
+    (si.MASK_CAUSAL, 0, 512, 512, si.BIAS_NONE), (si.MASK_CAUSAL, 0, 256, 640, si.BIAS_NONE),
+    (si.MASK_SLIDING, 100, 512, 512, si.BIAS_NONE), (si.MASK_SLIDING, 1, 384, 384, si.BIAS_NONE),
+    (si.MASK_SLIDING, 300, 448, 576, si.BIAS_FULL), (si.MASK_CAUSAL, 0, 640, 384, si.BIAS_FULL)])
+def test_bwd_blocks_are_exactly_those_with_a_visible_pair(mask, w, sq, sk, bias):
+    # brute force over the visibility of every (row, key): with Sq, Sk multiples of 64, the dq
+    # kernel computes a 32-row x 64-key block and the dk/dv kernel a 32-row x 32-key block iff
+    # some row of it sees some key of it
+    wl = si.WORKLOADS["c3"].replace(Sq=sq, Sk=sk, B=1, Hq=2, Hkv=1, window=w, mask_kind=mask,
+                                    bias_kind=bias)
+    off = wl.Sk - wl.Sq
+    dq_blocks, kv_blocks = set(), set()
+    for i in range(wl.Sq):
+        p = i + off
+        for j in range(wl.Sk):
+            vis = j <= p if mask != si.MASK_NONE else True
+            if mask == si.MASK_SLIDING:
+                vis = vis and p - j < w
+            if vis:
+                dq_blocks.add((i // 32, j // 64))
+                kv_blocks.add((i // 32, j // 32))
+    D, G = wl.D, 2
+    dq, dkdv = bench.bwd_tile_mfmas(wl)
+    assert dq == len(dq_blocks) * 2 * (2 * (D // 16) + 2 * (D // 32)) * wl.Hq
+    per_pair = (D // 16 + 2 * (D // 32)) + (2 * (D // 16) + 2 * (D // 32))
+    assert dkdv == len(kv_blocks) * per_pair * G
