@@ -51,6 +51,7 @@ KERNEL_SOURCES = ["scaled_dot_product_03_amd/csrc/sdpa_fwd_bf16.hip",
                   "scaled_dot_product_03_amd/csrc/sdpa_params.h"]
 TRAFFIC_FILE = "profiles/sdpa_fwd_bf16_c2_traffic.json"
 KERNEL_SOURCES_BWD = ["scaled_dot_product_03_amd/csrc/sdpa_bwd_bf16.hip",
+                      "scaled_dot_product_03_amd/csrc/sdpa_device.h",
                       "scaled_dot_product_03_amd/csrc/sdpa_params.h"]
 TRAFFIC_FILE_BWD = "profiles/sdpa_bwd_bf16_c2_traffic.json"
 

@@ -54,6 +54,8 @@
 #ifndef SDPA_MI355X_SDPA_H
 #define SDPA_MI355X_SDPA_H
 
+#include <stddef.h>
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -74,7 +76,8 @@ enum sdpa_status {
     SDPA_ERR_BIAS = 7,      /* unknown bias_kind, or bias_tbl NULL/non-NULL against it */
     SDPA_ERR_SCALE = 8,     /* scale not finite */
     SDPA_ERR_ALIGN = 9,     /* a pointer is not aligned as required */
-    SDPA_ERR_LAUNCH = 10    /* the HIP launch reported an error */
+    SDPA_ERR_LAUNCH = 10,   /* the HIP launch reported an error */
+    SDPA_ERR_WORKSPACE = 11 /* workspace NULL, misaligned or smaller than required */
 };
 
 /*
@@ -129,6 +132,32 @@ int sdpa_bwd_f32out(const void* q, const void* k, const void* v, const void* out
                     float* ws, int B, int Hq, int Hkv, int Sq, int Sk, int D, float scale,
                     int mask_kind, int window, int bias_kind, const void* bias_tbl,
                     void* stream);
+
+/*
+ * KV-cache decode: the forward above (same operation, arguments, layouts, masks, biases, head
+ * sharing and outputs) for few query rows against a long key/value cache, the generation
+ * setting of the KV-cache section of the Medium post "Simplified Explanation of Attention"
+ * (bottom-right alignment: query row i sits at position i + Sk - Sq). Any Sq is accepted; the
+ * kernels are built for Sq * Hq / Hkv up to a few 32-row blocks. The key range is split so
+ * that every CU streams part of the cache: one launch forms a partial (max, sum, O) per split,
+ * a second combines the splits in split order. The split count is a function of
+ * (B, Hq, Hkv, Sq, Sk) alone, so results are bitwise reproducible run to run; they are not
+ * bitwise equal to sdpa_fwd's (another summation order), both meeting the forward's bars.
+ *   ws       : caller-owned device workspace, 16-byte aligned, at least
+ *              sdpa_decode_ws_bytes(B, Hq, Hkv, Sq, Sk, D) bytes; contents on entry do not
+ *              matter. Error SDPA_ERR_WORKSPACE otherwise.
+ *   q, k, v, out: bf16 (sdpa_decode) or bf16 in / fp32 out (sdpa_decode_f32out); lse fp32.
+ */
+size_t sdpa_decode_ws_bytes(int B, int Hq, int Hkv, int Sq, int Sk, int D);
+
+int sdpa_decode(const void* q, const void* k, const void* v, void* out, float* lse, void* ws,
+                size_t ws_bytes, int B, int Hq, int Hkv, int Sq, int Sk, int D, float scale,
+                int mask_kind, int window, int bias_kind, const void* bias_tbl, void* stream);
+
+int sdpa_decode_f32out(const void* q, const void* k, const void* v, float* out, float* lse,
+                       void* ws, size_t ws_bytes, int B, int Hq, int Hkv, int Sq, int Sk, int D,
+                       float scale, int mask_kind, int window, int bias_kind,
+                       const void* bias_tbl, void* stream);
 
 /* Static English text for a status code (never NULL). */
 const char* sdpa_status_str(int status);

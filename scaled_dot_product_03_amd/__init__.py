@@ -7,6 +7,7 @@ fallback: if the library is missing, calls raise.
 
     out, lse = fwd(q, k, v, mask="causal")           # q [B,Sq,Hq,D], k/v [B,Sk,Hkv,D]
     dq, dk, dv = bwd(q, k, v, out, lse, dout, mask="causal")
+    out, lse = decode(q_new, k_cache, v_cache, mask="causal")   # few rows, long cache
 
 Layout follows the "jax-gpu-05-attention-gpu" codelab, section 3 (batch, sequence, heads,
 head dim). lse is [B, Hq, Sq] fp32 (natural log).
@@ -30,11 +31,12 @@ SDPA_OK = 0
 STATUS_NAMES = {0: "SDPA_OK", 1: "SDPA_ERR_NULL", 2: "SDPA_ERR_SHAPE", 3: "SDPA_ERR_HEADS",
                 4: "SDPA_ERR_HEADDIM", 5: "SDPA_ERR_MASK", 6: "SDPA_ERR_WINDOW",
                 7: "SDPA_ERR_BIAS", 8: "SDPA_ERR_SCALE", 9: "SDPA_ERR_ALIGN",
-                10: "SDPA_ERR_LAUNCH"}
+                10: "SDPA_ERR_LAUNCH", 11: "SDPA_ERR_WORKSPACE"}
 
 # symbols exported by the library (must match include/sdpa.h)
 ENTRY_POINTS = ("sdpa_fwd", "sdpa_fwd_bf16_f32out", "sdpa_fwd_f32", "sdpa_bwd",
-                "sdpa_bwd_f32out", "sdpa_status_str", "sdpa_abi_version")
+                "sdpa_bwd_f32out", "sdpa_decode_ws_bytes", "sdpa_decode", "sdpa_decode_f32out",
+                "sdpa_status_str", "sdpa_abi_version")
 ABI_VERSION = 2
 
 _lib = None
@@ -72,6 +74,14 @@ def load():
         fn = getattr(L, name)
         fn.argtypes = bwd_args
         fn.restype = ctypes.c_int
+    L.sdpa_decode_ws_bytes.argtypes = [ctypes.c_int] * 6
+    L.sdpa_decode_ws_bytes.restype = ctypes.c_size_t
+    dec_args = [ctypes.c_void_p] * 6 + [ctypes.c_size_t] + [ctypes.c_int] * 6 + \
+               [ctypes.c_float] + [ctypes.c_int] * 3 + [ctypes.c_void_p, ctypes.c_void_p]
+    for name in ("sdpa_decode", "sdpa_decode_f32out"):
+        fn = getattr(L, name)
+        fn.argtypes = dec_args
+        fn.restype = ctypes.c_int
     L.sdpa_status_str.argtypes = [ctypes.c_int]
     L.sdpa_status_str.restype = ctypes.c_char_p
     L.sdpa_abi_version.argtypes = []
@@ -98,6 +108,19 @@ def call_raw_bwd(entry: str, q, k, v, out, lse, dout, dq, dk, dv, ws, B, Hq, Hkv
     fn = getattr(load(), entry)
     return fn(q, k, v, out, lse, dout, dq, dk, dv, ws, B, Hq, Hkv, Sq, Sk, D,
               ctypes.c_float(scale), mask_kind, window, bias_kind, bias, stream)
+
+
+def call_raw_decode(entry: str, q, k, v, out, lse, ws, ws_bytes, B, Hq, Hkv, Sq, Sk, D, scale,
+                    mask_kind, window, bias_kind, bias, stream) -> int:
+    """Call a decode entry point with raw integer pointers; returns the status code."""
+    fn = getattr(load(), entry)
+    return fn(q, k, v, out, lse, ws, ws_bytes, B, Hq, Hkv, Sq, Sk, D, ctypes.c_float(scale),
+              mask_kind, window, bias_kind, bias, stream)
+
+
+def decode_ws_bytes(B, Hq, Hkv, Sq, Sk, D) -> int:
+    """Workspace bytes sdpa_decode needs for this shape (0 for an invalid shape)."""
+    return int(load().sdpa_decode_ws_bytes(B, Hq, Hkv, Sq, Sk, D))
 
 
 def _kind(val, table, what):
@@ -233,3 +256,42 @@ def bwd(q, k, v, out, lse, dout, *, scale: Optional[float] = None, mask="causal"
     if st != SDPA_OK:
         raise SdpaError(st, L.sdpa_status_str(st).decode())
     return dq, dk, dv
+
+
+def decode(q, k, v, *, scale: Optional[float] = None, mask="causal", window: int = 0,
+           bias_kind="none", bias=None, out=None, lse=None, out_dtype=None, ws=None,
+           stream=None):
+    """Split-key decode on the current HIP stream (few query rows against a long K/V cache).
+    Same arguments and results as fwd for bf16 inputs; ws is an optional uint8 device buffer
+    of at least decode_ws_bytes(...) bytes (allocated here when None)."""
+    import torch
+
+    L = load()
+    B, Sq, Hq, D, Sk, Hkv = _check_qkv(q, k, v)
+    if q.dtype != torch.bfloat16:
+        raise ValueError("decode takes bf16 q, k, v")
+    mk = _kind(mask, _MASKS, "mask")
+    bk = _kind(bias_kind, _BIASES, "bias kind")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    odt = out_dtype or torch.bfloat16
+    if odt not in (torch.bfloat16, torch.float32):
+        raise ValueError("out_dtype must be bf16 or fp32")
+    entry = "sdpa_decode" if odt == torch.bfloat16 else "sdpa_decode_f32out"
+    bias_ptr = _bias_ptr(bk, bias, q.dtype, B, Hq, Sq, Sk)
+    need = decode_ws_bytes(B, Hq, Hkv, Sq, Sk, D)
+    if ws is None:
+        ws = torch.empty((max(need, 16),), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((B, Sq, Hq, D), dtype=odt, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = getattr(L, entry)(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                           lse.data_ptr(), ws.data_ptr(), ws.numel() * ws.element_size(), B, Hq,
+                           Hkv, Sq, Sk, D, ctypes.c_float(scale), mk, int(window), bk, bias_ptr,
+                           stream)
+    if st != SDPA_OK:
+        raise SdpaError(st, L.sdpa_status_str(st).decode())
+    return out, lse

@@ -19,7 +19,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_NAME = "libsdpa_mi355x.so"
-SOURCES = ["sdpa_api.hip", "sdpa_fwd_bf16.hip", "sdpa_fwd_f32.hip", "sdpa_bwd_bf16.hip"]
+SOURCES = ["sdpa_api.hip", "sdpa_fwd_bf16.hip", "sdpa_fwd_f32.hip", "sdpa_bwd_bf16.hip",
+           "sdpa_decode_bf16.hip"]
 ARCH = os.environ.get("SDPA_OFFLOAD_ARCH", "gfx950")
 
 COMMON_FLAGS = [

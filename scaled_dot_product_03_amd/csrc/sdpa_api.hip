@@ -6,12 +6,14 @@
 #include <stdint.h>
 
 #include "sdpa.h"
+#include "sdpa_decode.h"
 #include "sdpa_params.h"
 
 namespace sdpa {
 hipError_t launch_fwd_bf16(FwdParams p, int D, int mask, int bias, bool out_f32, hipStream_t s);
 hipError_t launch_fwd_f32(FwdParams p, int D, int mask, int bias, hipStream_t s);
 hipError_t launch_bwd_bf16(BwdParams p, int D, int mask, int bias, bool out_f32, hipStream_t s);
+hipError_t launch_decode_bf16(DecParams p, int D, int mask, int bias, bool out_f32, hipStream_t s);
 }  // namespace sdpa
 
 namespace {
@@ -100,9 +102,61 @@ sdpa::BwdParams make_bwd_params(const void* q, const void* k, const void* v, con
     return p;
 }
 
+bool dec_shape_ok(int B, int Hq, int Hkv, int Sq, int Sk, int D) {
+    return B >= 1 && Hq >= 1 && Hkv >= 1 && Sq >= 1 && Sk >= 1 && Hq % Hkv == 0 &&
+           (D == 64 || D == 128) && (long long)Sq * (Hq / Hkv) < (1LL << 30);
+}
+
+int decode_common(const void* q, const void* k, const void* v, void* out, float* lse, void* ws,
+                  size_t ws_bytes, int B, int Hq, int Hkv, int Sq, int Sk, int D, float scale,
+                  int mask_kind, int window, int bias_kind, const void* bias_tbl, void* stream,
+                  bool out_f32) {
+    int st = validate(q, k, v, out, lse, B, Hq, Hkv, Sq, Sk, D, scale, mask_kind, window,
+                      bias_kind, bias_tbl, 2);
+    if (st != SDPA_OK) return st;
+    const int G = Hq / Hkv;
+    if ((long long)Sq * G >= (1LL << 30)) return SDPA_ERR_SHAPE;
+    const long long grid = (long long)B * Hkv * sdpa::dec_row_blocks(G, Sq) *
+                           sdpa::dec_splits(B, Hkv, G, Sq, Sk);
+    if (grid >= (1LL << 31)) return SDPA_ERR_SHAPE;
+    if (!ws || !aligned(ws, 16) ||
+        ws_bytes < sdpa::dec_ws_floats(B, Hkv, G, Sq, Sk, D) * sizeof(float))
+        return SDPA_ERR_WORKSPACE;
+    const sdpa::FwdParams f = make_params(q, k, v, out, lse, B, Hq, Hkv, Sq, Sk, scale,
+                                          mask_kind, window, bias_tbl);
+    sdpa::DecParams p{};
+    p.q = q; p.k = k; p.v = v; p.out = out; p.lse = lse; p.ws = (float*)ws; p.bias = bias_tbl;
+    p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.Sq = Sq; p.Sk = Sk;
+    p.G = f.G; p.off = f.off; p.window = f.window;
+    p.scale = f.scale; p.scale_log2 = f.scale_log2;
+    hipError_t e = sdpa::launch_decode_bf16(p, D, mask_kind, bias_kind, out_f32,
+                                            (hipStream_t)stream);
+    return e == hipSuccess ? SDPA_OK : SDPA_ERR_LAUNCH;
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t sdpa_decode_ws_bytes(int B, int Hq, int Hkv, int Sq, int Sk, int D) {
+    if (!dec_shape_ok(B, Hq, Hkv, Sq, Sk, D)) return 0;
+    return sdpa::dec_ws_floats(B, Hkv, Hq / Hkv, Sq, Sk, D) * sizeof(float);
+}
+
+int sdpa_decode(const void* q, const void* k, const void* v, void* out, float* lse, void* ws,
+                size_t ws_bytes, int B, int Hq, int Hkv, int Sq, int Sk, int D, float scale,
+                int mask_kind, int window, int bias_kind, const void* bias_tbl, void* stream) {
+    return decode_common(q, k, v, out, lse, ws, ws_bytes, B, Hq, Hkv, Sq, Sk, D, scale,
+                         mask_kind, window, bias_kind, bias_tbl, stream, false);
+}
+
+int sdpa_decode_f32out(const void* q, const void* k, const void* v, float* out, float* lse,
+                       void* ws, size_t ws_bytes, int B, int Hq, int Hkv, int Sq, int Sk, int D,
+                       float scale, int mask_kind, int window, int bias_kind,
+                       const void* bias_tbl, void* stream) {
+    return decode_common(q, k, v, out, lse, ws, ws_bytes, B, Hq, Hkv, Sq, Sk, D, scale,
+                         mask_kind, window, bias_kind, bias_tbl, stream, true);
+}
 
 int sdpa_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq,
              int Hkv, int Sq, int Sk, int D, float scale, int mask_kind, int window,
@@ -181,6 +235,7 @@ const char* sdpa_status_str(int status) {
         case SDPA_ERR_SCALE: return "scale is not finite";
         case SDPA_ERR_ALIGN: return "pointer misaligned (q/k/v/out/full bias need 16 bytes)";
         case SDPA_ERR_LAUNCH: return "HIP kernel launch failed";
+        case SDPA_ERR_WORKSPACE: return "workspace NULL, misaligned (16 bytes) or too small";
         default: return "unknown status";
     }
 }

@@ -1,0 +1,385 @@
+// gfx950 split-key decode: O = softmax(Q.K^T * scale + bias + mask) . V for few query rows
+// against a long key/value cache (generation: each new token's queries attend to the cached
+// keys and values, the KV-cache section of the Medium post "Simplified Explanation of
+// Attention"), with the masks, biases and head sharing of the forward kernel (the
+// "jax-gpu-05-attention-gpu" codelab, sections 1, 7 and 9; FAT5 README attention biases).
+//
+// With one query row per head there is too little work per (batch, head) to fill the chip by
+// splitting query rows, so the key range is split instead:
+//   split_kernel : one workgroup = 4 waves = one 32-row block of the G * Sq query rows sharing
+//                  a KV head (row r = i * G + g: query row i of head kvh * G + g), and one
+//                  contiguous range of 64-key tiles. K and V tiles stream through a 4-slot LDS
+//                  ring; waves 0-1 take the two 32-key halves of even tiles, waves 2-3 of odd
+//                  tiles. Per 32 keys: S^T = K.Q^T (lane = query row), an online softmax
+//                  (running max m, sum l, both per row) and O^T += V^T.P^T with V^T from
+//                  transposing LDS reads. The four waves' (m, l, O) are then combined in a
+//                  fixed order into one partial result per split, stored in the workspace
+//                  (or, with a single split, normalised and stored as the output).
+//   merge_kernel : combines the splits of each row in split order:
+//                  m = max m_s, l = sum l_s 2^(m_s - m), O = sum O_s 2^(m_s - m) / l.
+// Every value has one writer and a fixed summation order: bitwise reproducible run to run.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "sdpa_decode.h"
+#include "sdpa_device.h"
+#include "sdpa_params.h"
+
+namespace sdpa {
+namespace dec {
+
+using namespace dev;
+
+constexpr int kWaves = 4, kThreads = 256, kBN = 64, kNS = 4;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// D / 8 output columns starting at col0 of query row r (= i * G + g) of (batch b, KV head kvh),
+// times mul, and (from the first column chunk) the row's log-sum-exp
+template <int D, bool OUT_F32>
+__device__ __forceinline__ void store_out(const DecParams& p, int b, int kvh, int r, int col0,
+                                          const float* o, float mul, float lse) {
+    const int i = r / p.G, hq = kvh * p.G + (r - i * p.G);
+    const size_t row = ((size_t)b * p.Sq + i) * p.Hq + hq;
+    if constexpr (OUT_F32) {
+        float* dst = (float*)p.out + row * D + col0;
+#pragma unroll
+        for (int c = 0; c < D / 8; c += 4) {
+            u32x4 w;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) w[e] = __float_as_uint(o[c + e] * mul);
+            *(u32x4*)(dst + c) = w;
+        }
+    } else {
+        uint16_t* dst = (uint16_t*)p.out + row * D + col0;
+#pragma unroll
+        for (int c = 0; c < D / 8; c += 8) {
+            u32x4 w;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(o[c + 2 * e] * mul, o[c + 2 * e + 1] * mul);
+            *(u32x4*)(dst + c) = w;
+        }
+    }
+    if (col0 == 0) p.lse[((size_t)b * p.Hq + hq) * p.Sq + i] = lse;
+}
+
+// ------------------------------------------------------------------------------------------
+// one (batch, KV head, 32-row block, key split)
+// ------------------------------------------------------------------------------------------
+template <int D, int MASK, int BIAS, bool OUT_F32>
+__global__ __launch_bounds__(256, D == 128 ? 1 : 2) void split_kernel(const DecParams p) {
+    constexpr int KS = D / 16, DB = D / 32, TILE = kBN * D, CH = D / 8;
+    constexpr bool FB = BIAS == BIAS_FULL;
+    // slot u of the ring: K tile at [2u], V tile at [2u + 1]; reused for the wave merge
+    __shared__ __attribute__((aligned(16))) uint16_t smem[kNS * 2 * TILE];
+    __shared__ float t5s[BIAS == BIAS_T5 ? 32 * kT5Buckets : 1];   // [row of block][bucket]
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int hh = lane >> 5, r32 = lane & 31;
+    const int split = blockIdx.x % p.n_split;
+    const int rest = blockIdx.x / p.n_split;
+    const int rb = rest % p.n_rb, group = rest / p.n_rb;
+    const int b = group / p.Hkv, kvh = group - b * p.Hkv;
+    const int G = p.G, Sq = p.Sq, Sk = p.Sk, off = p.off;
+
+    // this lane's query row
+    const int r = 32 * rb + r32;
+    const bool row_ok = r < p.rows;
+    const int rr = row_ok ? r : 0;
+    const int my_i = rr / G, my_g = rr - my_i * G, my_hq = kvh * G + my_g;
+    const int my_pos = my_i + off;
+
+    // keys any row of the block may see, cut into this split's range of 64-key tiles
+    const int r_last = min(32 * rb + 31, p.rows - 1);
+    const int pmin = (32 * rb) / G + off, pmax = r_last / G + off;
+    int klo = 0, khi = Sk - 1;
+    if constexpr (MASK != MASK_NONE) khi = min(khi, pmax);
+    if constexpr (MASK == MASK_SLIDING) klo = max(0, pmin - p.window + 1);
+    const int t_lo = klo / kBN;
+    const int n_t = (khi < klo) ? 0 : khi / kBN - t_lo + 1;
+    const int tps = (n_t + p.n_split - 1) / p.n_split;
+    const int ts = t_lo + split * tps;
+    const int nt = max(0, min(t_lo + n_t, ts + tps) - ts);
+
+    // workspace of this unit
+    const size_t unit = ((size_t)group * p.n_rb + rb) * p.n_split + split;
+    const size_t units = (size_t)p.B * p.Hkv * p.n_rb * p.n_split;
+    float* ws_o = p.ws + unit * 32 * D;
+    float* ws_ml = p.ws + units * 32 * D + unit * 64;
+
+    if constexpr (BIAS == BIAS_T5) {
+        for (int idx = tid; idx < 32 * kT5Buckets; idx += kThreads) {
+            const int row = idx / kT5Buckets, bk = idx - row * kT5Buckets;
+            const int rw = min(32 * rb + row, p.rows - 1);
+            const int hq = kvh * G + (rw - (rw / G) * G);
+            t5s[idx] = ((const float*)p.bias)[(size_t)hq * kT5Buckets + bk] * kLog2e;
+        }
+    }
+
+    const bool neg = p.scale_log2 < 0.f;
+    const float c_scale = neg ? -p.scale_log2 : (p.scale_log2 == 0.f ? kTinyScale : p.scale_log2);
+    bf16x8 qf[KS];
+    {
+        const uint16_t* qr = (const uint16_t*)p.q + (((size_t)b * Sq + my_i) * p.Hq + my_hq) * D + hh * 8;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            u32x4 x = *(const u32x4*)(qr + ks * 16);
+            if (!row_ok) x = u32x4{0, 0, 0, 0};
+            if (neg) x ^= 0x80008000u;
+            qf[ks] = __builtin_bit_cast(bf16x8, x);
+        }
+    }
+
+    // K / V tile u of the split (rows past the end of the cache clamped; they are masked)
+    const size_t kv_row = (size_t)p.Hkv * D;
+    const uint16_t* kg = (const uint16_t*)p.k + ((size_t)b * Sk * p.Hkv + kvh) * D;
+    const uint16_t* vg = (const uint16_t*)p.v + ((size_t)b * Sk * p.Hkv + kvh) * D;
+    constexpr int ROWS_PER_XFER = 1024 / (D * 2), XFERS = TILE * 2 / 1024, XPW = XFERS / kWaves;
+    static_assert(XPW * kWaves == XFERS, "dma split");
+    const uint32_t lds_base = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint16_t*)smem);
+    auto dma_tile = [&](int u) {
+        const int sl = u % kNS, j0 = (ts + u) * kBN;
+#pragma unroll
+        for (int n = 0; n < XPW; ++n) {
+            const int xi = wave * XPW + n;
+            const int row = xi * ROWS_PER_XFER + lane / CH;
+            const int j = min(j0 + row, Sk - 1);
+            const int ch = ((lane % CH) ^ swz<D>(row)) * 8;
+            dma16(kg + (size_t)j * kv_row + ch, lds_base + (uint32_t)((2 * sl) * TILE * 2 + xi * 1024));
+            dma16(vg + (size_t)j * kv_row + ch, lds_base + (uint32_t)((2 * sl + 1) * TILE * 2 + xi * 1024));
+        }
+    };
+
+    // running state of this wave's rows: max m (log2 units), this lane half's part of the sum l,
+    // and O^T (head dims x rows)
+    float m = -INFINITY, l = 0.f;
+    f32x16 acc[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[db][v] = 0.f;
+
+    const int kh = wave & 1;                         // key half of the tile this wave takes
+    const uint16_t* fbrow = FB ? (const uint16_t*)p.bias + (((size_t)b * p.Hq + my_hq) * Sq + my_i) * (size_t)Sk
+                               : nullptr;
+    auto compute = [&](int u) {
+        const int sl = u % kNS;
+        const int j0 = (ts + u) * kBN + 32 * kh;     // key of register 0 of lane half 0
+        const uint16_t* kb = smem + (2 * sl) * TILE;
+        const uint16_t* vb = smem + (2 * sl + 1) * TILE;
+        f32x16 s;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) s[v] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_rows<D>(kb, kh, ks, lane), qf[ks], s, 0, 0, 0);
+        const int jl = j0 + 16 * hh;                 // key of register 0 of this lane
+        float x[16];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            float t = s[v] * c_scale;
+            if constexpr (BIAS == BIAS_T5) t += t5s[r32 * kT5Buckets + t5_bucket(jl + v - my_pos)];
+            if constexpr (FB) {
+                const int j = jl + v;
+                t = fmaf((row_ok && j < Sk) ? bf16_to_f32(fbrow[j]) : 0.f, kLog2e, t);
+            }
+            x[v] = t;
+        }
+        bool mneed = !uniform(p.rows >= 32 * rb + 32) || (j0 + 32 > Sk);
+        if constexpr (MASK != MASK_NONE) mneed = mneed || (j0 + 31 > pmin);
+        if constexpr (MASK == MASK_SLIDING) mneed = mneed || (j0 <= pmax - p.window);
+        if (uniform(mneed)) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int j = jl + v;
+                bool vis = row_ok & (j < Sk);
+                if constexpr (MASK != MASK_NONE) vis = vis & (j <= my_pos);
+                if constexpr (MASK == MASK_SLIDING) vis = vis & (my_pos - j < p.window);
+                x[v] = vis ? x[v] : -INFINITY;
+            }
+        }
+        float mx = x[0];
+#pragma unroll
+        for (int v = 1; v < 16; ++v) mx = fmaxf(mx, x[v]);
+        const float m_new = fmaxf(m, partner_max(mx));
+        const float mref = (m_new == -INFINITY) ? 0.f : m_new;
+        const float alpha = __builtin_amdgcn_exp2f(m - mref);
+        float ps = 0.f;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            x[v] = __builtin_amdgcn_exp2f(x[v] - mref);
+            ps += x[v];
+        }
+        l = fmaf(l, alpha, ps);
+        m = m_new;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[db][v] *= alpha;
+        // O^T += V^T P^T over the two 16-key groups of this half
+#pragma unroll
+        for (int sg = 0; sg < 2; ++sg) {
+            u32x4 pk;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) pk[c] = pack_bf16x2(x[8 * sg + 2 * c], x[8 * sg + 2 * c + 1]);
+            bf16x8 vt[DB];
+            read_tr<D>(vb, 2 * kh + sg, lane, vt);
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+                acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt[db], __builtin_bit_cast(bf16x8, pk), acc[db], 0, 0, 0);
+        }
+    };
+
+    if (nt > 0) dma_tile(0);
+    if (nt > 1) dma_tile(1);
+    dma_wait();
+    __syncthreads();
+    const int my_tile = uniform(wave >> 1);
+#pragma unroll 1
+    for (int u0 = 0; u0 < nt; u0 += 2) {
+        if (u0 + 2 < nt) dma_tile(u0 + 2);
+        if (u0 + 3 < nt) dma_tile(u0 + 3);
+        if (u0 + my_tile < nt) compute(u0 + my_tile);
+        dma_wait();
+        __syncthreads();
+    }
+
+    // combine the four waves in order 0..3 (LDS of the ring is free after the last barrier)
+    float* obuf = (float*)smem;                      // [wave][row][D]
+    float* mbuf = obuf + kWaves * 32 * D;            // [wave][row]
+    float* lbuf = mbuf + kWaves * 32;                // [wave][row]
+    static_assert((kWaves * 32 * D + 2 * kWaves * 32) * 4 <= kNS * 2 * TILE * 2, "merge buffer");
+    {
+        const float l_row = partner_sum(l);
+        float* orow = obuf + (wave * 32 + r32) * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            const int d0[2] = {16 * db + 8 * hh, 16 * (db + DB) + 8 * hh};
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+#pragma unroll
+                for (int hv = 0; hv < 2; ++hv) {
+                    u32x4 w;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) w[e] = __float_as_uint(acc[db][8 * c + 4 * hv + e]);
+                    *(u32x4*)(orow + d0[c] + 4 * hv) = w;
+                }
+        }
+        if (hh == 0) {
+            mbuf[wave * 32 + r32] = m;
+            lbuf[wave * 32 + r32] = l_row;
+        }
+    }
+    __syncthreads();
+    {
+        const int row = tid >> 3, cc = tid & 7;      // 32 rows x 8 column chunks of D / 8
+        float mw[kWaves], ms = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) { mw[w] = mbuf[w * 32 + row]; ms = fmaxf(ms, mw[w]); }
+        float wt[kWaves], ls = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            wt[w] = (ms == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw[w] - ms);
+            ls = fmaf(lbuf[w * 32 + row], wt[w], ls);
+        }
+        float o[D / 8];
+#pragma unroll
+        for (int c = 0; c < D / 8; ++c) {
+            float t = 0.f;
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) t = fmaf(obuf[(w * 32 + row) * D + cc * (D / 8) + c], wt[w], t);
+            o[c] = t;
+        }
+        const int rg = 32 * rb + row;
+        if (p.n_split == 1) {
+            if (rg < p.rows)
+                store_out<D, OUT_F32>(p, b, kvh, rg, cc * (D / 8), o, ls > 0.f ? 1.f / ls : 0.f,
+                                      ls > 0.f ? (ms + __builtin_amdgcn_logf(ls)) * kLn2 : -INFINITY);
+        } else {
+            float* dst = ws_o + row * D + cc * (D / 8);
+#pragma unroll
+            for (int c = 0; c < D / 8; c += 4) {
+                u32x4 w;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) w[e] = __float_as_uint(o[c + e]);
+                *(u32x4*)(dst + c) = w;
+            }
+            if (cc == 0) {
+                ws_ml[2 * row] = ms;
+                ws_ml[2 * row + 1] = ls;
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// combine the splits of each (batch, KV head, row block) in split order
+// ------------------------------------------------------------------------------------------
+template <int D, bool OUT_F32>
+__global__ __launch_bounds__(256) void merge_kernel(const DecParams p) {
+    const int tid = threadIdx.x;
+    const int row = tid >> 3, cc = tid & 7;
+    const int rb = blockIdx.x % p.n_rb, group = blockIdx.x / p.n_rb;
+    const int b = group / p.Hkv, kvh = group - b * p.Hkv;
+    const int rg = 32 * rb + row;
+    if (rg >= p.rows) return;
+    const size_t units = (size_t)p.B * p.Hkv * p.n_rb * p.n_split;
+    const size_t unit0 = ((size_t)group * p.n_rb + rb) * p.n_split;
+    const float* ml = p.ws + units * 32 * D + unit0 * 64 + 2 * row;
+    float ms = -INFINITY;
+    for (int s = 0; s < p.n_split; ++s) ms = fmaxf(ms, ml[64 * s]);
+    float ls = 0.f;
+    float o[D / 8];
+#pragma unroll
+    for (int c = 0; c < D / 8; ++c) o[c] = 0.f;
+    for (int s = 0; s < p.n_split; ++s) {
+        const float w = (ms == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ml[64 * s] - ms);
+        ls = fmaf(ml[64 * s + 1], w, ls);
+        const float* src = p.ws + (unit0 + s) * 32 * D + row * D + cc * (D / 8);
+#pragma unroll
+        for (int c = 0; c < D / 8; c += 4) {
+            const u32x4 v = *(const u32x4*)(src + c);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[c + e] = fmaf(__uint_as_float(v[e]), w, o[c + e]);
+        }
+    }
+    store_out<D, OUT_F32>(p, b, kvh, rg, cc * (D / 8), o, ls > 0.f ? 1.f / ls : 0.f,
+                          ls > 0.f ? (ms + __builtin_amdgcn_logf(ls)) * kLn2 : -INFINITY);
+}
+
+template <int D, int MASK, int BIAS, bool OUT_F32>
+static hipError_t launch_one(const DecParams& p, hipStream_t s) {
+    const unsigned grid = (unsigned)((size_t)p.B * p.Hkv * p.n_rb * p.n_split);
+    hipLaunchKernelGGL((split_kernel<D, MASK, BIAS, OUT_F32>), dim3(grid), dim3(kThreads), 0, s, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || p.n_split == 1) return e;
+    const unsigned gm = (unsigned)((size_t)p.B * p.Hkv * p.n_rb);
+    hipLaunchKernelGGL((merge_kernel<D, OUT_F32>), dim3(gm), dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
+template <int D, bool OUT_F32>
+static hipError_t launch_d(const DecParams& p, int mask, int bias, hipStream_t s) {
+#define SDPA_CASE(M, Bk) \
+    if (mask == M && bias == Bk) return launch_one<D, M, Bk, OUT_F32>(p, s);
+    SDPA_CASE(MASK_NONE, BIAS_NONE) SDPA_CASE(MASK_NONE, BIAS_T5) SDPA_CASE(MASK_NONE, BIAS_FULL)
+    SDPA_CASE(MASK_CAUSAL, BIAS_NONE) SDPA_CASE(MASK_CAUSAL, BIAS_T5) SDPA_CASE(MASK_CAUSAL, BIAS_FULL)
+    SDPA_CASE(MASK_SLIDING, BIAS_NONE) SDPA_CASE(MASK_SLIDING, BIAS_T5) SDPA_CASE(MASK_SLIDING, BIAS_FULL)
+#undef SDPA_CASE
+    return hipErrorInvalidValue;
+}
+
+}  // namespace dec
+
+hipError_t launch_decode_bf16(DecParams p, int D, int mask, int bias, bool out_f32, hipStream_t s) {
+    p.rows = p.G * p.Sq;
+    p.n_rb = dec_row_blocks(p.G, p.Sq);
+    p.n_split = dec_splits(p.B, p.Hkv, p.G, p.Sq, p.Sk);
+    if (D == 128)
+        return out_f32 ? dec::launch_d<128, true>(p, mask, bias, s) : dec::launch_d<128, false>(p, mask, bias, s);
+    if (D == 64)
+        return out_f32 ? dec::launch_d<64, true>(p, mask, bias, s) : dec::launch_d<64, false>(p, mask, bias, s);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace sdpa

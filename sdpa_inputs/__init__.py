@@ -97,6 +97,14 @@ WORKLOADS = {
     "c5mha": _c5(32),
     "c5gqa": _c5(8),
     "c5mqa": _c5(1),
+    # KV-cache decode (survey NEXT-2): one new query row per head against a long cache
+    # (Mistral-7B heads), the MQA variant, and four new rows against a sliding-window cache
+    "dec": Workload("mistral_gqa_decode_b16_q1_k16384", 16, 32, 8, 1, 16384, 128, "bf16",
+                    MASK_CAUSAL, seed=6000),
+    "decmqa": Workload("mqa_decode_b16_q1_k16384", 16, 32, 1, 1, 16384, 128, "bf16",
+                       MASK_CAUSAL, seed=6100),
+    "decsw": Workload("mistral_gqa_decode_b8_q4_k32768_sliding4096", 8, 32, 8, 4, 32768, 128,
+                      "bf16", MASK_SLIDING, window=4096, seed=6200),
 }
 
 

@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_abi_version_and_status_strings(lib):
     assert lib.sdpa_abi_version() == sdpa.ABI_VERSION == 2
-    for code in range(0, 11):
+    for code in range(0, 12):
         s = sdpa.status_str(code)
         assert s and s != "unknown status"
     assert sdpa.status_str(999) == "unknown status"
@@ -146,4 +146,40 @@ def test_backward_binding_rejects_before_launch(lib):
     lse = torch.zeros(1, 2, 8)
     with pytest.raises(ValueError):
         sdpa.bwd(q, q, q, q, lse, q)  # cpu tensors are refused by the binding
+
+
+# decode: the forward's validation, plus the workspace
+def call_dec(entry="sdpa_decode", **kw):
+    a = dict(GOOD, ws=P, ws_bytes=1 << 40)
+    a.update(kw)
+    return sdpa.call_raw_decode(entry, a["q"], a["k"], a["v"], a["out"], a["lse"], a["ws"],
+                                a["ws_bytes"], a["B"], a["Hq"], a["Hkv"], a["Sq"], a["Sk"],
+                                a["D"], a["scale"], a["mask_kind"], a["window"],
+                                a["bias_kind"], a["bias"], a["stream"])
+
+
+DEC_CASES = BAD_CASES + [
+    ("null ws", dict(ws=None), 11),
+    ("misaligned ws", dict(ws=P + 8), 11),
+    ("small ws", dict(ws_bytes=16), 11),
+]
+
+
+@pytest.mark.parametrize("entry", ["sdpa_decode", "sdpa_decode_f32out"])
+@pytest.mark.parametrize("name,kw,code", DEC_CASES, ids=[c[0] for c in DEC_CASES])
+def test_decode_invalid_arguments_return_status(lib, entry, name, kw, code):
+    assert call_dec(entry, **kw) == code
+
+
+def test_decode_workspace_size(lib):
+    # 32 fp32 rows of (D + 2) per (batch, KV head, 32-row block, split); 0 for invalid shapes
+    n = sdpa.decode_ws_bytes(16, 32, 8, 1, 16384, 128)
+    assert n > 0 and n % (32 * 130 * 4) == 0
+    units = n // (32 * 130 * 4)
+    assert units % (16 * 8) == 0
+    assert sdpa.decode_ws_bytes(1, 6, 4, 1, 100, 128) == 0
+    assert sdpa.decode_ws_bytes(1, 8, 8, 1, 100, 96) == 0
+    # the exact requirement is accepted, one byte less is not (validation only, no launch)
+    need = sdpa.decode_ws_bytes(1, 4, 2, 8, 8, 64)
+    assert call_dec(ws_bytes=need - 1) == 11
 
