@@ -18,6 +18,12 @@ baseline is the fp64 oracle timed on the same workload on this host's cores.
 --sweep additionally times every other workload and prints one JSON line per workload on
 stderr.
 
+--decode measures the split-key decode instead (default workload: one new query row per head
+against a 16384-key cache, B16, Mistral-7B heads): a step is one sdpa_decode call (split
+kernel + merge kernel); `value` is HBM GB/s over the algorithmic bytes (visible K/V range, q,
+out, lse); the roofline is HBM-bound against 8 TB/s. The CPU baseline is the fp64 oracle on
+the same rows.
+
 --bwd measures the gradients instead: a step is one sdpa_bwd call (dQ, dK, dV of
 sum(dO * O), two kernel launches) on the same workload, with O and the LSE produced by the
 forward once before the timed region. `value` counts 10*D flop per visible pair (the five
@@ -54,6 +60,12 @@ KERNEL_SOURCES_BWD = ["scaled_dot_product_03_amd/csrc/sdpa_bwd_bf16.hip",
                       "scaled_dot_product_03_amd/csrc/sdpa_device.h",
                       "scaled_dot_product_03_amd/csrc/sdpa_params.h"]
 TRAFFIC_FILE_BWD = "profiles/sdpa_bwd_bf16_c2_traffic.json"
+METRIC_DEC = "attention decode HBM GB/s (visible K/V range + q, out, lse) + % of HBM peak"
+KERNEL_SOURCES_DEC = ["scaled_dot_product_03_amd/csrc/sdpa_decode_bf16.hip",
+                      "scaled_dot_product_03_amd/csrc/sdpa_decode.h",
+                      "scaled_dot_product_03_amd/csrc/sdpa_device.h",
+                      "scaled_dot_product_03_amd/csrc/sdpa_params.h"]
+TRAFFIC_FILE_DEC = "profiles/sdpa_decode_bf16_dec_traffic.json"
 
 
 def kernel_sha(sources=None) -> str:
@@ -64,15 +76,17 @@ def kernel_sha(sources=None) -> str:
     return h.hexdigest()[:16]
 
 
-def load_traffic(workload: str, bwd: bool = False):
-    """HBM bytes per launch (per gradient call with bwd) measured by rocprofv3 counters, if
+def load_traffic(workload: str, bwd: bool = False, decode: bool = False):
+    """HBM bytes per launch (per call with bwd / decode) measured by rocprofv3 counters, if
     taken on this exact kernel source."""
-    path = os.path.join(ROOT, TRAFFIC_FILE_BWD if bwd else TRAFFIC_FILE)
+    path = os.path.join(ROOT, TRAFFIC_FILE_DEC if decode else
+                        (TRAFFIC_FILE_BWD if bwd else TRAFFIC_FILE))
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    sha = kernel_sha(KERNEL_SOURCES_BWD if bwd else KERNEL_SOURCES)
+    sha = kernel_sha(KERNEL_SOURCES_DEC if decode else
+                     (KERNEL_SOURCES_BWD if bwd else KERNEL_SOURCES))
     if rec.get("kernel_sha") != sha or rec.get("workload") != workload:
         return None
     return rec.get("traffic_bytes_per_launch")
@@ -93,9 +107,11 @@ def to_device(inp: si.Inputs):
     return dev(inp.q), dev(inp.k), dev(inp.v), bias
 
 
-def time_workload(sdpa, wl: si.Workload, steps: int, warmup: int, bwd: bool = False):
+def time_workload(sdpa, wl: si.Workload, steps: int, warmup: int, bwd: bool = False,
+                  decode: bool = False):
     """Returns dict with ms_per_step (wall, synchronised), kernel_ms_avg / median (events).
-    With bwd, a step is one gradient call (dQ, dK, dV) instead of one forward."""
+    With bwd, a step is one gradient call (dQ, dK, dV) instead of one forward; with decode,
+    one split-key decode call."""
     import torch
     inp = si.make_inputs(wl)
     q, k, v, bias = to_device(inp)
@@ -113,6 +129,13 @@ def time_workload(sdpa, wl: si.Workload, steps: int, warmup: int, bwd: bool = Fa
 
         def launch():
             sdpa.bwd(q, k, v, out, lse, dout, dq=dq, dk=dk, dv=dv, ws=ws, **kw)
+    elif decode:
+        wsd = torch.empty((max(16, sdpa.decode_ws_bytes(wl.B, wl.Hq, wl.Hkv, wl.Sq, wl.Sk,
+                                                        wl.D)),), dtype=torch.uint8,
+                          device=q.device)
+
+        def launch():
+            sdpa.decode(q, k, v, out=out, lse=lse, ws=wsd, **kw)
     else:
         def launch():
             sdpa.fwd(q, k, v, out=out, lse=lse, **kw)
@@ -230,6 +253,44 @@ def cpu_baseline_bwd(wl: si.Workload, budget_s: float = 15.0):
                       f"{threads} threads, {secs:.1f} s"}
 
 
+def cpu_baseline_decode(wl: si.Workload, budget_s: float = 15.0):
+    """The fp64 oracle on the decode workload's rows, timed on this host's cores: (batch, head)
+    pairs in rounds of `threads` (one pair per thread, BLAS pinned to one thread each) until
+    the workload is done or the budget is spent. GB/s over the same algorithmic bytes."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:          # pragma: no cover
+        threadpool_limits = None
+    threads = oracle.default_threads()
+    inp = si.make_inputs(wl)
+    q, k, v, extra = inp.as_f64()
+    del inp
+    pairs = [(b, h) for b in range(wl.B) for h in range(wl.Hq)]
+    done = 0
+    t0 = time.perf_counter()
+    ctx = threadpool_limits(limits=1) if threadpool_limits else None
+    if ctx:
+        ctx.__enter__()
+    try:
+        while done < len(pairs) and time.perf_counter() - t0 < budget_s:
+            chunk = pairs[done:done + threads]
+            oracle.sdpa_forward(q, k, v, scale=float(np.float32(wl.scale)),
+                                mask_kind=wl.mask_kind, window=wl.window,
+                                bias_kind=wl.bias_kind, bias=extra, threads=threads,
+                                heads=chunk)
+            done += len(chunk)
+    finally:
+        if ctx:
+            ctx.__exit__(None, None, None)
+    secs = time.perf_counter() - t0
+    per_pair = si.algorithmic_bytes_decode(wl) / len(pairs)
+    return {"value": per_pair * done / secs / 1e9, "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{done} of {len(pairs)} (batch, head) pairs of {wl.name} (all {wl.Sq} "
+                      f"query rows each), fp64 numpy, one pair per thread, {secs:.1f} s"}
+
+
 def tile_flops(wl: si.Workload) -> float:
     """FLOP of the matrix work the bf16 kernel performs: 4*D per (row, key) slot of every block
     of 32 query rows x 64 keys it computes, masked slots included. Follows the kernel's tile
@@ -332,11 +393,13 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="c2", choices=sorted(si.WORKLOADS))
+    ap.add_argument("--workload", default=None, choices=sorted(si.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", action="store_true")
     ap.add_argument("--bwd", action="store_true",
                     help="time the gradient call (dQ, dK, dV) instead of the forward")
+    ap.add_argument("--decode", action="store_true",
+                    help="time the split-key decode (workload default: dec)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of attention, run `steps` device-to-device copies of MIB "
                          "MiB (reference kernel for scaling HBM byte counters)")
@@ -366,9 +429,11 @@ def main(argv=None):
                           "launches": args.steps}), flush=True)
         return 0
 
-    wl = si.WORKLOADS[args.workload]
+    wl = si.WORKLOADS[args.workload or ("dec" if args.decode else "c2")]
     if args.bwd:
         return main_bwd(sdpa, wl, args)
+    if args.decode:
+        return main_decode(sdpa, wl, args)
     t = time_workload(sdpa, wl, args.steps, args.warmup)
     flops, achieved = report(wl, t)
     value = flops / (t["ms_per_step"] * 1e-3) / 1e12
@@ -426,6 +491,53 @@ def main(argv=None):
                               "pairs_ratio": round(si.effective_flops(si.WORKLOADS[a]) /
                                                    si.effective_flops(si.WORKLOADS[b]), 4)}),
                   file=sys.stderr, flush=True)
+    return 0
+
+
+def main_decode(sdpa, wl: si.Workload, args) -> int:
+    t = time_workload(sdpa, wl, args.steps, args.warmup, decode=True)
+    nbytes = si.algorithmic_bytes_decode(wl)
+    value = nbytes / (t["ms_per_step"] * 1e-3) / 1e9
+    achieved = nbytes / (t["kernel_ms_avg"] * 1e-3) / 1e9
+    line = {
+        "metric": METRIC_DEC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(t["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "pct_of_hbm_peak": round(100.0 * value / PEAK_HBM_GBS, 2),
+        "config": {**wl.describe(), "pass": "decode (split keys + merge)",
+                   "algorithmic_mb": round(nbytes / 1e6, 2),
+                   "call_ms_median": round(t["kernel_ms_median"], 4),
+                   "event_ms_per_step": round(t["region_ms_per_step"], 4)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": load_traffic(wl.name, decode=True),
+                     "unit_of_work": "one decode call (split kernel + merge kernel)"},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_decode(wl)
+    print(json.dumps(line), flush=True)
+    if args.sweep:
+        for key in ["dec", "decmqa", "decsw"]:
+            w2 = si.WORKLOADS[key]
+            t2 = time_workload(sdpa, w2, max(5, args.steps // 2), max(30, args.warmup),
+                               decode=True)
+            nb = si.algorithmic_bytes_decode(w2)
+            rec = {"workload": key, "pass": "decode", **w2.describe(),
+                   "call_ms_avg": round(t2["kernel_ms_avg"], 4),
+                   "call_ms_median": round(t2["kernel_ms_median"], 4),
+                   "hbm_gbs": round(nb / (t2["kernel_ms_avg"] * 1e-3) / 1e9, 1),
+                   "pct_of_hbm_peak": round(100 * nb / (t2["kernel_ms_avg"] * 1e-3) / 1e9 /
+                                            PEAK_HBM_GBS, 2)}
+            print(json.dumps(rec), file=sys.stderr, flush=True)
     return 0
 
 

@@ -9,11 +9,11 @@
 //   split_kernel : one workgroup = 4 waves = one 32-row block of the G * Sq query rows sharing
 //                  a KV head (row r = i * G + g: query row i of head kvh * G + g), and one
 //                  contiguous range of 64-key tiles. K and V tiles stream through a 4-slot LDS
-//                  ring; waves 0-1 take the two 32-key halves of even tiles, waves 2-3 of odd
-//                  tiles. Per 32 keys: S^T = K.Q^T (lane = query row), an online softmax
-//                  (running max m, sum l, both per row) and O^T += V^T.P^T with V^T from
-//                  transposing LDS reads. The four waves' (m, l, O) are then combined in a
-//                  fixed order into one partial result per split, stored in the workspace
+//                  ring with three tiles in flight. Wave (kh, dh) takes key half kh of every
+//                  tile and head-dim half dh of O: S^T = K.Q^T (lane = query row), an online
+//                  softmax (running max m, sum l, both per row) and O^T += V^T.P^T with V^T
+//                  from transposing LDS reads. The two key halves' (m, l, O) are then combined
+//                  in a fixed order into one partial result per split, stored in the workspace
 //                  (or, with a single split, normalised and stored as the output).
 //   merge_kernel : combines the splits of each row in split order:
 //                  m = max m_s, l = sum l_s 2^(m_s - m), O = sum O_s 2^(m_s - m) / l.
@@ -150,16 +150,19 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void split_kernel(const DecP
         }
     };
 
-    // running state of this wave's rows: max m (log2 units), this lane half's part of the sum l,
-    // and O^T (head dims x rows)
+    // Each 64-key tile is computed by all four waves: wave (kh, dh) takes key half kh and
+    // accumulates the head dims of fragment half dh, so both waves of a key half form the same
+    // S and P (same instructions). Running state of this wave's rows: max m (log2 units), this
+    // lane half's part of the sum l, and its half of O^T (head dims x rows).
+    constexpr int DH = DB / 2;
+    const int kh = wave & 1, dh = wave >> 1;
     float m = -INFINITY, l = 0.f;
-    f32x16 acc[DB];
+    f32x16 acc[DH];
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+    for (int db = 0; db < DH; ++db)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[db][v] = 0.f;
 
-    const int kh = wave & 1;                         // key half of the tile this wave takes
     const uint16_t* fbrow = FB ? (const uint16_t*)p.bias + (((size_t)b * p.Hq + my_hq) * Sq + my_i) * (size_t)Sk
                                : nullptr;
     auto compute = [&](int u) {
@@ -213,10 +216,10 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void split_kernel(const DecP
         l = fmaf(l, alpha, ps);
         m = m_new;
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
+        for (int db = 0; db < DH; ++db)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[db][v] *= alpha;
-        // O^T += V^T P^T over the two 16-key groups of this half
+        // O^T += V^T P^T over the two 16-key groups of this half, head-dim fragments of half dh
 #pragma unroll
         for (int sg = 0; sg < 2; ++sg) {
             u32x4 pk;
@@ -225,35 +228,46 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void split_kernel(const DecP
             bf16x8 vt[DB];
             read_tr<D>(vb, 2 * kh + sg, lane, vt);
 #pragma unroll
-            for (int db = 0; db < DB; ++db)
-                acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt[db], __builtin_bit_cast(bf16x8, pk), acc[db], 0, 0, 0);
+            for (int db = 0; db < DH; ++db)
+                acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dh ? vt[DH + db] : vt[db],
+                                                                  __builtin_bit_cast(bf16x8, pk), acc[db], 0, 0, 0);
         }
     };
 
-    if (nt > 0) dma_tile(0);
-    if (nt > 1) dma_tile(1);
-    dma_wait();
+    // Ring of kNS = 4 tiles, three in flight: tile u + 3 is requested while tile u is computed,
+    // and each iteration waits only for tile u + 1 (the DMA requests of the two younger tiles,
+    // 2 * XPW per tile and wave, may stay outstanding).
+    static_assert(kNS == 4, "three tiles in flight");
+    constexpr int PT = 2 * XPW;                      // DMA requests per tile and wave
+    auto wait_tile = [&](int younger) {              // younger tiles still allowed in flight
+        if (younger >= 2) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * PT) : "memory");
+        else if (younger == 1) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(PT) : "memory");
+        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    };
+    for (int u = 0; u < 3; ++u)
+        if (u < nt) dma_tile(u);
+    wait_tile(min(nt, 3) - 1);
     __syncthreads();
-    const int my_tile = uniform(wave >> 1);
 #pragma unroll 1
-    for (int u0 = 0; u0 < nt; u0 += 2) {
-        if (u0 + 2 < nt) dma_tile(u0 + 2);
-        if (u0 + 3 < nt) dma_tile(u0 + 3);
-        if (u0 + my_tile < nt) compute(u0 + my_tile);
-        dma_wait();
+    for (int u = 0; u < nt; ++u) {
+        if (u + 3 < nt) dma_tile(u + 3);
+        compute(u);
+        wait_tile(min(nt - 1, u + 3) - (u + 1));
         __syncthreads();
     }
 
-    // combine the four waves in order 0..3 (LDS of the ring is free after the last barrier)
-    float* obuf = (float*)smem;                      // [wave][row][D]
-    float* mbuf = obuf + kWaves * 32 * D;            // [wave][row]
-    float* lbuf = mbuf + kWaves * 32;                // [wave][row]
-    static_assert((kWaves * 32 * D + 2 * kWaves * 32) * 4 <= kNS * 2 * TILE * 2, "merge buffer");
+    // combine the two key halves in order (LDS of the ring is free after the last barrier):
+    // waves (0, dh) and (1, dh) hold the same head dims for key halves 0 and 1
+    float* obuf = (float*)smem;                      // [wave][row][D], half of D used per wave
+    float* mbuf = obuf + kWaves * 32 * D;            // [key half][row]
+    float* lbuf = mbuf + 2 * 32;                     // [key half][row]
+    static_assert((kWaves * 32 * D + 4 * 32) * 4 <= kNS * 2 * TILE * 2, "merge buffer");
     {
         const float l_row = partner_sum(l);
         float* orow = obuf + (wave * 32 + r32) * D;
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
+        for (int q = 0; q < DH; ++q) {
+            const int db = dh * DH + q;
             const int d0[2] = {16 * db + 8 * hh, 16 * (db + DB) + 8 * hh};
 #pragma unroll
             for (int c = 0; c < 2; ++c)
@@ -261,42 +275,39 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void split_kernel(const DecP
                 for (int hv = 0; hv < 2; ++hv) {
                     u32x4 w;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) w[e] = __float_as_uint(acc[db][8 * c + 4 * hv + e]);
+                    for (int e = 0; e < 4; ++e) w[e] = __float_as_uint(acc[q][8 * c + 4 * hv + e]);
                     *(u32x4*)(orow + d0[c] + 4 * hv) = w;
                 }
         }
-        if (hh == 0) {
-            mbuf[wave * 32 + r32] = m;
-            lbuf[wave * 32 + r32] = l_row;
+        if (hh == 0 && dh == 0) {
+            mbuf[kh * 32 + r32] = m;
+            lbuf[kh * 32 + r32] = l_row;
         }
     }
     __syncthreads();
     {
         const int row = tid >> 3, cc = tid & 7;      // 32 rows x 8 column chunks of D / 8
-        float mw[kWaves], ms = -INFINITY;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) { mw[w] = mbuf[w * 32 + row]; ms = fmaxf(ms, mw[w]); }
-        float wt[kWaves], ls = 0.f;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-            wt[w] = (ms == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw[w] - ms);
-            ls = fmaf(lbuf[w * 32 + row], wt[w], ls);
-        }
+        const int c0 = cc * (D / 8);
+        // fragment db holds the 16-dim blocks db and db + DB; waves with dh hold fragments
+        // dh * DH .. dh * DH + DH - 1, so the chunk's 16-dim block picks the wave pair
+        const int dhc = ((c0 / 16) % DB) / DH;
+        const float m0 = mbuf[row], m1 = mbuf[32 + row];
+        const float ms = fmaxf(m0, m1);
+        const float w0 = (ms == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m0 - ms);
+        const float w1 = (ms == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m1 - ms);
+        const float ls = fmaf(lbuf[32 + row], w1, lbuf[row] * w0);
+        const float* o0 = obuf + ((2 * dhc + 0) * 32 + row) * D + c0;
+        const float* o1 = obuf + ((2 * dhc + 1) * 32 + row) * D + c0;
         float o[D / 8];
 #pragma unroll
-        for (int c = 0; c < D / 8; ++c) {
-            float t = 0.f;
-#pragma unroll
-            for (int w = 0; w < kWaves; ++w) t = fmaf(obuf[(w * 32 + row) * D + cc * (D / 8) + c], wt[w], t);
-            o[c] = t;
-        }
+        for (int c = 0; c < D / 8; ++c) o[c] = fmaf(o1[c], w1, o0[c] * w0);
         const int rg = 32 * rb + row;
         if (p.n_split == 1) {
             if (rg < p.rows)
-                store_out<D, OUT_F32>(p, b, kvh, rg, cc * (D / 8), o, ls > 0.f ? 1.f / ls : 0.f,
+                store_out<D, OUT_F32>(p, b, kvh, rg, c0, o, ls > 0.f ? 1.f / ls : 0.f,
                                       ls > 0.f ? (ms + __builtin_amdgcn_logf(ls)) * kLn2 : -INFINITY);
-        } else {
-            float* dst = ws_o + row * D + cc * (D / 8);
+        } else if (rg < p.rows) {
+            float* dst = ws_o + row * D + c0;
 #pragma unroll
             for (int c = 0; c < D / 8; c += 4) {
                 u32x4 w;

@@ -244,6 +244,31 @@ def algorithmic_bytes(wl: Workload) -> float:
     return float(b)
 
 
+def decode_key_range(wl: Workload) -> int:
+    """Keys of one (batch, KV head) that some query row may see (bottom-right alignment)."""
+    off = wl.Sk - wl.Sq
+    pmin, pmax = off, wl.Sq - 1 + off
+    lo, hi = 0, wl.Sk - 1
+    if wl.mask_kind != MASK_NONE:
+        hi = min(hi, pmax)
+    if wl.mask_kind == MASK_SLIDING:
+        lo = max(0, pmin - wl.window + 1)
+    return max(0, hi - lo + 1)
+
+
+def algorithmic_bytes_decode(wl: Workload) -> float:
+    """Decode (bf16): read the visible range of the K/V cache and q once, write out and lse
+    once (plus a full bias, read once)."""
+    es = 2
+    b = es * wl.B * wl.Hkv * wl.D * 2 * decode_key_range(wl)
+    b += es * wl.B * wl.D * 2 * wl.Sq * wl.Hq + 4 * wl.B * wl.Hq * wl.Sq
+    if wl.bias_kind == BIAS_FULL:
+        b += es * wl.B * wl.Hq * wl.Sq * wl.Sk
+    elif wl.bias_kind == BIAS_T5:
+        b += 4 * wl.Hq * T5_NUM_BUCKETS
+    return float(b)
+
+
 def algorithmic_bytes_bwd(wl: Workload) -> float:
     """One gradient call (bf16): read q, k, v, out, dout, lse (and a full bias) once, write dq,
     dk, dv once, and write then read the fp32 row sums rowsum(dout * out) once."""
