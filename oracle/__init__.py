@@ -13,3 +13,4 @@ from .sdpa_ref import (  # noqa: F401
     default_threads,
 )
 from .sdpa_bwd_ref import head_backward, sdpa_backward  # noqa: F401
+from .sdpa_varlen_ref import sdpa_forward_varlen  # noqa: F401
