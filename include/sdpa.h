@@ -134,6 +134,36 @@ int sdpa_bwd_f32out(const void* q, const void* k, const void* v, const void* out
                     void* stream);
 
 /*
+ * Packed variable-length sequences: n_seqs sequences stored back to back along the token axis,
+ * each attending only to itself (a block-diagonal document mask, generated from the offsets;
+ * training with packing in the transformers issue "Slowdown in Training Speed Due to SDPA
+ * Mask Fix in Version 4.40.0"). Sequence s owns query tokens cu_seqlens_q[s] ..
+ * cu_seqlens_q[s+1]-1 and key tokens cu_seqlens_k[s] .. cu_seqlens_k[s+1]-1; inside it the
+ * operation, masks (bottom-right alignment with the sequence's own lengths), T5 bias and head
+ * sharing are those of sdpa_fwd.
+ *   q, out : [total_q][Hq][D]    k, v : [total_k][Hkv][D]    lse : [Hq][total_q] fp32
+ *   cu_seqlens_q, cu_seqlens_k : DEVICE int32 arrays of n_seqs + 1 nondecreasing offsets.
+ *   max_seqlen_q / max_seqlen_k : upper bounds of the sequences' lengths (they size the grid).
+ * bias_kind: NONE or T5 (a full bias has no packed frame: SDPA_ERR_BIAS). The offsets live on
+ * the device and are not read by the host: a sequence whose offsets leave [0, total] or exceed
+ * the stated maximum lengths is treated as empty (its rows are not written) instead of being
+ * read out of bounds. Tokens not covered by any sequence are not written.
+ * Same kernel as sdpa_fwd (bitwise: a pack of equal-length sequences gives sdpa_fwd's bits).
+ */
+int sdpa_fwd_varlen(const void* q, const void* k, const void* v, void* out, float* lse,
+                    const int* cu_seqlens_q, const int* cu_seqlens_k, int n_seqs, int total_q,
+                    int total_k, int max_seqlen_q, int max_seqlen_k, int Hq, int Hkv, int D,
+                    float scale, int mask_kind, int window, int bias_kind, const void* bias_tbl,
+                    void* stream);
+
+/* Same as sdpa_fwd_varlen with fp32 out. */
+int sdpa_fwd_varlen_f32out(const void* q, const void* k, const void* v, float* out, float* lse,
+                           const int* cu_seqlens_q, const int* cu_seqlens_k, int n_seqs,
+                           int total_q, int total_k, int max_seqlen_q, int max_seqlen_k, int Hq,
+                           int Hkv, int D, float scale, int mask_kind, int window, int bias_kind,
+                           const void* bias_tbl, void* stream);
+
+/*
  * KV-cache decode: the forward above (same operation, arguments, layouts, masks, biases, head
  * sharing and outputs) for few query rows against a long key/value cache, the generation
  * setting of the KV-cache section of the Medium post "Simplified Explanation of Attention"

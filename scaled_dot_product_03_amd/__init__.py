@@ -8,6 +8,7 @@ fallback: if the library is missing, calls raise.
     out, lse = fwd(q, k, v, mask="causal")           # q [B,Sq,Hq,D], k/v [B,Sk,Hkv,D]
     dq, dk, dv = bwd(q, k, v, out, lse, dout, mask="causal")
     out, lse = decode(q_new, k_cache, v_cache, mask="causal")   # few rows, long cache
+    out, lse = fwd_varlen(q_packed, k_packed, v_packed, cu_q, cu_k, max_q, max_k)
 
 Layout follows the "jax-gpu-05-attention-gpu" codelab, section 3 (batch, sequence, heads,
 head dim). lse is [B, Hq, Sq] fp32 (natural log).
@@ -36,7 +37,8 @@ STATUS_NAMES = {0: "SDPA_OK", 1: "SDPA_ERR_NULL", 2: "SDPA_ERR_SHAPE", 3: "SDPA_
 # symbols exported by the library (must match include/sdpa.h)
 ENTRY_POINTS = ("sdpa_fwd", "sdpa_fwd_bf16_f32out", "sdpa_fwd_f32", "sdpa_bwd",
                 "sdpa_bwd_f32out", "sdpa_decode_ws_bytes", "sdpa_decode", "sdpa_decode_f32out",
-                "sdpa_status_str", "sdpa_abi_version")
+                "sdpa_fwd_varlen", "sdpa_fwd_varlen_f32out", "sdpa_status_str",
+                "sdpa_abi_version")
 ABI_VERSION = 2
 
 _lib = None
@@ -82,6 +84,12 @@ def load():
         fn = getattr(L, name)
         fn.argtypes = dec_args
         fn.restype = ctypes.c_int
+    vl_args = [ctypes.c_void_p] * 7 + [ctypes.c_int] * 8 + [ctypes.c_float] + \
+              [ctypes.c_int] * 3 + [ctypes.c_void_p, ctypes.c_void_p]
+    for name in ("sdpa_fwd_varlen", "sdpa_fwd_varlen_f32out"):
+        fn = getattr(L, name)
+        fn.argtypes = vl_args
+        fn.restype = ctypes.c_int
     L.sdpa_status_str.argtypes = [ctypes.c_int]
     L.sdpa_status_str.restype = ctypes.c_char_p
     L.sdpa_abi_version.argtypes = []
@@ -116,6 +124,15 @@ def call_raw_decode(entry: str, q, k, v, out, lse, ws, ws_bytes, B, Hq, Hkv, Sq,
     fn = getattr(load(), entry)
     return fn(q, k, v, out, lse, ws, ws_bytes, B, Hq, Hkv, Sq, Sk, D, ctypes.c_float(scale),
               mask_kind, window, bias_kind, bias, stream)
+
+
+def call_raw_varlen(entry: str, q, k, v, out, lse, cu_q, cu_k, n_seqs, total_q, total_k,
+                    max_q, max_k, Hq, Hkv, D, scale, mask_kind, window, bias_kind, bias,
+                    stream) -> int:
+    """Call a packed-sequence entry point with raw integer pointers; returns the status."""
+    fn = getattr(load(), entry)
+    return fn(q, k, v, out, lse, cu_q, cu_k, n_seqs, total_q, total_k, max_q, max_k, Hq, Hkv, D,
+              ctypes.c_float(scale), mask_kind, window, bias_kind, bias, stream)
 
 
 def decode_ws_bytes(B, Hq, Hkv, Sq, Sk, D) -> int:
@@ -292,6 +309,55 @@ def decode(q, k, v, *, scale: Optional[float] = None, mask="causal", window: int
                            lse.data_ptr(), ws.data_ptr(), ws.numel() * ws.element_size(), B, Hq,
                            Hkv, Sq, Sk, D, ctypes.c_float(scale), mk, int(window), bk, bias_ptr,
                            stream)
+    if st != SDPA_OK:
+        raise SdpaError(st, L.sdpa_status_str(st).decode())
+    return out, lse
+
+
+def fwd_varlen(q, k, v, cu_q, cu_k, max_seqlen_q: int, max_seqlen_k: int, *,
+               scale: Optional[float] = None, mask="causal", window: int = 0, bias_kind="none",
+               bias=None, out=None, lse=None, out_dtype=None, stream=None):
+    """Packed variable-length sequences on the current HIP stream. Returns (out, lse).
+
+    q [total_q, Hq, D], k/v [total_k, Hkv, D] contiguous bf16 cuda tensors; cu_q, cu_k int32
+    cuda tensors of n + 1 offsets; lse is [Hq, total_q]. bias_kind "none" or "t5".
+    """
+    import torch
+
+    L = load()
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3 or tuple(k.shape) != tuple(v.shape):
+        raise ValueError("q [total_q, Hq, D], k and v [total_k, Hkv, D] expected")
+    total_q, Hq, D = q.shape
+    total_k, Hkv, Dk = k.shape
+    if Dk != D or q.dtype != torch.bfloat16 or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must be bf16 with one head dim")
+    for t in (q, k, v, cu_q, cu_k):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("inputs must be contiguous cuda tensors")
+    if cu_q.dtype != torch.int32 or cu_k.dtype != torch.int32 or cu_q.numel() != cu_k.numel():
+        raise ValueError("cu_q and cu_k must be int32 tensors of equal length")
+    n = cu_q.numel() - 1
+    mk = _kind(mask, _MASKS, "mask")
+    bk = _kind(bias_kind, _BIASES, "bias kind")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    odt = out_dtype or torch.bfloat16
+    entry = "sdpa_fwd_varlen" if odt == torch.bfloat16 else "sdpa_fwd_varlen_f32out"
+    bias_ptr = None
+    if bk == BIAS_T5:
+        bias_ptr = _bias_ptr(bk, bias, q.dtype, 1, Hq, 1, 1)
+    elif bias is not None or bk != BIAS_NONE:
+        raise ValueError("packed sequences take no bias or a T5 table")
+    if out is None:
+        out = torch.empty((total_q, Hq, D), dtype=odt, device=q.device)
+    if lse is None:
+        lse = torch.empty((Hq, total_q), dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = getattr(L, entry)(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                           lse.data_ptr(), cu_q.data_ptr(), cu_k.data_ptr(), n, total_q, total_k,
+                           int(max_seqlen_q), int(max_seqlen_k), Hq, Hkv, D,
+                           ctypes.c_float(scale), mk, int(window), bk, bias_ptr, stream)
     if st != SDPA_OK:
         raise SdpaError(st, L.sdpa_status_str(st).decode())
     return out, lse

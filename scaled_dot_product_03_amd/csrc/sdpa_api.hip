@@ -134,9 +134,52 @@ int decode_common(const void* q, const void* k, const void* v, void* out, float*
     return e == hipSuccess ? SDPA_OK : SDPA_ERR_LAUNCH;
 }
 
+int varlen_common(const void* q, const void* k, const void* v, void* out, float* lse,
+                  const int* cu_q, const int* cu_k, int n_seqs, int total_q, int total_k,
+                  int max_q, int max_k, int Hq, int Hkv, int D, float scale, int mask_kind,
+                  int window, int bias_kind, const void* bias_tbl, void* stream, bool out_f32) {
+    if (!cu_q || !cu_k) return SDPA_ERR_NULL;
+    if (n_seqs < 1 || total_q < 1 || total_k < 1 || max_q < 1 || max_k < 1) return SDPA_ERR_SHAPE;
+    if (bias_kind == SDPA_BIAS_FULL) return SDPA_ERR_BIAS;
+    // the per-token checks of the dense forward, on one packed "batch" of total tokens
+    int st = validate(q, k, v, out, lse, 1, Hq, Hkv, total_q, total_k, D, scale, mask_kind,
+                      window, bias_kind, bias_tbl, 2);
+    if (st != SDPA_OK) return st;
+    if ((long long)n_seqs * Hq * ((max_q + 255) / 256) >= (1LL << 31)) return SDPA_ERR_SHAPE;
+    if (!aligned(cu_q, 4) || !aligned(cu_k, 4)) return SDPA_ERR_ALIGN;
+    sdpa::FwdParams p = make_params(q, k, v, out, lse, n_seqs, Hq, Hkv, max_q, max_k, scale,
+                                    mask_kind, window, bias_tbl);
+    p.cu_q = cu_q;
+    p.cu_k = cu_k;
+    p.total_q = total_q;
+    p.total_k = total_k;
+    hipError_t e = sdpa::launch_fwd_bf16(p, D, mask_kind, bias_kind, out_f32, (hipStream_t)stream);
+    return e == hipSuccess ? SDPA_OK : SDPA_ERR_LAUNCH;
+}
+
 }  // namespace
 
 extern "C" {
+
+int sdpa_fwd_varlen(const void* q, const void* k, const void* v, void* out, float* lse,
+                    const int* cu_seqlens_q, const int* cu_seqlens_k, int n_seqs, int total_q,
+                    int total_k, int max_seqlen_q, int max_seqlen_k, int Hq, int Hkv, int D,
+                    float scale, int mask_kind, int window, int bias_kind, const void* bias_tbl,
+                    void* stream) {
+    return varlen_common(q, k, v, out, lse, cu_seqlens_q, cu_seqlens_k, n_seqs, total_q, total_k,
+                         max_seqlen_q, max_seqlen_k, Hq, Hkv, D, scale, mask_kind, window,
+                         bias_kind, bias_tbl, stream, false);
+}
+
+int sdpa_fwd_varlen_f32out(const void* q, const void* k, const void* v, float* out, float* lse,
+                           const int* cu_seqlens_q, const int* cu_seqlens_k, int n_seqs,
+                           int total_q, int total_k, int max_seqlen_q, int max_seqlen_k, int Hq,
+                           int Hkv, int D, float scale, int mask_kind, int window, int bias_kind,
+                           const void* bias_tbl, void* stream) {
+    return varlen_common(q, k, v, out, lse, cu_seqlens_q, cu_seqlens_k, n_seqs, total_q, total_k,
+                         max_seqlen_q, max_seqlen_k, Hq, Hkv, D, scale, mask_kind, window,
+                         bias_kind, bias_tbl, stream, true);
+}
 
 size_t sdpa_decode_ws_bytes(int B, int Hq, int Hkv, int Sq, int Sk, int D) {
     if (!dec_shape_ok(B, Hq, Hkv, Sq, Sk, D)) return 0;

@@ -108,7 +108,7 @@ __device__ __forceinline__ s16x4 lds_read_tr(const uint16_t* p) {
 __device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
 
 
-template <int D, int MASK, int BIAS, bool OUT_F32>
+template <int D, int MASK, int BIAS, bool OUT_F32, bool VARLEN>
 __global__ __launch_bounds__(kThreads, 1) void sdpa_fwd_bf16_kernel(const FwdParams p) {
     constexpr int CH = D / 8;           // 16-byte chunks per K/V row
     constexpr int KS = D / 16;          // k-steps of Q.K^T
@@ -139,8 +139,24 @@ __global__ __launch_bounds__(kThreads, 1) void sdpa_fwd_bf16_kernel(const FwdPar
 
     const WorkItem w = decode_work(p, blockIdx.x);
     const int b = w.b, hq = w.hq, kvh = hq / p.G;
-    const int Sq = p.Sq, Sk = p.Sk, off = p.off;
+    int Sq = p.Sq, Sk = p.Sk, off = p.off;
+    size_t q_base = (size_t)b * Sq, k_base = (size_t)b * Sk;   // first token of the sequence
+    if constexpr (VARLEN) {
+        // packed sequence b: its own lengths and alignment; offsets that leave the packed
+        // buffers or exceed the launch's longest sequence make it empty
+        const int qs = p.cu_q[b], qe = p.cu_q[b + 1], ks = p.cu_k[b], ke = p.cu_k[b + 1];
+        const bool ok = 0 <= qs && qs <= qe && qe <= p.total_q && qe - qs <= p.Sq &&
+                        0 <= ks && ks <= ke && ke <= p.total_k && ke - ks <= p.Sk;
+        Sq = ok ? qe - qs : 0;
+        Sk = ok ? ke - ks : 0;
+        off = Sk - Sq;
+        q_base = (size_t)(ok ? qs : 0);
+        k_base = (size_t)(ok ? ks : 0);
+    }
     const int q0 = w.qt * kBM;
+    if constexpr (VARLEN) {
+        if (q0 >= Sq) return;     // query tile past the end of a shorter sequence
+    }
 
     // ---- key range of the workgroup; tiles outside it are never visited -------------------
     const int pa = q0 + off;
@@ -153,9 +169,9 @@ __global__ __launch_bounds__(kThreads, 1) void sdpa_fwd_bf16_kernel(const FwdPar
 
     const size_t q_row = (size_t)p.Hq * D;
     const size_t kv_row = (size_t)p.Hkv * D;
-    const uint16_t* qg = (const uint16_t*)p.q + ((size_t)b * Sq * p.Hq + hq) * D;
-    const uint16_t* kg = (const uint16_t*)p.k + ((size_t)b * Sk * p.Hkv + kvh) * D;
-    const uint16_t* vg = (const uint16_t*)p.v + ((size_t)b * Sk * p.Hkv + kvh) * D;
+    const uint16_t* qg = (const uint16_t*)p.q + (q_base * p.Hq + hq) * D;
+    const uint16_t* kg = (const uint16_t*)p.k + (k_base * p.Hkv + kvh) * D;
+    const uint16_t* vg = (const uint16_t*)p.v + (k_base * p.Hkv + kvh) * D;
 
     const int wq0 = q0 + wave * 32;          // first query row of this wave
     const int my_i = wq0 + r32;              // query row of this lane
@@ -165,9 +181,10 @@ __global__ __launch_bounds__(kThreads, 1) void sdpa_fwd_bf16_kernel(const FwdPar
     const int pwa = wq0 + off;
     const int pwb = min(wq0 + 31, Sq - 1) + off;
 
-    float* lse_row = p.lse + ((size_t)b * p.Hq + hq) * Sq;
+    float* lse_row = VARLEN ? p.lse + (size_t)hq * p.total_q + q_base
+                            : p.lse + ((size_t)b * p.Hq + hq) * Sq;
     auto out_ptr = [&](int i) -> char* {
-        const size_t e = ((size_t)b * Sq + i) * q_row + (size_t)hq * D;
+        const size_t e = (q_base + i) * q_row + (size_t)hq * D;
         return (char*)p.out + e * (OUT_F32 ? 4 : 2);
     };
 
@@ -694,18 +711,18 @@ __global__ __launch_bounds__(kThreads, 1) void sdpa_fwd_bf16_kernel(const FwdPar
 // ------------------------------------------------------------------------------------------
 // host-side launch (called by the C ABI after validation)
 // ------------------------------------------------------------------------------------------
-template <int D, int MASK, int BIAS, bool OUT_F32>
+template <int D, int MASK, int BIAS, bool OUT_F32, bool VARLEN>
 static hipError_t launch_one(const FwdParams& p, hipStream_t stream) {
     const unsigned grid = (unsigned)((size_t)p.B * p.Hq * p.n_qt);
-    hipLaunchKernelGGL((sdpa_fwd_bf16_kernel<D, MASK, BIAS, OUT_F32>), dim3(grid), dim3(kThreads),
-                       0, stream, p);
+    hipLaunchKernelGGL((sdpa_fwd_bf16_kernel<D, MASK, BIAS, OUT_F32, VARLEN>), dim3(grid),
+                       dim3(kThreads), 0, stream, p);
     return hipGetLastError();
 }
 
 template <int D, bool OUT_F32>
 static hipError_t launch_d(const FwdParams& p, int mask, int bias, hipStream_t s) {
 #define SDPA_CASE(M, Bk) \
-    if (mask == M && bias == Bk) return launch_one<D, M, Bk, OUT_F32>(p, s);
+    if (mask == M && bias == Bk) return launch_one<D, M, Bk, OUT_F32, false>(p, s);
     SDPA_CASE(MASK_NONE, BIAS_NONE) SDPA_CASE(MASK_NONE, BIAS_T5) SDPA_CASE(MASK_NONE, BIAS_FULL)
     SDPA_CASE(MASK_CAUSAL, BIAS_NONE) SDPA_CASE(MASK_CAUSAL, BIAS_T5) SDPA_CASE(MASK_CAUSAL, BIAS_FULL)
     SDPA_CASE(MASK_SLIDING, BIAS_NONE) SDPA_CASE(MASK_SLIDING, BIAS_T5) SDPA_CASE(MASK_SLIDING, BIAS_FULL)
@@ -713,9 +730,28 @@ static hipError_t launch_d(const FwdParams& p, int mask, int bias, hipStream_t s
     return hipErrorInvalidValue;
 }
 
+// packed variable-length sequences: no full bias (no [B][Hq][Sq][Sk] frame)
+template <int D, bool OUT_F32>
+static hipError_t launch_varlen_d(const FwdParams& p, int mask, int bias, hipStream_t s) {
+#define SDPA_CASE(M, Bk) \
+    if (mask == M && bias == Bk) return launch_one<D, M, Bk, OUT_F32, true>(p, s);
+    SDPA_CASE(MASK_NONE, BIAS_NONE) SDPA_CASE(MASK_NONE, BIAS_T5)
+    SDPA_CASE(MASK_CAUSAL, BIAS_NONE) SDPA_CASE(MASK_CAUSAL, BIAS_T5)
+    SDPA_CASE(MASK_SLIDING, BIAS_NONE) SDPA_CASE(MASK_SLIDING, BIAS_T5)
+#undef SDPA_CASE
+    return hipErrorInvalidValue;
+}
+
 hipError_t launch_fwd_bf16(FwdParams p, int D, int mask, int bias, bool out_f32, hipStream_t s) {
     p.n_qt = (p.Sq + kBM - 1) / kBM;
     p.xcd_remap = ((p.B * p.Hkv) % 8 == 0) ? 1 : 0;
+    if (p.cu_q) {
+        if (D == 128)
+            return out_f32 ? launch_varlen_d<128, true>(p, mask, bias, s) : launch_varlen_d<128, false>(p, mask, bias, s);
+        if (D == 64)
+            return out_f32 ? launch_varlen_d<64, true>(p, mask, bias, s) : launch_varlen_d<64, false>(p, mask, bias, s);
+        return hipErrorInvalidValue;
+    }
     if (D == 128) return out_f32 ? launch_d<128, true>(p, mask, bias, s) : launch_d<128, false>(p, mask, bias, s);
     if (D == 64) return out_f32 ? launch_d<64, true>(p, mask, bias, s) : launch_d<64, false>(p, mask, bias, s);
     return hipErrorInvalidValue;

@@ -29,6 +29,12 @@ struct FwdParams {
     int xcd_remap;       // 1: place all work of one (batch, KV head) on one XCD
     float scale;         // softmax scale
     float scale_log2;    // scale * log2(e)
+    // Packed variable-length sequences (B = number of sequences, Sq / Sk = the longest query /
+    // key sequence): sequence b owns query tokens cu_q[b] .. cu_q[b+1]-1 of q/out ([total_q]
+    // [Hq][D]) and key tokens cu_k[b] .. cu_k[b+1]-1 of k/v; lse is [Hq][total_q].
+    const int* cu_q;
+    const int* cu_k;
+    int total_q, total_k;
 };
 
 // Backward: gradients of L = sum(dO * O) for the forward above.

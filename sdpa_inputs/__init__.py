@@ -194,6 +194,107 @@ def make_dout(wl: Workload) -> np.ndarray:
     return _store(normal_f32(wl.seed + 5, (wl.B, wl.Sq, wl.Hq, wl.D)), wl.dtype)
 
 
+# ----------------------------------------------------------------------------------------------
+# Packed variable-length sequences (survey NEXT-3)
+# ----------------------------------------------------------------------------------------------
+@dataclasses.dataclass(frozen=True)
+class VarlenWorkload:
+    """Sequences packed back to back: lengths drawn from a seeded log-normal (median `median`,
+    log-sd `sigma`, clipped to [lo, hi]) until they fill `total` tokens (the last one cut)."""
+    name: str
+    total: int
+    Hq: int
+    Hkv: int
+    D: int
+    mask_kind: int
+    window: int = 0
+    bias_kind: int = BIAS_NONE
+    seed: int = 0
+    median: float = 1024.0
+    sigma: float = 0.8
+    lo: int = 16
+    hi: int = 8192
+    scale_override: Optional[float] = None
+    lengths_override: Optional[tuple] = None
+
+    @property
+    def scale(self) -> float:
+        if self.scale_override is not None:
+            return float(np.float32(self.scale_override))
+        return float(np.float32(1.0 / np.sqrt(self.D)))
+
+    def lengths(self) -> list:
+        if self.lengths_override is not None:
+            return list(self.lengths_override)
+        rng = np.random.default_rng(self.seed + 9)
+        out, left = [], self.total
+        while left > 0:
+            n = int(np.clip(round(self.median * np.exp(self.sigma * rng.standard_normal())),
+                            self.lo, self.hi))
+            n = min(n, left)
+            out.append(n)
+            left -= n
+        return out
+
+    def replace(self, **kw) -> "VarlenWorkload":
+        return dataclasses.replace(self, **kw)
+
+    def describe(self) -> dict:
+        ls = self.lengths()
+        d = dict(workload=self.name, packed_tokens=sum(ls), sequences=len(ls),
+                 max_len=max(ls), Hq=self.Hq, Hkv=self.Hkv, D=self.D, dtype="bf16",
+                 mask=MASK_NAMES[self.mask_kind], bias=BIAS_NAMES[self.bias_kind])
+        if self.mask_kind == MASK_SLIDING:
+            d["window"] = self.window
+        return d
+
+
+# Mistral-7B heads, 32768 packed tokens (one training micro-batch's worth, like B4 x S8192),
+# causal inside each sequence; lengths stand in for packed instruction-tuning examples
+VARLEN_WORKLOADS = {
+    "vl": VarlenWorkload("mistral_gqa_packed_32768_causal", 32768, 32, 8, 128, MASK_CAUSAL,
+                         seed=7000),
+}
+
+
+@dataclasses.dataclass
+class VarlenInputs:
+    wl: VarlenWorkload
+    q: np.ndarray          # bf16 words [total, Hq, D]
+    k: np.ndarray          # bf16 words [total_k, Hkv, D]
+    v: np.ndarray
+    cu_q: np.ndarray       # int32 [n + 1]
+    cu_k: np.ndarray
+    t5_table: Optional[np.ndarray] = None
+
+    def as_f64(self):
+        return (bf16_bits_to_f64(self.q), bf16_bits_to_f64(self.k), bf16_bits_to_f64(self.v),
+                None if self.t5_table is None else self.t5_table.astype(np.float64))
+
+
+def make_varlen_inputs(wl: VarlenWorkload, key_lengths: Optional[list] = None) -> VarlenInputs:
+    """q [total_q, Hq, D], k/v [total_k, Hkv, D] bf16 from seeds seed, seed+1, seed+2 (T5 table
+    seed+3); key lengths equal the query lengths unless given."""
+    lq = wl.lengths()
+    lk = list(key_lengths) if key_lengths is not None else lq
+    cu_q = np.concatenate([[0], np.cumsum(lq)]).astype(np.int32)
+    cu_k = np.concatenate([[0], np.cumsum(lk)]).astype(np.int32)
+    q = f32_to_bf16_bits(normal_f32(wl.seed, (int(cu_q[-1]), wl.Hq, wl.D)))
+    k = f32_to_bf16_bits(normal_f32(wl.seed + 1, (int(cu_k[-1]), wl.Hkv, wl.D)))
+    v = f32_to_bf16_bits(normal_f32(wl.seed + 2, (int(cu_k[-1]), wl.Hkv, wl.D)))
+    inp = VarlenInputs(wl, q, k, v, cu_q, cu_k)
+    if wl.bias_kind == BIAS_T5:
+        inp.t5_table = normal_f32(wl.seed + 3, (wl.Hq, T5_NUM_BUCKETS))
+    return inp
+
+
+def varlen_visible_pairs(wl: VarlenWorkload, key_lengths: Optional[list] = None) -> int:
+    """Visible (query, key) pairs of one head summed over the sequences."""
+    lq = wl.lengths()
+    lk = list(key_lengths) if key_lengths is not None else lq
+    return sum(visible_pairs(a, b, wl.mask_kind, wl.window) for a, b in zip(lq, lk) if a and b)
+
+
 def small(wl: Workload, *, B=None, Hq=None, Hkv=None, Sq=None, Sk=None, window=None,
           name_suffix="small") -> Workload:
     """A reduced copy of a workload with the same kinds (for element-by-element parity)."""

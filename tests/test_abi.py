@@ -183,3 +183,34 @@ def test_decode_workspace_size(lib):
     need = sdpa.decode_ws_bytes(1, 4, 2, 8, 8, 64)
     assert call_dec(ws_bytes=need - 1) == 11
 
+
+
+# packed variable-length sequences
+def call_vl(entry="sdpa_fwd_varlen", **kw):
+    a = dict(q=P, k=P, v=P, out=P, lse=P, cu_q=P, cu_k=P, n=3, tq=100, tk=100, mq=50, mk=50,
+             Hq=4, Hkv=2, D=64, scale=0.125, mask_kind=1, window=0, bias_kind=0, bias=None,
+             stream=None)
+    a.update(kw)
+    return sdpa.call_raw_varlen(entry, a["q"], a["k"], a["v"], a["out"], a["lse"], a["cu_q"],
+                                a["cu_k"], a["n"], a["tq"], a["tk"], a["mq"], a["mk"], a["Hq"],
+                                a["Hkv"], a["D"], a["scale"], a["mask_kind"], a["window"],
+                                a["bias_kind"], a["bias"], a["stream"])
+
+
+VL_CASES = [
+    ("null cu_q", dict(cu_q=None), 1), ("null cu_k", dict(cu_k=None), 1),
+    ("null q", dict(q=None), 1),
+    ("no sequences", dict(n=0), 2), ("no query tokens", dict(tq=0), 2),
+    ("no key tokens", dict(tk=0), 2), ("max len 0", dict(mq=0), 2),
+    ("heads", dict(Hq=6, Hkv=4), 3), ("head dim", dict(D=32), 4),
+    ("mask", dict(mask_kind=7), 5), ("window", dict(mask_kind=2, window=0), 6),
+    ("full bias", dict(bias_kind=2, bias=P), 7), ("t5 without table", dict(bias_kind=1), 7),
+    ("scale", dict(scale=math.inf), 8),
+    ("misaligned cu", dict(cu_q=P + 2), 9), ("misaligned q", dict(q=P + 4), 9),
+]
+
+
+@pytest.mark.parametrize("entry", ["sdpa_fwd_varlen", "sdpa_fwd_varlen_f32out"])
+@pytest.mark.parametrize("name,kw,code", VL_CASES, ids=[c[0] for c in VL_CASES])
+def test_varlen_invalid_arguments_return_status(lib, entry, name, kw, code):
+    assert call_vl(entry, **kw) == code
