@@ -24,6 +24,10 @@ kernel + merge kernel); `value` is HBM GB/s over the algorithmic bytes (visible 
 out, lse); the roofline is HBM-bound against 8 TB/s. The CPU baseline is the fp64 oracle on
 the same rows.
 
+--varlen measures packed variable-length sequences (32768 tokens of Mistral-7B heads in
+sequences of seeded log-normal lengths, causal inside each): a step is one sdpa_fwd_varlen
+call; `value` is effective TFLOP/s over the visible pairs of all sequences (4*D flop each).
+
 --bwd measures the gradients instead: a step is one sdpa_bwd call (dQ, dK, dV of
 sum(dO * O), two kernel launches) on the same workload, with O and the LSE produced by the
 forward once before the timed region. `value` counts 10*D flop per visible pair (the five
@@ -400,6 +404,8 @@ def main(argv=None):
                     help="time the gradient call (dQ, dK, dV) instead of the forward")
     ap.add_argument("--decode", action="store_true",
                     help="time the split-key decode (workload default: dec)")
+    ap.add_argument("--varlen", action="store_true",
+                    help="time packed variable-length sequences (workload vl)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of attention, run `steps` device-to-device copies of MIB "
                          "MiB (reference kernel for scaling HBM byte counters)")
@@ -429,6 +435,8 @@ def main(argv=None):
                           "launches": args.steps}), flush=True)
         return 0
 
+    if args.varlen:
+        return main_varlen(sdpa, si.VARLEN_WORKLOADS["vl"], args)
     wl = si.WORKLOADS[args.workload or ("dec" if args.decode else "c2")]
     if args.bwd:
         return main_bwd(sdpa, wl, args)
@@ -491,6 +499,105 @@ def main(argv=None):
                               "pairs_ratio": round(si.effective_flops(si.WORKLOADS[a]) /
                                                    si.effective_flops(si.WORKLOADS[b]), 4)}),
                   file=sys.stderr, flush=True)
+    return 0
+
+
+def time_varlen(sdpa, wl, steps: int, warmup: int):
+    import torch
+    inp = si.make_varlen_inputs(wl)
+
+    def bf(a):
+        return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+    q, k, v = bf(inp.q), bf(inp.k), bf(inp.v)
+    cq, ck = torch.from_numpy(inp.cu_q).cuda(), torch.from_numpy(inp.cu_k).cuda()
+    m = int(np.diff(inp.cu_q).max())
+    out = torch.empty_like(q)
+    lse = torch.empty((wl.Hq, q.shape[0]), dtype=torch.float32, device=q.device)
+    stream = torch.cuda.current_stream()
+
+    def launch():
+        sdpa.fwd_varlen(q, k, v, cq, ck, m, m, scale=wl.scale, mask=wl.mask_kind,
+                        window=wl.window, out=out, lse=lse, stream=stream.cuda_stream)
+    for _ in range(warmup):
+        launch()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        launch()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    for i in range(steps):
+        starts[i].record(stream)
+        launch()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    ev = np.array([a.elapsed_time(b) for a, b in zip(starts, ends)])
+    return dict(ms_per_step=1e3 * wall / steps, kernel_ms_avg=float(ev.mean()),
+                kernel_ms_median=float(np.median(ev)))
+
+
+def cpu_baseline_varlen(wl, budget_s: float = 12.0):
+    """The fp64 packed-sequence oracle on whole sequences of the pack, shortest first, until
+    the budget is spent; TFLOP/s over their visible pairs."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:          # pragma: no cover
+        threadpool_limits = None
+    inp = si.make_varlen_inputs(wl)
+    q, k, v, _ = inp.as_f64()
+    lens = np.diff(inp.cu_q)
+    order = np.argsort(lens)
+    threads = oracle.default_threads()
+    done, flops = 0, 0.0
+    ctx = threadpool_limits(limits=1) if threadpool_limits else None
+    if ctx:
+        ctx.__enter__()
+    t0 = time.perf_counter()
+    try:
+        for s in order:
+            a, b = int(inp.cu_q[s]), int(inp.cu_q[s + 1])
+            oracle.sdpa_forward_varlen(q[a:b], k[a:b], v[a:b], [0, b - a], [0, b - a],
+                                       scale=wl.scale, mask_kind=wl.mask_kind, window=wl.window,
+                                       threads=threads)
+            done += 1
+            flops += 4.0 * wl.D * wl.Hq * si.visible_pairs(b - a, b - a, wl.mask_kind,
+                                                            wl.window)
+            if time.perf_counter() - t0 >= budget_s:
+                break
+    finally:
+        if ctx:
+            ctx.__exit__(None, None, None)
+    secs = time.perf_counter() - t0
+    return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} of {len(lens)} sequences of {wl.name} (shortest first, all heads "
+                      f"and rows), fp64 numpy, one head per thread (BLAS on one thread each), "
+                      f"{secs:.1f} s"}
+
+
+def main_varlen(sdpa, wl, args) -> int:
+    t = time_varlen(sdpa, wl, args.steps, args.warmup)
+    flops = 4.0 * wl.D * wl.Hq * si.varlen_visible_pairs(wl)
+    value = flops / (t["ms_per_step"] * 1e-3) / 1e12
+    achieved = flops / (t["kernel_ms_avg"] * 1e-3) / 1e12
+    line = {
+        "metric": "attention fwd over packed sequences, effective TFLOP/s (visible pairs of "
+                  "every sequence) + % of bf16 MFMA peak",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(t["ms_per_step"], 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic", "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "config": {**wl.describe(), "effective_gflop": round(flops / 1e9, 2),
+                   "call_ms_median": round(t["kernel_ms_median"], 4)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_varlen(wl)
+    print(json.dumps(line), flush=True)
     return 0
 
 
