@@ -7,9 +7,9 @@ tests/test_oracle.py pin it to brute force, a library special case, closed forms
 hand-derived golden values.
 """
 from .sdpa_ref import (  # noqa: F401
-    MASK_NONE, MASK_CAUSAL, MASK_SLIDING, BIAS_NONE, BIAS_T5, BIAS_FULL,
+    MASK_NONE, MASK_CAUSAL, MASK_SLIDING, BIAS_NONE, BIAS_T5, BIAS_FULL, BIAS_ALIBI, BIAS_T5U,
     T5_NUM_BUCKETS, T5_MAX_DISTANCE,
-    t5_bucket, visible, attend_rows, attention_weights, sdpa_rows, sdpa_forward,
+    t5_bucket, t5u_bucket, visible, attend_rows, attention_weights, sdpa_rows, sdpa_forward,
     default_threads,
 )
 from .sdpa_bwd_ref import head_backward, sdpa_backward  # noqa: F401

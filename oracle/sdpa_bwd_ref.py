@@ -33,7 +33,8 @@ from typing import Optional, Sequence
 
 import numpy as np
 
-from .sdpa_ref import BIAS_FULL, BIAS_NONE, BIAS_T5, t5_bucket, visible
+from .sdpa_ref import (BIAS_ALIBI, BIAS_FULL, BIAS_NONE, BIAS_T5, BIAS_T5U, t5_bucket,
+                       t5u_bucket, visible)
 
 
 def _bias(bias_kind, bias, b, h, q_pos, Sk):
@@ -44,6 +45,11 @@ def _bias(bias_kind, bias, b, h, q_pos, Sk):
         return bias[h][t5_bucket(rel)]
     if bias_kind == BIAS_FULL:
         return bias[b, h]
+    rel = np.arange(Sk, dtype=np.int64)[None, :] - np.asarray(q_pos, np.int64)[:, None]
+    if bias_kind == BIAS_ALIBI:
+        return -float(bias[h]) * np.abs(rel).astype(np.float64)
+    if bias_kind == BIAS_T5U:
+        return bias[h][t5u_bucket(rel)]
     raise ValueError(f"unknown bias kind {bias_kind}")
 
 

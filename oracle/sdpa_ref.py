@@ -32,6 +32,13 @@ Readings where the pages are silent (each also listed in the design notes):
   R5 T5 table layout: fp32 [Hq][32], row h holds the 32 bucket values of head h.
   R8 a query row with no visible key gives O = 0 and LSE = -inf.
   R9 LSE = natural log of sum_j exp(s'_ij) where s' includes scale and bias.
+  R19 ALiBi (named in the FAT5 README's list of attention biases, not defined there): the
+     score of (query position p, key j) in head h gets -slope[h] * |p - j|, slopes an fp32
+     [Hq] table given by the caller (for causal rows this is the ALiBi paper's
+     slope * (j - p)).
+  R20 T5 unidirectional (decoder) buckets: keys at or after the query share bucket 0; a key
+     n = p - j positions back gets bucket n for n < 16, else 16 + floor(16 log(n/16) / log 8)
+     capped at 31 (the T5 formula with bidirectional=False, 32 buckets, max distance 128).
 """
 from __future__ import annotations
 
@@ -43,7 +50,7 @@ from typing import Optional, Sequence
 import numpy as np
 
 MASK_NONE, MASK_CAUSAL, MASK_SLIDING = 0, 1, 2
-BIAS_NONE, BIAS_T5, BIAS_FULL = 0, 1, 2
+BIAS_NONE, BIAS_T5, BIAS_FULL, BIAS_ALIBI, BIAS_T5U = 0, 1, 2, 3, 4
 
 T5_NUM_BUCKETS = 32
 T5_MAX_DISTANCE = 128
@@ -73,6 +80,17 @@ def t5_bucket(rel) -> np.ndarray:
     large = np.minimum(large, half - 1)
     bucket = np.where(n < max_exact, n, large)
     return bucket + np.where(rel > 0, half, 0)
+
+
+def t5u_bucket(rel) -> np.ndarray:
+    """T5 unidirectional bucket of rel = key_position - query_position (R20), the T5
+    real-valued formula in fp64: n = max(-rel, 0); n below 16 exact; otherwise
+    16 + floor(16 * log(n / 16) / log(128 / 16)), capped at 31."""
+    rel = np.asarray(rel, dtype=np.int64)
+    n = np.maximum(-rel, 0)
+    nf = np.maximum(n, 1).astype(np.float64)
+    large = 16 + np.floor(np.log(nf / 16.0) / math.log(128.0 / 16.0) * 16.0).astype(np.int64)
+    return np.where(n < 16, n, np.minimum(large, 31))
 
 
 def visible(q_pos: np.ndarray, Sk: int, mask_kind: int, window: int) -> np.ndarray:
@@ -140,6 +158,11 @@ def _bias_rows(bias_kind, bias, b, h, q_pos, rows, Sk):
         return bias[h][t5_bucket(rel)]          # table [Hq][32]
     if bias_kind == BIAS_FULL:
         return bias[b, h][np.asarray(rows)]     # [B, Hq, Sq, Sk]
+    rel = np.arange(Sk, dtype=np.int64)[None, :] - np.asarray(q_pos, np.int64)[:, None]
+    if bias_kind == BIAS_ALIBI:
+        return -float(bias[h]) * np.abs(rel).astype(np.float64)     # slopes [Hq] (R19)
+    if bias_kind == BIAS_T5U:
+        return bias[h][t5u_bucket(rel)]                              # table [Hq][32] (R20)
     raise ValueError(f"unknown bias kind {bias_kind}")
 
 

@@ -102,3 +102,40 @@ def test_causal_last_row_equals_unmasked_last_row(gpu_lib):
     a, c = out_to_f64(oc), out_to_f64(on)
     assert np.max(np.abs(a[:, -1] - c[:, -1])) <= 1e-5
     assert np.max(np.abs(a[:, 0] - c[:, 0])) > 1e-2
+
+
+_FRESH = r"""
+import hashlib, sys
+sys.path.insert(0, {root!r}); sys.path.insert(0, {tests!r})
+import torch
+import sdpa_inputs as si
+import scaled_dot_product_03_amd as sdpa
+from helpers import run_gpu, to_device
+wl = si.small(si.WORKLOADS["c2"], B=1, Hq=8, Hkv=2, Sq=1000, Sk=1000, window=1000,
+              name_suffix="fresh")
+o, l = run_gpu(sdpa, wl, to_device(si.make_inputs(wl)))
+h = hashlib.sha256(o.view(torch.int16).cpu().numpy().tobytes() +
+                   l.cpu().numpy().tobytes()).hexdigest()
+print("HASH", h)
+"""
+
+
+def test_bitwise_same_in_a_fresh_process(gpu_lib):
+    """The determinism issue compares runs of a training step; besides repeats within one
+    process, a second process must produce the same bits (same shape, same launch)."""
+    import hashlib
+    import os
+    import subprocess
+    import sys
+    import torch
+    wl = si.small(W["c2"], B=1, Hq=8, Hkv=2, Sq=1000, Sk=1000, window=1000, name_suffix="fresh")
+    o, l = run_gpu(gpu_lib, wl, to_device(si.make_inputs(wl)))
+    here = hashlib.sha256(o.view(torch.int16).cpu().numpy().tobytes() +
+                          l.cpu().numpy().tobytes()).hexdigest()
+    tests = os.path.dirname(os.path.abspath(__file__))
+    code = _FRESH.format(root=os.path.dirname(tests), tests=tests)
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=180)
+    assert r.returncode == 0, r.stderr[-2000:]
+    there = [x.split()[1] for x in r.stdout.splitlines() if x.startswith("HASH ")][0]
+    print(f"in-process {here[:16]} fresh process {there[:16]}")
+    assert here == there
