@@ -104,7 +104,7 @@ def to_device(inp: si.Inputs):
             return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
         return torch.from_numpy(np.ascontiguousarray(a)).cuda()
     bias = None
-    if inp.wl.bias_kind == si.BIAS_T5:
+    if inp.wl.bias_kind in (si.BIAS_T5, si.BIAS_T5U, si.BIAS_ALIBI):
         bias = torch.from_numpy(inp.t5_table).cuda()
     elif inp.wl.bias_kind == si.BIAS_FULL:
         bias = dev(inp.bias)
@@ -477,7 +477,8 @@ def main(argv=None):
 
     if args.sweep:
         ms = {}
-        for key in ["c2", "c2c", "c3", "c3c", "c4t5", "c4full", "c5mha", "c5gqa", "c5mqa"]:
+        for key in ["c2", "c2c", "c3", "c3c", "c4t5", "c4full", "c5mha", "c5gqa", "c5mqa",
+                    "c2alibi", "c4t5u"]:
             w2 = si.WORKLOADS[key]
             # at least 30 warmup launches: clocks ramp up over ~15 launches after the GPU idles
             t2 = time_workload(sdpa, w2, max(5, args.steps // 2), max(30, args.warmup))
@@ -681,7 +682,8 @@ def main_bwd(sdpa, wl: si.Workload, args) -> int:
         line["cpu_baseline"] = cpu_baseline_bwd(wl)
     print(json.dumps(line), flush=True)
     if args.sweep:
-        for key in ["c2", "c3", "c3c", "c4t5", "c4full", "c5mha", "c5gqa", "c5mqa"]:
+        for key in ["c2", "c3", "c3c", "c4t5", "c4full", "c5mha", "c5gqa", "c5mqa", "c2alibi",
+                    "c4t5u"]:
             w2 = si.WORKLOADS[key]
             t2 = time_workload(sdpa, w2, max(5, args.steps // 2), max(30, args.warmup), bwd=True)
             f2, a2 = report(w2, t2, bwd=True)

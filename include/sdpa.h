@@ -34,6 +34,12 @@
  *                   saturating at the last bucket of the half.
  *   SDPA_BIAS_FULL  bias_tbl = [B][Hq][Sq][Sk] in the input dtype (bf16 for sdpa_fwd and
  *                   sdpa_fwd_bf16_f32out, fp32 for sdpa_fwd_f32).
+ *   SDPA_BIAS_ALIBI bias_tbl = fp32 slopes [Hq]; the score of (query position p, key j) in head
+ *                   h gets -slope[h] * |p - j| (ALiBi, named in the FAT5 README's bias list;
+ *                   under a causal mask this is slope * (j - p)).
+ *   SDPA_BIAS_T5U   bias_tbl = fp32 table [Hq][32] with T5 unidirectional (decoder) buckets:
+ *                   keys at or after the query use bucket 0, a key n positions back bucket n
+ *                   below 16, then log-spaced to 31 (reached at n = 113).
  *
  * Conventions for every entry point:
  *   - All pointers are DEVICE pointers owned by the caller. The library allocates nothing,
@@ -63,7 +69,9 @@ extern "C" {
 #define SDPA_ABI_VERSION 2
 
 enum sdpa_mask_kind { SDPA_MASK_NONE = 0, SDPA_MASK_CAUSAL = 1, SDPA_MASK_SLIDING = 2 };
-enum sdpa_bias_kind { SDPA_BIAS_NONE = 0, SDPA_BIAS_T5 = 1, SDPA_BIAS_FULL = 2 };
+enum sdpa_bias_kind {
+    SDPA_BIAS_NONE = 0, SDPA_BIAS_T5 = 1, SDPA_BIAS_FULL = 2, SDPA_BIAS_ALIBI = 3, SDPA_BIAS_T5U = 4
+};
 
 enum sdpa_status {
     SDPA_OK = 0,

@@ -24,9 +24,10 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_NAME = "libsdpa_mi355x.so"
 
 MASK_NONE, MASK_CAUSAL, MASK_SLIDING = 0, 1, 2
-BIAS_NONE, BIAS_T5, BIAS_FULL = 0, 1, 2
+BIAS_NONE, BIAS_T5, BIAS_FULL, BIAS_ALIBI, BIAS_T5U = 0, 1, 2, 3, 4
 _MASKS = {"none": MASK_NONE, "causal": MASK_CAUSAL, "sliding": MASK_SLIDING}
-_BIASES = {"none": BIAS_NONE, "t5": BIAS_T5, "full": BIAS_FULL}
+_BIASES = {"none": BIAS_NONE, "t5": BIAS_T5, "full": BIAS_FULL, "alibi": BIAS_ALIBI,
+           "t5u": BIAS_T5U}
 
 SDPA_OK = 0
 STATUS_NAMES = {0: "SDPA_OK", 1: "SDPA_ERR_NULL", 2: "SDPA_ERR_SHAPE", 3: "SDPA_ERR_HEADS",
@@ -166,10 +167,15 @@ def _check_qkv(q, k, v):
 def _bias_ptr(bk, bias, dtype, B, Hq, Sq, Sk):
     import torch
 
-    if bk == BIAS_T5:
+    if bk in (BIAS_T5, BIAS_T5U):
         if bias is None or bias.dtype != torch.float32 or tuple(bias.shape) != (Hq, 32) \
                 or not bias.is_contiguous() or not bias.is_cuda:
             raise ValueError("t5 bias must be a contiguous cuda fp32 [Hq, 32] table")
+        return bias.data_ptr()
+    if bk == BIAS_ALIBI:
+        if bias is None or bias.dtype != torch.float32 or tuple(bias.shape) != (Hq,) \
+                or not bias.is_contiguous() or not bias.is_cuda:
+            raise ValueError("alibi bias must be a contiguous cuda fp32 [Hq] slope table")
         return bias.data_ptr()
     if bk == BIAS_FULL:
         if bias is None or bias.dtype != dtype or tuple(bias.shape) != (B, Hq, Sq, Sk) \
@@ -188,8 +194,9 @@ def fwd(q, k, v, *, scale: Optional[float] = None, mask="causal", window: int = 
 
     q [B,Sq,Hq,D], k/v [B,Sk,Hkv,D]: contiguous cuda tensors, all bf16 or all fp32.
     mask: "none" | "causal" | "sliding" (window keys, including the query's own position).
-    bias_kind: "none" | "t5" (bias = fp32 table [Hq, 32]) | "full" (bias [B, Hq, Sq, Sk] in
-    the input dtype). out_dtype: torch.float32 with bf16 inputs selects the fp32 epilogue.
+    bias_kind: "none" | "t5" / "t5u" (bias = fp32 table [Hq, 32], bidirectional or decoder
+    buckets) | "alibi" (bias = fp32 slopes [Hq]) | "full" (bias [B, Hq, Sq, Sk] in the input
+    dtype). out_dtype: torch.float32 with bf16 inputs selects the fp32 epilogue.
     """
     import torch
 
@@ -343,11 +350,9 @@ def fwd_varlen(q, k, v, cu_q, cu_k, max_seqlen_q: int, max_seqlen_k: int, *,
         scale = 1.0 / math.sqrt(D)
     odt = out_dtype or torch.bfloat16
     entry = "sdpa_fwd_varlen" if odt == torch.bfloat16 else "sdpa_fwd_varlen_f32out"
-    bias_ptr = None
-    if bk == BIAS_T5:
-        bias_ptr = _bias_ptr(bk, bias, q.dtype, 1, Hq, 1, 1)
-    elif bias is not None or bk != BIAS_NONE:
-        raise ValueError("packed sequences take no bias or a T5 table")
+    if bk == BIAS_FULL:
+        raise ValueError("packed sequences take no full bias")
+    bias_ptr = _bias_ptr(bk, bias, q.dtype, 1, Hq, 1, 1)
     if out is None:
         out = torch.empty((total_q, Hq, D), dtype=odt, device=q.device)
     if lse is None:

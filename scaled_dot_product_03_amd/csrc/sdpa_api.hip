@@ -33,8 +33,7 @@ int validate(const void* q, const void* k, const void* v, const void* out, const
         mask_kind != SDPA_MASK_SLIDING)
         return SDPA_ERR_MASK;
     if (mask_kind == SDPA_MASK_SLIDING && window < 1) return SDPA_ERR_WINDOW;
-    if (bias_kind != SDPA_BIAS_NONE && bias_kind != SDPA_BIAS_T5 && bias_kind != SDPA_BIAS_FULL)
-        return SDPA_ERR_BIAS;
+    if (bias_kind < SDPA_BIAS_NONE || bias_kind > SDPA_BIAS_T5U) return SDPA_ERR_BIAS;
     if ((bias_kind == SDPA_BIAS_NONE) != (bias_tbl == nullptr)) return SDPA_ERR_BIAS;
     if (!isfinite(scale)) return SDPA_ERR_SCALE;
     const long long qe = (long long)B * Sq * Hq * D;
@@ -50,7 +49,9 @@ int validate(const void* q, const void* k, const void* v, const void* out, const
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
         !aligned(lse, 4))
         return SDPA_ERR_ALIGN;
-    if (bias_kind == SDPA_BIAS_T5 && !aligned(bias_tbl, 4)) return SDPA_ERR_ALIGN;
+    if ((bias_kind == SDPA_BIAS_T5 || bias_kind == SDPA_BIAS_T5U || bias_kind == SDPA_BIAS_ALIBI) &&
+        !aligned(bias_tbl, 4))
+        return SDPA_ERR_ALIGN;
     if (bias_kind == SDPA_BIAS_FULL && !aligned(bias_tbl, 16)) return SDPA_ERR_ALIGN;
     return SDPA_OK;
 }

@@ -46,11 +46,14 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(const BwdParams p) {
     constexpr int kWaves = 8, kThreads = 512, kBM = 256, kBN = 64;
     constexpr int CH = D / 8, KS = D / 16, DB = D / 32, TILE = kBN * D;
     constexpr bool FB = BIAS == BIAS_FULL;
-    constexpr int kT5Pad = kT5Sat + kBN + 31;
+    constexpr bool IS_T5 = BIAS == BIAS_T5 || BIAS == BIAS_T5U;
+    constexpr bool ALIBI = BIAS == BIAS_ALIBI;
+    constexpr int kSat = BIAS == BIAS_T5U ? kT5USat : kT5Sat;
+    constexpr int kT5Pad = kSat + kBN + 31;
     constexpr int BTILE = kBM * kBN;                 // full-bias tile: 256 rows x 64 keys
     // K slots 0-1, V slots 2-3, then (full bias) two bias slots
     __shared__ __attribute__((aligned(16))) uint16_t smem[4 * TILE + (FB ? 2 * BTILE : 0)];
-    __shared__ float t5s[BIAS == BIAS_T5 ? 2 * kT5Pad + 1 : 1];
+    __shared__ float t5s[IS_T5 ? 2 * kT5Pad + 1 : 1];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int hh = lane >> 5, r32 = lane & 31;
@@ -108,10 +111,12 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(const BwdParams p) {
         if (row_ok) store_zero_row<D, OUT_F32>(dq_row, hh);
         return;
     }
-    if constexpr (BIAS == BIAS_T5) {
+    if constexpr (IS_T5) {
         const float* tbl = (const float*)p.bias + (size_t)hq * kT5Buckets;
-        for (int i = tid; i < 2 * kT5Pad + 1; i += kThreads) t5s[i] = tbl[t5_bucket(i - kT5Pad)] * kLog2e;
+        for (int i = tid; i < 2 * kT5Pad + 1; i += kThreads)
+            t5s[i] = tbl[BIAS == BIAS_T5U ? t5u_bucket(i - kT5Pad) : t5_bucket(i - kT5Pad)] * kLog2e;
     }
+    const float aslope = ALIBI ? ((const float*)p.bias)[hq] * kLog2e : 0.f;   // ALiBi, log2 units
 
     // A negative scale flips the sign of the Q fragment (S is unchanged); dQ = scale * dS K
     // uses the signed scale. A zero scale computes P with the smallest normal float.
@@ -199,9 +204,9 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(const BwdParams p) {
         // bias of the tile: constant for T5 far from the diagonal
         bool per_elem = FB;
         float bconst = 0.f;
-        if constexpr (BIAS == BIAS_T5) {
+        if constexpr (IS_T5) {
             const int rmin = j0 - pwb, rmax = j0 + kBN - 1 - pwa;
-            const int side = uniform(rmin >= kT5Sat ? 1 : (rmax <= -kT5Sat ? -1 : 0));
+            const int side = uniform(rmin >= kSat ? 1 : (rmax <= -kSat ? -1 : 0));
             if (side > 0) bconst = t5s[2 * kT5Pad];
             else if (side < 0) bconst = t5s[0];
             else per_elem = true;
@@ -221,7 +226,11 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(const BwdParams p) {
             }
             // x = scores in log2 units including the bias
             float x[16];
-            if constexpr (BIAS == BIAS_T5) {
+            if constexpr (ALIBI) {
+                const float base = (float)(jl - my_pos);
+#pragma unroll
+                for (int v = 0; v < 16; ++v) x[v] = fmaf(s[v], c_scale, -aslope * fabsf(base + (float)v));
+            } else if constexpr (IS_T5) {
                 if (per_elem) {
                     const float* trow = t5s + kT5Pad + (jl - min(my_pos, pwb));
 #pragma unroll
@@ -316,12 +325,15 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(const BwdParams p) {
     constexpr int kWaves = 8, kThreads = 512, kBK = 128, kBQ = (FB && D == 128) ? 64 : 128;
     constexpr int NB = kBQ / 32;
     constexpr int CH = D / 8, KS = D / 16, DB = D / 32, QT = kBQ * D, BTILE = kBQ * kBK;
-    constexpr int kT5Pad = kT5Sat + 64 + 31;
+    constexpr bool IS_T5 = BIAS == BIAS_T5 || BIAS == BIAS_T5U;
+    constexpr bool ALIBI = BIAS == BIAS_ALIBI;
+    constexpr int kSat = BIAS == BIAS_T5U ? kT5USat : kT5Sat;
+    constexpr int kT5Pad = kSat + 64 + 31;
     // LDS: slot sl holds the Q tile at [2 sl] and the dO tile at [2 sl + 1] (kBQ rows each),
     // then (full bias) two bias slots of kBQ rows x 128 keys
     __shared__ __attribute__((aligned(16))) uint16_t smem[4 * QT + (FB ? 2 * BTILE : 0)];
     __shared__ __attribute__((aligned(16))) float rowc[2][2][kBQ];    // [slot][lse2, D][row]
-    __shared__ float t5s[BIAS == BIAS_T5 ? 2 * kT5Pad + 1 : 1];
+    __shared__ float t5s[IS_T5 ? 2 * kT5Pad + 1 : 1];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int hh = lane >> 5, r32 = lane & 31;
@@ -509,9 +521,15 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(const BwdParams p) {
             const int rl = 32 * QB + 16 * hh;                      // row of register 0 in the tile
             const int pos0 = r0 + 16 * hh + off;                   // its position
             float x[16];
-            if constexpr (BIAS == BIAS_T5) {
+            if constexpr (ALIBI) {
+                // rel = my_j - position of row v
+                const float aslope = ((const float*)p.bias)[h] * kLog2e;
+                const float base = (float)(my_j - pos0);
+#pragma unroll
+                for (int v = 0; v < 16; ++v) x[v] = fmaf(s[v], c_scale, -aslope * fabsf(base - (float)v));
+            } else if constexpr (IS_T5) {
                 const int rmin = kw0 - pb, rmax = kwe - pa;
-                const int side = uniform(rmin >= kT5Sat ? 1 : (rmax <= -kT5Sat ? -1 : 0));
+                const int side = uniform(rmin >= kSat ? 1 : (rmax <= -kSat ? -1 : 0));
                 if (side == 0) {
                     // rel = my_j - position of row v; stays inside the padded table
                     const float* trow = t5s + kT5Pad + (my_j - pos0);
@@ -592,14 +610,14 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(const BwdParams p) {
 
         auto step = [&](int n, auto sl_tag) {
             constexpr int SL = decltype(sl_tag)::value;
-            if constexpr (BIAS == BIAS_T5) {
+            if constexpr (IS_T5) {
                 // table of head h when the head changes (no reader of the previous table is
                 // still running: the barrier ending the previous step, and one after the writes)
                 const int h = kvh * G + n / nqs;
                 if (n == 0 || h != kvh * G + (n - 1) / nqs) {
                     const float* tbl = (const float*)p.bias + (size_t)h * kT5Buckets;
                     for (int i = tid; i < 2 * kT5Pad + 1; i += kThreads)
-                        t5s[i] = tbl[t5_bucket(i - kT5Pad)] * kLog2e;
+                        t5s[i] = tbl[BIAS == BIAS_T5U ? t5u_bucket(i - kT5Pad) : t5_bucket(i - kT5Pad)] * kLog2e;
                     __syncthreads();
                 }
             }
@@ -651,6 +669,8 @@ static hipError_t launch_d(const BwdParams& p, int mask, int bias, hipStream_t s
     SDPA_CASE(MASK_NONE, BIAS_NONE) SDPA_CASE(MASK_NONE, BIAS_T5) SDPA_CASE(MASK_NONE, BIAS_FULL)
     SDPA_CASE(MASK_CAUSAL, BIAS_NONE) SDPA_CASE(MASK_CAUSAL, BIAS_T5) SDPA_CASE(MASK_CAUSAL, BIAS_FULL)
     SDPA_CASE(MASK_SLIDING, BIAS_NONE) SDPA_CASE(MASK_SLIDING, BIAS_T5) SDPA_CASE(MASK_SLIDING, BIAS_FULL)
+    SDPA_CASE(MASK_NONE, BIAS_ALIBI) SDPA_CASE(MASK_CAUSAL, BIAS_ALIBI) SDPA_CASE(MASK_SLIDING, BIAS_ALIBI)
+    SDPA_CASE(MASK_NONE, BIAS_T5U) SDPA_CASE(MASK_CAUSAL, BIAS_T5U) SDPA_CASE(MASK_SLIDING, BIAS_T5U)
 #undef SDPA_CASE
     return hipErrorInvalidValue;
 }

@@ -72,7 +72,8 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void split_kernel(const DecP
     constexpr bool FB = BIAS == BIAS_FULL;
     // slot u of the ring: K tile at [2u], V tile at [2u + 1]; reused for the wave merge
     __shared__ __attribute__((aligned(16))) uint16_t smem[kNS * 2 * TILE];
-    __shared__ float t5s[BIAS == BIAS_T5 ? 32 * kT5Buckets : 1];   // [row of block][bucket]
+    constexpr bool IS_T5 = BIAS == BIAS_T5 || BIAS == BIAS_T5U;
+    __shared__ float t5s[IS_T5 ? 32 * kT5Buckets : 1];   // [row of block][bucket]
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int hh = lane >> 5, r32 = lane & 31;
@@ -107,7 +108,7 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void split_kernel(const DecP
     float* ws_o = p.ws + unit * 32 * D;
     float* ws_ml = p.ws + units * 32 * D + unit * 64;
 
-    if constexpr (BIAS == BIAS_T5) {
+    if constexpr (IS_T5) {
         for (int idx = tid; idx < 32 * kT5Buckets; idx += kThreads) {
             const int row = idx / kT5Buckets, bk = idx - row * kT5Buckets;
             const int rw = min(32 * rb + row, p.rows - 1);
@@ -116,6 +117,8 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void split_kernel(const DecP
         }
     }
 
+    // ALiBi slope of this lane's head, log2 units
+    const float aslope = BIAS == BIAS_ALIBI ? ((const float*)p.bias)[my_hq] * kLog2e : 0.f;
     const bool neg = p.scale_log2 < 0.f;
     const float c_scale = neg ? -p.scale_log2 : (p.scale_log2 == 0.f ? kTinyScale : p.scale_log2);
     bf16x8 qf[KS];
@@ -182,6 +185,8 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void split_kernel(const DecP
         for (int v = 0; v < 16; ++v) {
             float t = s[v] * c_scale;
             if constexpr (BIAS == BIAS_T5) t += t5s[r32 * kT5Buckets + t5_bucket(jl + v - my_pos)];
+            if constexpr (BIAS == BIAS_T5U) t += t5s[r32 * kT5Buckets + t5u_bucket(jl + v - my_pos)];
+            if constexpr (BIAS == BIAS_ALIBI) t -= aslope * fabsf((float)(jl + v - my_pos));
             if constexpr (FB) {
                 const int j = jl + v;
                 t = fmaf((row_ok && j < Sk) ? bf16_to_f32(fbrow[j]) : 0.f, kLog2e, t);
@@ -376,6 +381,8 @@ static hipError_t launch_d(const DecParams& p, int mask, int bias, hipStream_t s
     SDPA_CASE(MASK_NONE, BIAS_NONE) SDPA_CASE(MASK_NONE, BIAS_T5) SDPA_CASE(MASK_NONE, BIAS_FULL)
     SDPA_CASE(MASK_CAUSAL, BIAS_NONE) SDPA_CASE(MASK_CAUSAL, BIAS_T5) SDPA_CASE(MASK_CAUSAL, BIAS_FULL)
     SDPA_CASE(MASK_SLIDING, BIAS_NONE) SDPA_CASE(MASK_SLIDING, BIAS_T5) SDPA_CASE(MASK_SLIDING, BIAS_FULL)
+    SDPA_CASE(MASK_NONE, BIAS_ALIBI) SDPA_CASE(MASK_CAUSAL, BIAS_ALIBI) SDPA_CASE(MASK_SLIDING, BIAS_ALIBI)
+    SDPA_CASE(MASK_NONE, BIAS_T5U) SDPA_CASE(MASK_CAUSAL, BIAS_T5U) SDPA_CASE(MASK_SLIDING, BIAS_T5U)
 #undef SDPA_CASE
     return hipErrorInvalidValue;
 }

@@ -127,11 +127,15 @@ __global__ __launch_bounds__(kThreads, 1) void sdpa_fwd_bf16_kernel(const FwdPar
     constexpr int VRING = NKS * KSTAGE;
     static_assert((NKS * KSTAGE + NVS * TILE) * 2 <= 160 * 1024, "LDS");
     __shared__ __attribute__((aligned(16))) uint16_t smem[NKS * KSTAGE + NVS * TILE];
-    // T5 bias by relative position rel = key - query, log2 units, at t5s[kT5Pad + rel]. Padded
-    // so that every rel of a tile near the diagonal indexes it without clamping: such a tile has
-    // j0 - pwb < kT5Sat and j0 + 63 - pwa > -kT5Sat, and pwb - pwa <= 31, so |rel| < kT5Pad.
-    constexpr int kT5Pad = kT5Sat + kBN + 31;
-    __shared__ float t5s[BIAS == BIAS_T5 ? 2 * kT5Pad + 1 : 1];
+    // T5 bias (bidirectional or decoder buckets) by relative position rel = key - query, log2
+    // units, at t5s[kT5Pad + rel]. Padded so that every rel of a tile near the diagonal indexes
+    // it without clamping: such a tile has j0 - pwb < kSat and j0 + 63 - pwa > -kSat, and
+    // pwb - pwa <= 31, so |rel| < kT5Pad. Beyond +-kSat the bucket is constant.
+    constexpr bool IS_T5 = BIAS == BIAS_T5 || BIAS == BIAS_T5U;
+    constexpr bool ALIBI = BIAS == BIAS_ALIBI;
+    constexpr int kSat = BIAS == BIAS_T5U ? kT5USat : kT5Sat;
+    constexpr int kT5Pad = kSat + kBN + 31;
+    __shared__ float t5s[IS_T5 ? 2 * kT5Pad + 1 : 1];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -205,10 +209,14 @@ __global__ __launch_bounds__(kThreads, 1) void sdpa_fwd_bf16_kernel(const FwdPar
     }
 
     // ---- T5: expanded bias by relative position, already in log2 units --------------------
-    if constexpr (BIAS == BIAS_T5) {
+    if constexpr (IS_T5) {
         const float* tbl = (const float*)p.bias + (size_t)hq * kT5Buckets;
-        for (int i = tid; i < 2 * kT5Pad + 1; i += kThreads) t5s[i] = tbl[t5_bucket(i - kT5Pad)] * kLog2e;
+        for (int i = tid; i < 2 * kT5Pad + 1; i += kThreads)
+            t5s[i] = tbl[BIAS == BIAS_T5U ? t5u_bucket(i - kT5Pad) : t5_bucket(i - kT5Pad)] * kLog2e;
     }
+    // ALiBi: -slope * |p - j| in log2 units, slope of this head from the [Hq] table
+    float aslope = 0.f;
+    if constexpr (ALIBI) aslope = ((const float*)p.bias)[hq] * kLog2e;
 
     // ---- Q fragment: lane holds row my_i, dims 16ks + 8hh .. +7 ----------------------------
     bf16x8 qf[KS];
@@ -486,15 +494,15 @@ __global__ __launch_bounds__(kThreads, 1) void sdpa_fwd_bf16_kernel(const FwdPar
         // Per-element path: full bias, or T5 near the diagonal. Otherwise the bias is constant
         // over the tile (none, or T5 far from the diagonal) and the scale is folded into the
         // exponent's FMA after a max over the raw scores.
-        bool per_elem = FB;
+        bool per_elem = FB || ALIBI;
         float bconst = 0.f;
         bool msk = false;
         if constexpr (DO_PREP) {
             msk = needs_mask(tn);
-            if constexpr (BIAS == BIAS_T5) {
+            if constexpr (IS_T5) {
                 const int rmin = j0 - pwb, rmax = j0 + kBN - 1 - pwa;
-                if (rmin >= kT5Sat) bconst = t5s[2 * kT5Pad];
-                else if (rmax <= -kT5Sat) bconst = t5s[0];
+                if (rmin >= kSat) bconst = t5s[2 * kT5Pad];
+                else if (rmax <= -kSat) bconst = t5s[0];
                 else per_elem = true;
             }
         }
@@ -537,7 +545,14 @@ __global__ __launch_bounds__(kThreads, 1) void sdpa_fwd_bf16_kernel(const FwdPar
                     }
                 } else if (g == 1) {
                     if (per_elem) {
-                        if constexpr (BIAS == BIAS_T5) {
+                        if constexpr (ALIBI) {
+                            // register e holds key jl + 32 (e >> 4) + (e & 15)
+                            const float base = (float)(jl - my_pos);
+#pragma unroll
+                            for (int e = 0; e < 32; ++e)
+                                ns[e >> 4][e & 15] = fmaf(ns[e >> 4][e & 15], c_scale,
+                                    -aslope * fabsf(base + (float)((e >> 4) * 32 + (e & 15))));
+                        } else if constexpr (IS_T5) {
                             // register e holds key jl + 32 (e >> 4) + (e & 15): one base per
                             // lane, compile-time offsets (rows past the end of the queries use
                             // the wave's last row, so the index stays in the table)
@@ -726,6 +741,8 @@ static hipError_t launch_d(const FwdParams& p, int mask, int bias, hipStream_t s
     SDPA_CASE(MASK_NONE, BIAS_NONE) SDPA_CASE(MASK_NONE, BIAS_T5) SDPA_CASE(MASK_NONE, BIAS_FULL)
     SDPA_CASE(MASK_CAUSAL, BIAS_NONE) SDPA_CASE(MASK_CAUSAL, BIAS_T5) SDPA_CASE(MASK_CAUSAL, BIAS_FULL)
     SDPA_CASE(MASK_SLIDING, BIAS_NONE) SDPA_CASE(MASK_SLIDING, BIAS_T5) SDPA_CASE(MASK_SLIDING, BIAS_FULL)
+    SDPA_CASE(MASK_NONE, BIAS_ALIBI) SDPA_CASE(MASK_CAUSAL, BIAS_ALIBI) SDPA_CASE(MASK_SLIDING, BIAS_ALIBI)
+    SDPA_CASE(MASK_NONE, BIAS_T5U) SDPA_CASE(MASK_CAUSAL, BIAS_T5U) SDPA_CASE(MASK_SLIDING, BIAS_T5U)
 #undef SDPA_CASE
     return hipErrorInvalidValue;
 }
@@ -738,6 +755,8 @@ static hipError_t launch_varlen_d(const FwdParams& p, int mask, int bias, hipStr
     SDPA_CASE(MASK_NONE, BIAS_NONE) SDPA_CASE(MASK_NONE, BIAS_T5)
     SDPA_CASE(MASK_CAUSAL, BIAS_NONE) SDPA_CASE(MASK_CAUSAL, BIAS_T5)
     SDPA_CASE(MASK_SLIDING, BIAS_NONE) SDPA_CASE(MASK_SLIDING, BIAS_T5)
+    SDPA_CASE(MASK_NONE, BIAS_ALIBI) SDPA_CASE(MASK_CAUSAL, BIAS_ALIBI) SDPA_CASE(MASK_SLIDING, BIAS_ALIBI)
+    SDPA_CASE(MASK_NONE, BIAS_T5U) SDPA_CASE(MASK_CAUSAL, BIAS_T5U) SDPA_CASE(MASK_SLIDING, BIAS_T5U)
 #undef SDPA_CASE
     return hipErrorInvalidValue;
 }

@@ -41,9 +41,10 @@ __global__ __launch_bounds__(kRowsF32) void sdpa_fwd_f32_kernel(const FwdParams 
         const int r = e / D, d = e % D;
         qs[r][d] = (q0 + r < Sq) ? qg[(size_t)(q0 + r) * q_row + d] : 0.f;
     }
-    if constexpr (BIAS == BIAS_T5) {
+    if constexpr (BIAS == BIAS_T5 || BIAS == BIAS_T5U) {
         if (tid < kT5Buckets) tbl[tid] = ((const float*)p.bias)[(size_t)hq * kT5Buckets + tid];
     }
+    const float slope = BIAS == BIAS_ALIBI ? ((const float*)p.bias)[hq] : 0.f;
 
     // key range of the 64-row block
     const int pa = q0 + p.off, pb = min(q0 + kRowsF32, Sq) - 1 + p.off;
@@ -79,6 +80,8 @@ __global__ __launch_bounds__(kRowsF32) void sdpa_fwd_f32_kernel(const FwdParams 
             for (int d = 0; d < D; ++d) acc = fmaf(qs[tid][d], ks[jj][d], acc);
             float x = acc * p.scale;
             if constexpr (BIAS == BIAS_T5) x += tbl[t5_bucket(j - pos)];
+            if constexpr (BIAS == BIAS_T5U) x += tbl[t5u_bucket(j - pos)];
+            if constexpr (BIAS == BIAS_ALIBI) x -= slope * fabsf((float)(j - pos));
             if constexpr (BIAS == BIAS_FULL) x += (row_ok && j < Sk) ? brow[j] : 0.f;
             bool vis = j < Sk;
             if constexpr (MASK != MASK_NONE) vis = vis && (j <= pos);
@@ -126,6 +129,8 @@ static hipError_t launch_f32_d(const FwdParams& p, int mask, int bias, hipStream
     SDPA_CASE(MASK_NONE, BIAS_NONE) SDPA_CASE(MASK_NONE, BIAS_T5) SDPA_CASE(MASK_NONE, BIAS_FULL)
     SDPA_CASE(MASK_CAUSAL, BIAS_NONE) SDPA_CASE(MASK_CAUSAL, BIAS_T5) SDPA_CASE(MASK_CAUSAL, BIAS_FULL)
     SDPA_CASE(MASK_SLIDING, BIAS_NONE) SDPA_CASE(MASK_SLIDING, BIAS_T5) SDPA_CASE(MASK_SLIDING, BIAS_FULL)
+    SDPA_CASE(MASK_NONE, BIAS_ALIBI) SDPA_CASE(MASK_CAUSAL, BIAS_ALIBI) SDPA_CASE(MASK_SLIDING, BIAS_ALIBI)
+    SDPA_CASE(MASK_NONE, BIAS_T5U) SDPA_CASE(MASK_CAUSAL, BIAS_T5U) SDPA_CASE(MASK_SLIDING, BIAS_T5U)
 #undef SDPA_CASE
     return hipErrorInvalidValue;
 }

@@ -7,7 +7,7 @@
 namespace sdpa {
 
 enum { MASK_NONE = 0, MASK_CAUSAL = 1, MASK_SLIDING = 2 };
-enum { BIAS_NONE = 0, BIAS_T5 = 1, BIAS_FULL = 2 };
+enum { BIAS_NONE = 0, BIAS_T5 = 1, BIAS_FULL = 2, BIAS_ALIBI = 3, BIAS_T5U = 4 };
 
 // T5 relative-position table: [Hq][32] fp32. Within one sign of (key - query) the bucket
 // saturates for distances >= 91, so a relative position only matters inside [-91, 91].
@@ -76,6 +76,22 @@ __host__ __device__ inline int t5_bucket(int rel) {
         b = 1 + bitlen;
     }
     return b + (rel > 0 ? 16 : 0);
+}
+
+// T5 unidirectional (decoder) bucket of rel = key position - query position: keys at or after
+// the query share bucket 0; a key n positions back gets n below 16, else
+// 16 + floor(16 log(n/16) / log 8) capped at 31, i.e. 16 plus the number of thresholds below
+// that n reaches (threshold b: the smallest n with n^16 >= 2^(64 + 3b), b = 1..15). Saturates
+// from distance 113.
+constexpr int kT5USat = 113;
+__host__ __device__ inline int t5u_bucket(int rel) {
+    const int n = rel < 0 ? -rel : 0;
+    if (n < 16) return n;
+    const int thr[15] = {19, 21, 24, 27, 31, 35, 40, 46, 52, 59, 67, 77, 87, 99, 113};
+    int b = 16;
+#pragma unroll
+    for (int i = 0; i < 15; ++i) b += (n >= thr[i]) ? 1 : 0;
+    return b;
 }
 
 // Decode a workgroup index into (batch, query head, query tile). Query tiles of one

@@ -25,9 +25,20 @@ from typing import Optional
 import numpy as np
 
 MASK_NONE, MASK_CAUSAL, MASK_SLIDING = 0, 1, 2
-BIAS_NONE, BIAS_T5, BIAS_FULL = 0, 1, 2
+BIAS_NONE, BIAS_T5, BIAS_FULL, BIAS_ALIBI, BIAS_T5U = 0, 1, 2, 3, 4
 MASK_NAMES = {MASK_NONE: "none", MASK_CAUSAL: "causal", MASK_SLIDING: "sliding"}
-BIAS_NAMES = {BIAS_NONE: "none", BIAS_T5: "t5", BIAS_FULL: "full"}
+BIAS_NAMES = {BIAS_NONE: "none", BIAS_T5: "t5", BIAS_FULL: "full", BIAS_ALIBI: "alibi",
+              BIAS_T5U: "t5u"}
+
+
+def alibi_slopes(H: int) -> np.ndarray:
+    """The ALiBi paper's head slopes for H heads (H a power of two): 2^(-8 h / H), h = 1..H;
+    for other H the sequence of the next power of two, interleaved as the paper prescribes."""
+    def pow2(n):
+        return [2.0 ** (-8.0 * (i + 1) / n) for i in range(n)]
+    p = 1 << (H - 1).bit_length()
+    s = pow2(p) if p == H else pow2(p // 2) + pow2(p)[0::2][: H - p // 2]
+    return np.asarray(s[:H], dtype=np.float32)
 
 # T5 relative-position table geometry (fixed constants of the bias kind).
 T5_NUM_BUCKETS = 32
@@ -105,6 +116,12 @@ WORKLOADS = {
                        MASK_CAUSAL, seed=6100),
     "decsw": Workload("mistral_gqa_decode_b8_q4_k32768_sliding4096", 8, 32, 8, 4, 32768, 128,
                       "bf16", MASK_SLIDING, window=4096, seed=6200),
+    # more index-generated biases (survey NEXT-4): ALiBi on the Mistral GQA shape, and the
+    # T5 decoder's unidirectional buckets on T5-small decoder self-attention
+    "c2alibi": Workload("mistral_gqa_causal_alibi_b4_s4096", 4, 32, 8, 4096, 4096, 128, "bf16",
+                        MASK_CAUSAL, bias_kind=BIAS_ALIBI, seed=8000),
+    "c4t5u": Workload("t5_decoder_rpe_b8_h12_s2048_d64", 8, 12, 12, 2048, 2048, 64, "bf16",
+                      MASK_CAUSAL, bias_kind=BIAS_T5U, seed=8100),
 }
 
 
@@ -149,7 +166,7 @@ class Inputs:
     """One workload's inputs, in the storage the kernel receives.
 
     For bf16 workloads q/k/v (and a full bias) are uint16 bf16 words; for f32 they are float32.
-    t5_table is always float32 [Hq][32].
+    t5_table holds the float32 bias table: [Hq][32] for T5 buckets, [Hq] ALiBi slopes.
     """
     wl: Workload
     q: np.ndarray
@@ -162,7 +179,7 @@ class Inputs:
         """float64 views of the exact values the kernel sees: (q, k, v, bias-or-table)."""
         conv = bf16_bits_to_f64 if self.wl.dtype == "bf16" else (lambda a: a.astype(np.float64))
         extra = None
-        if self.wl.bias_kind == BIAS_T5:
+        if self.wl.bias_kind in (BIAS_T5, BIAS_T5U, BIAS_ALIBI):
             extra = self.t5_table.astype(np.float64)
         elif self.wl.bias_kind == BIAS_FULL:
             extra = conv(self.bias)
@@ -180,8 +197,10 @@ def make_inputs(wl: Workload) -> Inputs:
     k = _store(normal_f32(kvs + 1, (wl.B, wl.Sk, wl.Hkv, wl.D)), wl.dtype)
     v = _store(normal_f32(kvs + 2, (wl.B, wl.Sk, wl.Hkv, wl.D)), wl.dtype)
     inp = Inputs(wl, q, k, v)
-    if wl.bias_kind == BIAS_T5:
+    if wl.bias_kind in (BIAS_T5, BIAS_T5U):
         inp.t5_table = normal_f32(wl.seed + 3, (wl.Hq, T5_NUM_BUCKETS))
+    elif wl.bias_kind == BIAS_ALIBI:
+        inp.t5_table = alibi_slopes(wl.Hq)
     elif wl.bias_kind == BIAS_FULL:
         inp.bias = _store(normal_f32(wl.seed + 4, (wl.B, wl.Hq, wl.Sq, wl.Sk), wl.bias_std),
                           wl.dtype)
@@ -283,8 +302,10 @@ def make_varlen_inputs(wl: VarlenWorkload, key_lengths: Optional[list] = None) -
     k = f32_to_bf16_bits(normal_f32(wl.seed + 1, (int(cu_k[-1]), wl.Hkv, wl.D)))
     v = f32_to_bf16_bits(normal_f32(wl.seed + 2, (int(cu_k[-1]), wl.Hkv, wl.D)))
     inp = VarlenInputs(wl, q, k, v, cu_q, cu_k)
-    if wl.bias_kind == BIAS_T5:
+    if wl.bias_kind in (BIAS_T5, BIAS_T5U):
         inp.t5_table = normal_f32(wl.seed + 3, (wl.Hq, T5_NUM_BUCKETS))
+    elif wl.bias_kind == BIAS_ALIBI:
+        inp.t5_table = alibi_slopes(wl.Hq)
     return inp
 
 

@@ -35,9 +35,13 @@ RMS_BAR = U_BF16
 def _bias_rows(bias_kind, bias, b, h, q_pos, Sk):
     if bias_kind == oracle.BIAS_NONE:
         return None
+    rel = np.arange(Sk, dtype=np.int64)[None, :] - q_pos[:, None]
     if bias_kind == oracle.BIAS_T5:
-        rel = np.arange(Sk, dtype=np.int64)[None, :] - q_pos[:, None]
         return bias[h][oracle.t5_bucket(rel)]
+    if bias_kind == oracle.BIAS_T5U:
+        return bias[h][oracle.t5u_bucket(rel)]
+    if bias_kind == oracle.BIAS_ALIBI:
+        return -float(bias[h]) * np.abs(rel).astype(np.float64)
     return bias[b, h]
 
 

@@ -22,7 +22,7 @@ def to_device(inp: si.Inputs):
         return torch.from_numpy(np.ascontiguousarray(a)).cuda()
     q, k, v = dev(inp.q), dev(inp.k), dev(inp.v)
     bias = None
-    if wl.bias_kind == si.BIAS_T5:
+    if wl.bias_kind in (si.BIAS_T5, si.BIAS_T5U, si.BIAS_ALIBI):
         bias = torch.from_numpy(inp.t5_table).cuda()
     elif wl.bias_kind == si.BIAS_FULL:
         bias = dev(inp.bias)

@@ -72,7 +72,11 @@ BAD_CASES = [
     ("mask -1", dict(mask_kind=-1), 5),
     ("sliding window 0", dict(mask_kind=2, window=0), 6),
     ("sliding window -5", dict(mask_kind=2, window=-5), 6),
-    ("bias kind 3", dict(bias_kind=3, bias=P), 7),
+    ("bias kind 5", dict(bias_kind=5, bias=P), 7),
+    ("bias kind -1", dict(bias_kind=-1, bias=P), 7),
+    ("alibi without table", dict(bias_kind=3, bias=None), 7),
+    ("t5u without table", dict(bias_kind=4, bias=None), 7),
+    ("misaligned alibi table", dict(bias_kind=3, bias=P + 2), 9),
     ("t5 without table", dict(bias_kind=1, bias=None), 7),
     ("full without tensor", dict(bias_kind=2, bias=None), 7),
     ("no bias but pointer", dict(bias_kind=0, bias=P), 7),

@@ -75,7 +75,7 @@ def test_bwd_parity_small(gpu_lib, wl):
     check_pairs(gpu_lib, wl, pairs)
 
 
-FULL = ["c2", "c3", "c4t5", "c4full", "c5mha", "c5gqa", "c5mqa"]
+FULL = ["c2", "c3", "c4t5", "c4full", "c5mha", "c5gqa", "c2alibi", "c4t5u"]
 
 
 @pytest.mark.parametrize("key", FULL)

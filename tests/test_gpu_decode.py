@@ -46,6 +46,11 @@ SMALL = [
                  scale_override=-0.08),
     BASE.replace(name="dec_zero_scale_t5_q2_k900", B=1, Hq=4, Hkv=2, Sq=2, Sk=900,
                  bias_kind=si.BIAS_T5, scale_override=0.0),
+    BASE.replace(name="dec_alibi_q1_k5000", B=2, Hq=8, Hkv=2, Sk=5000, bias_kind=si.BIAS_ALIBI),
+    BASE.replace(name="dec_alibi_none_q3_k2000", B=1, Hq=8, Hkv=2, Sq=3, Sk=2000,
+                 mask_kind=si.MASK_NONE, bias_kind=si.BIAS_ALIBI),
+    BASE.replace(name="dec_t5u_d64_q2_k3000", B=1, Hq=6, Hkv=2, Sq=2, Sk=3000, D=64,
+                 bias_kind=si.BIAS_T5U),
 ]
 
 

@@ -64,6 +64,19 @@ SMALL_BF16 = [
         scale_override=0.0),
     si.small(W["c4t5"], B=1, Hq=2, Hkv=2, Sq=140, Sk=140, name_suffix="zero_scale").replace(
         scale_override=0.0),
+    # ALiBi and T5 decoder buckets (bidirectional, causal, sliding; GQA; Sq != Sk)
+    si.small(W["c2alibi"], B=1, Hq=8, Hkv=2, Sq=600, Sk=600, name_suffix="s600"),
+    si.small(W["c2alibi"], B=2, Hq=4, Hkv=4, Sq=300, Sk=300, name_suffix="none").replace(
+        mask_kind=si.MASK_NONE),
+    si.small(W["c2alibi"], B=1, Hq=4, Hkv=1, Sq=200, Sk=500, name_suffix="sliding_q200_k500"
+             ).replace(mask_kind=si.MASK_SLIDING, window=150),
+    si.small(W["c2alibi"], B=1, Hq=4, Hkv=2, Sq=256, Sk=256, name_suffix="d64_neg").replace(
+        D=64, scale_override=-0.1),
+    si.small(W["c4t5u"], B=2, Hq=3, Hkv=3, Sq=333, Sk=333, name_suffix="s333"),
+    si.small(W["c4t5u"], B=1, Hq=4, Hkv=2, Sq=300, Sk=300, name_suffix="none").replace(
+        mask_kind=si.MASK_NONE),
+    si.small(W["c4t5u"], B=1, Hq=4, Hkv=2, Sq=150, Sk=400, name_suffix="d128_q150_k400"
+             ).replace(D=128),
 ]
 
 SMALL_F32 = [
@@ -77,6 +90,8 @@ SMALL_F32 = [
     W["c1"].replace(name="c1_q_gt_k", Sq=170, Sk=90),
     W["c1"].replace(name="c1_neg_scale_none", mask_kind=si.MASK_NONE, scale_override=-0.1),
     W["c1"].replace(name="c1_zero_scale", scale_override=0.0),
+    W["c1"].replace(name="c1_alibi_gqa", Hq=4, Hkv=2, bias_kind=si.BIAS_ALIBI),
+    W["c1"].replace(name="c1_t5u_none", mask_kind=si.MASK_NONE, bias_kind=si.BIAS_T5U, Sk=170),
 ]
 
 
@@ -119,7 +134,7 @@ def test_parity_f32(gpu_lib, wl):
     assert mo <= F32_MAX_ABS and ml <= F32_MAX_ABS
 
 
-FULL = ["c2", "c3", "c3c", "c4t5", "c4full", "c5mha", "c5gqa", "c5mqa"]
+FULL = ["c2", "c3", "c3c", "c4t5", "c4full", "c5mha", "c5gqa", "c5mqa", "c2alibi", "c4t5u"]
 
 
 @pytest.mark.parametrize("key", FULL)

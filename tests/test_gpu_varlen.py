@@ -80,6 +80,8 @@ SMALL = [
     small("vl_t5_causal_gqa", [350, 260], Hq=8, Hkv=2, bias_kind=si.BIAS_T5),
     small("vl_mqa_d128", [500, 31, 250], Hq=8, Hkv=1),
     small("vl_neg_scale", [260, 140], scale_override=-0.09),
+    small("vl_alibi_causal", [400, 150, 300], bias_kind=si.BIAS_ALIBI),
+    small("vl_t5u_d64", [300, 90], D=64, Hq=6, Hkv=3, bias_kind=si.BIAS_T5U),
 ]
 
 
