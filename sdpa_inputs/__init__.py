@@ -108,7 +108,7 @@ WORKLOADS = {
     "c5mha": _c5(32),
     "c5gqa": _c5(8),
     "c5mqa": _c5(1),
-    # KV-cache decode (survey NEXT-2): one new query row per head against a long cache
+    # KV-cache decode: one new query row per head against a long cache
     # (Mistral-7B heads), the MQA variant, and four new rows against a sliding-window cache
     "dec": Workload("mistral_gqa_decode_b16_q1_k16384", 16, 32, 8, 1, 16384, 128, "bf16",
                     MASK_CAUSAL, seed=6000),
@@ -116,7 +116,7 @@ WORKLOADS = {
                        MASK_CAUSAL, seed=6100),
     "decsw": Workload("mistral_gqa_decode_b8_q4_k32768_sliding4096", 8, 32, 8, 4, 32768, 128,
                       "bf16", MASK_SLIDING, window=4096, seed=6200),
-    # more index-generated biases (survey NEXT-4): ALiBi on the Mistral GQA shape, and the
+    # more index-generated biases: ALiBi on the Mistral GQA shape, and the
     # T5 decoder's unidirectional buckets on T5-small decoder self-attention
     "c2alibi": Workload("mistral_gqa_causal_alibi_b4_s4096", 4, 32, 8, 4096, 4096, 128, "bf16",
                         MASK_CAUSAL, bias_kind=BIAS_ALIBI, seed=8000),
@@ -214,7 +214,7 @@ def make_dout(wl: Workload) -> np.ndarray:
 
 
 # ----------------------------------------------------------------------------------------------
-# Packed variable-length sequences (survey NEXT-3)
+# Packed variable-length sequences
 # ----------------------------------------------------------------------------------------------
 @dataclasses.dataclass(frozen=True)
 class VarlenWorkload:
