@@ -478,7 +478,7 @@ def main(argv=None):
     if args.sweep:
         ms = {}
         for key in ["c2", "c2c", "c3", "c3c", "c4t5", "c4full", "c5mha", "c5gqa", "c5mqa",
-                    "c2alibi", "c4t5u"]:
+                    "c2alibi", "c4t5u", "c2d32", "c2d256"]:
             w2 = si.WORKLOADS[key]
             # at least 30 warmup launches: clocks ramp up over ~15 launches after the GPU idles
             t2 = time_workload(sdpa, w2, max(5, args.steps // 2), max(30, args.warmup))

@@ -28,7 +28,7 @@ int validate(const void* q, const void* k, const void* v, const void* out, const
     if (!q || !k || !v || !out || !lse) return SDPA_ERR_NULL;
     if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || Sk < 1) return SDPA_ERR_SHAPE;
     if (Hq % Hkv != 0) return SDPA_ERR_HEADS;
-    if (D != 64 && D != 128) return SDPA_ERR_HEADDIM;
+    if (D != 32 && D != 64 && D != 128 && D != 256) return SDPA_ERR_HEADDIM;
     if (mask_kind != SDPA_MASK_NONE && mask_kind != SDPA_MASK_CAUSAL &&
         mask_kind != SDPA_MASK_SLIDING)
         return SDPA_ERR_MASK;
@@ -80,6 +80,7 @@ int validate_bwd(const void* q, const void* k, const void* v, const void* out,
     int st = validate(q, k, v, out, lse, B, Hq, Hkv, Sq, Sk, D, scale, mask_kind, window,
                       bias_kind, bias_tbl, 2);
     if (st != SDPA_OK) return st;
+    if (D != 64 && D != 128) return SDPA_ERR_HEADDIM;   // gradient kernels: D = 64 and 128
     // grid of the dK/dV kernel: one workgroup per 128 keys of each (b, KV head)
     if ((long long)B * Hkv * ((Sk + 127) / 128) >= (1LL << 31)) return SDPA_ERR_SHAPE;
     if (!aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
@@ -115,6 +116,7 @@ int decode_common(const void* q, const void* k, const void* v, void* out, float*
     int st = validate(q, k, v, out, lse, B, Hq, Hkv, Sq, Sk, D, scale, mask_kind, window,
                       bias_kind, bias_tbl, 2);
     if (st != SDPA_OK) return st;
+    if (D != 64 && D != 128) return SDPA_ERR_HEADDIM;   // decode kernels: D = 64 and 128
     const int G = Hq / Hkv;
     if ((long long)Sq * G >= (1LL << 30)) return SDPA_ERR_SHAPE;
     const long long grid = (long long)B * Hkv * sdpa::dec_row_blocks(G, Sq) *
@@ -146,7 +148,8 @@ int varlen_common(const void* q, const void* k, const void* v, void* out, float*
     int st = validate(q, k, v, out, lse, 1, Hq, Hkv, total_q, total_k, D, scale, mask_kind,
                       window, bias_kind, bias_tbl, 2);
     if (st != SDPA_OK) return st;
-    if ((long long)n_seqs * Hq * ((max_q + 255) / 256) >= (1LL << 31)) return SDPA_ERR_SHAPE;
+    // grid: one workgroup per 128- or 256-row query tile of each (sequence, head)
+    if ((long long)n_seqs * Hq * ((max_q + 127) / 128) >= (1LL << 31)) return SDPA_ERR_SHAPE;
     if (!aligned(cu_q, 4) || !aligned(cu_k, 4)) return SDPA_ERR_ALIGN;
     sdpa::FwdParams p = make_params(q, k, v, out, lse, n_seqs, Hq, Hkv, max_q, max_k, scale,
                                     mask_kind, window, bias_tbl);
@@ -272,7 +275,7 @@ const char* sdpa_status_str(int status) {
         case SDPA_ERR_NULL: return "a required pointer is NULL";
         case SDPA_ERR_SHAPE: return "invalid or too large shape (B, Hq, Hkv, Sq, Sk)";
         case SDPA_ERR_HEADS: return "Hq is not a multiple of Hkv";
-        case SDPA_ERR_HEADDIM: return "head dim D must be 64 or 128";
+        case SDPA_ERR_HEADDIM: return "head dim D must be 32, 64, 128 or 256 (64 or 128 for gradients and decode)";
         case SDPA_ERR_MASK: return "unknown mask_kind";
         case SDPA_ERR_WINDOW: return "sliding window must be >= 1";
         case SDPA_ERR_BIAS: return "unknown bias_kind or bias_tbl inconsistent with it";

@@ -8,8 +8,9 @@
 // Version 4.40.0"; FAT5 README, T5-like relative position bias), and key tiles that a mask
 // hides completely are never visited.
 //
-// Work decomposition (one workgroup = 8 wave64s = one 256-row query tile of one (batch, head),
-// two waves per SIMD):
+// Work decomposition (one workgroup = one query tile of one (batch, head); 32 query rows per
+// wave; D = 64 and 128: 8 waves, two per SIMD; D = 32: 4 waves, up to four workgroups per CU;
+// D = 256: 4 waves, one per SIMD, whose O accumulators need the whole register file):
 //   * each wave owns 32 query rows; its Q fragment stays in VGPRs for the whole kernel;
 //   * keys are visited in tiles of 64, ascending. K and V tiles are copied global -> LDS by
 //     the DMA path of the load unit (global_load_lds_dwordx4) into a K ring (2 slots; 3 for
@@ -47,9 +48,12 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 
-constexpr int kWaves = 8;           // one workgroup per CU, two waves per SIMD
-constexpr int kThreads = 64 * kWaves;
-constexpr int kBM = 32 * kWaves;    // query rows per workgroup
+// waves per workgroup, and the waves per SIMD the register budget is sized for
+template <int D> constexpr int waves_of() { return (D == 64 || D == 128) ? 8 : 4; }
+template <int D, int BIAS> constexpr int waves_per_eu_of() {
+    return D == 256 ? 1 : ((D == 32 && BIAS != BIAS_FULL) ? 3 : 2);
+}
+template <int D> constexpr int rows_of() { return 32 * waves_of<D>(); }   // query rows per workgroup
 constexpr int kBN = 64;             // keys per tile
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -66,19 +70,24 @@ __device__ __forceinline__ int perm32(int r) {
 }
 
 // LDS bank swizzles: XOR on the 16-byte chunk index within a row of the K or V tile.
-// K (read by ds_read_b128, 8 lanes on rows {0..3, 16..19} + 4g): D=128 rows are 16 chunks,
-// D=64 rows are 8 chunks.
+// K (read by ds_read_b128, 8 lanes on rows {0..3, 16..19} + 4g): D=128 rows are 16 chunks
+// (one full sweep of the 64 banks), D=256 rows two sweeps (the D=128 pattern on the low four
+// bits of the chunk index), D=64 rows 8 chunks, D=32 rows 4 chunks (four rows per sweep).
 template <int D>
 __device__ __forceinline__ int k_swz(int row) {
-    if constexpr (D == 128) {
+    if constexpr (D >= 128) {
         return (row & 3) | (((row >> 4) & 1) << 2) | (((row >> 2) & 1) << 3);
-    } else {
+    } else if constexpr (D == 64) {
         return ((row & 3) ^ ((row >> 2) & 1)) | (((row >> 4) & 1) << 2);
+    } else {
+        return ((row >> 2) & 1) | (((row >> 4) & 1) << 1);
     }
 }
 // V (read by ds_read_b64_tr_b16, a 16-lane group touching two adjacent chunks of 4
-// consecutive rows): rows 4k..4k+3 go to XOR patterns {0, 2, 4, 6}.
-__device__ __forceinline__ int v_swz(int row) { return 2 * (row & 3); }
+// consecutive rows): rows 4k..4k+3 go to XOR patterns {0, 2, 4, 6} ({0, 2} for the 4-chunk
+// rows of D = 32). Depends on row & 3 only.
+template <int D>
+__device__ __forceinline__ int v_swz(int row) { return D == 32 ? 2 * (row & 1) : 2 * (row & 3); }
 
 __device__ __forceinline__ float partner_max(float x) {
     // max of this lane and lane l ^ 32 (the other half of the wave)
@@ -109,7 +118,11 @@ __device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
 
 
 template <int D, int MASK, int BIAS, bool OUT_F32, bool VARLEN>
-__global__ __launch_bounds__(kThreads, 1) void sdpa_fwd_bf16_kernel(const FwdParams p) {
+__global__ __launch_bounds__(64 * waves_of<D>(), (waves_per_eu_of<D, BIAS>()))
+void sdpa_fwd_bf16_kernel(const FwdParams p) {
+    constexpr int kWaves = waves_of<D>();
+    constexpr int kThreads = 64 * kWaves;
+    constexpr int kBM = rows_of<D>();
     constexpr int CH = D / 8;           // 16-byte chunks per K/V row
     constexpr int KS = D / 16;          // k-steps of Q.K^T
     constexpr int DB = D / 32;          // 32-wide d blocks of O^T
@@ -119,10 +132,12 @@ __global__ __launch_bounds__(kThreads, 1) void sdpa_fwd_bf16_kernel(const FwdPar
     // bias tile of the same keys), then the V ring (NVS slots).
     constexpr bool FB = BIAS == BIAS_FULL;
     // A full bias streams from HBM with the K tiles: for D = 64 the K ring is 3 deep (K tiles
-    // are fetched two iterations before use), which the LDS holds; otherwise 2 deep.
+    // are fetched two iterations before use), which the LDS holds; otherwise 2 deep. At
+    // D = 256 the K and V rings fill the LDS: the bias is read from HBM by each lane instead.
+    constexpr bool FB_LDS = FB && D != 256;
     constexpr int NKS = (FB && D == 64) ? 3 : 2;
     constexpr int NVS = 2;
-    constexpr int BTILE = FB ? kBM * kBN : 0;
+    constexpr int BTILE = FB_LDS ? kBM * kBN : 0;
     constexpr int KSTAGE = TILE + BTILE;
     constexpr int VRING = NKS * KSTAGE;
     static_assert((NKS * KSTAGE + NVS * TILE) * 2 <= 160 * 1024, "LDS");
@@ -255,10 +270,10 @@ __global__ __launch_bounds__(kThreads, 1) void sdpa_fwd_bf16_kernel(const FwdPar
     constexpr int XFERS = (kBN * D * 2) / 1024;                // per tensor per tile
     constexpr int XPW = XFERS / kWaves;                        // per wave per tensor
     static_assert(XPW * kWaves == XFERS, "dma split");
-    constexpr int XPB = FB ? (kBM * kBN * 2 / 1024) / kWaves : 0;   // bias transfers per wave
+    constexpr int XPB = FB_LDS ? (kBM * kBN * 2 / 1024) / kWaves : 0;   // bias transfers per wave
     const uint32_t lds_base = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint16_t*)smem);
     // a full bias goes through the LDS ring when its rows split into whole 16-byte chunks
-    const bool fb_dma = FB && ((Sk & 7) == 0);
+    const bool fb_dma = FB_LDS && ((Sk & 7) == 0);
     const uint16_t* fbg = FB ? (const uint16_t*)p.bias + ((size_t)b * p.Hq + hq) * (size_t)Sq * Sk
                              : nullptr;
     auto kslot = [&](int t) { return (t - t_begin) % NKS; };
@@ -277,7 +292,7 @@ __global__ __launch_bounds__(kThreads, 1) void sdpa_fwd_bf16_kernel(const FwdPar
     for (int n = 0; n < XPW; ++n) {
         const int row = (wave * XPW + n) * ROWS_PER_XFER + lane / CH;   // tile row this lane fills
         k_off[n] = (uint32_t)row * kv_row_bytes + (uint32_t)((((lane % CH) ^ k_swz<D>(row))) * 16);
-        v_off[n] = (uint32_t)row * kv_row_bytes + (uint32_t)((((lane % CH) ^ v_swz(row))) * 16);
+        v_off[n] = (uint32_t)row * kv_row_bytes + (uint32_t)((((lane % CH) ^ v_swz<D>(row))) * 16);
     }
     const uint32_t dma_wave_off = __builtin_amdgcn_readfirstlane((uint32_t)(wave * XPW * 1024));
     auto dma_kv_x = [&](const uint16_t* g, uint32_t off_full, bool vtile, uint32_t dst, int t, int n) {
@@ -286,7 +301,7 @@ __global__ __launch_bounds__(kThreads, 1) void sdpa_fwd_bf16_kernel(const FwdPar
         uint32_t off = off_full;
         if (j0 + kBN > Sk) {
             const int row = (wave * XPW + n) * ROWS_PER_XFER + lane / CH;
-            const int sw = vtile ? v_swz(row) : k_swz<D>(row);
+            const int sw = vtile ? v_swz<D>(row) : k_swz<D>(row);
             base = g;
             off = (uint32_t)min(j0 + row, Sk - 1) * kv_row_bytes + (uint32_t)(((lane % CH) ^ sw) * 16);
         }
@@ -302,7 +317,7 @@ __global__ __launch_bounds__(kThreads, 1) void sdpa_fwd_bf16_kernel(const FwdPar
                  lds_base + (uint32_t)((VRING + vslot(t) * TILE) * 2 + n * 1024) + dma_wave_off, t, n);
     };
     auto dma_b_x = [&](int t, int n) {     // full-bias transfer n of tile t
-        if constexpr (FB) {
+        if constexpr (FB_LDS) {
             if (fb_dma) {
                 // bias tile [kBM rows][kBN keys], 128-byte rows, chunk swizzle (row >> 1) & 7;
                 // keys past the end of a partial last tile re-read the last whole chunk
@@ -368,7 +383,7 @@ __global__ __launch_bounds__(kThreads, 1) void sdpa_fwd_bf16_kernel(const FwdPar
     const int gg = lane >> 4, li = lane & 15, la = li & 3;
     const int v_key = 16 * hh + (li >> 2);
     const int v_dlo = 16 * DB * (gg & 1) + 8 * (la & 1) + 4 * (la >> 1);
-    const int v_sw = v_swz(v_key);            // same for key + 4n
+    const int v_sw = v_swz<D>(v_key);         // same for key + 4n
 
     auto read_k = [&](const uint16_t* kb, int ks, bf16x8* dst) {
         const int ch = ((2 * ks + hh) ^ k_sw) * 8;
@@ -529,7 +544,7 @@ __global__ __launch_bounds__(kThreads, 1) void sdpa_fwd_bf16_kernel(const FwdPar
             }
             if constexpr (DO_PREP) {
                 if (g == 0) {
-                    if constexpr (FB) {
+                    if constexpr (FB_LDS) {
                         if (fb_dma) {
                             // this tile's bias rows from the LDS ring: row (wave*32 + r32),
                             // chunks 4 jb + 2 hh + {0, 1}
@@ -730,7 +745,7 @@ template <int D, int MASK, int BIAS, bool OUT_F32, bool VARLEN>
 static hipError_t launch_one(const FwdParams& p, hipStream_t stream) {
     const unsigned grid = (unsigned)((size_t)p.B * p.Hq * p.n_qt);
     hipLaunchKernelGGL((sdpa_fwd_bf16_kernel<D, MASK, BIAS, OUT_F32, VARLEN>), dim3(grid),
-                       dim3(kThreads), 0, stream, p);
+                       dim3(64 * waves_of<D>()), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -761,19 +776,24 @@ static hipError_t launch_varlen_d(const FwdParams& p, int mask, int bias, hipStr
     return hipErrorInvalidValue;
 }
 
+template <int D>
+static hipError_t launch_dim(FwdParams p, int mask, int bias, bool out_f32, hipStream_t s) {
+    constexpr int bm = rows_of<D>();
+    p.n_qt = (p.Sq + bm - 1) / bm;
+    if (p.cu_q)
+        return out_f32 ? launch_varlen_d<D, true>(p, mask, bias, s) : launch_varlen_d<D, false>(p, mask, bias, s);
+    return out_f32 ? launch_d<D, true>(p, mask, bias, s) : launch_d<D, false>(p, mask, bias, s);
+}
+
 hipError_t launch_fwd_bf16(FwdParams p, int D, int mask, int bias, bool out_f32, hipStream_t s) {
-    p.n_qt = (p.Sq + kBM - 1) / kBM;
     p.xcd_remap = ((p.B * p.Hkv) % 8 == 0) ? 1 : 0;
-    if (p.cu_q) {
-        if (D == 128)
-            return out_f32 ? launch_varlen_d<128, true>(p, mask, bias, s) : launch_varlen_d<128, false>(p, mask, bias, s);
-        if (D == 64)
-            return out_f32 ? launch_varlen_d<64, true>(p, mask, bias, s) : launch_varlen_d<64, false>(p, mask, bias, s);
-        return hipErrorInvalidValue;
+    switch (D) {
+        case 32: return launch_dim<32>(p, mask, bias, out_f32, s);
+        case 64: return launch_dim<64>(p, mask, bias, out_f32, s);
+        case 128: return launch_dim<128>(p, mask, bias, out_f32, s);
+        case 256: return launch_dim<256>(p, mask, bias, out_f32, s);
+        default: return hipErrorInvalidValue;
     }
-    if (D == 128) return out_f32 ? launch_d<128, true>(p, mask, bias, s) : launch_d<128, false>(p, mask, bias, s);
-    if (D == 64) return out_f32 ? launch_d<64, true>(p, mask, bias, s) : launch_d<64, false>(p, mask, bias, s);
-    return hipErrorInvalidValue;
 }
 
 }  // namespace sdpa

@@ -136,8 +136,10 @@ static hipError_t launch_f32_d(const FwdParams& p, int mask, int bias, hipStream
 }
 
 hipError_t launch_fwd_f32(FwdParams p, int D, int mask, int bias, hipStream_t s) {
-    if (D == 128) return launch_f32_d<128>(p, mask, bias, s);
+    if (D == 32) return launch_f32_d<32>(p, mask, bias, s);
     if (D == 64) return launch_f32_d<64>(p, mask, bias, s);
+    if (D == 128) return launch_f32_d<128>(p, mask, bias, s);
+    if (D == 256) return launch_f32_d<256>(p, mask, bias, s);
     return hipErrorInvalidValue;
 }
 

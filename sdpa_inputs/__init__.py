@@ -122,6 +122,11 @@ WORKLOADS = {
                         MASK_CAUSAL, bias_kind=BIAS_ALIBI, seed=8000),
     "c4t5u": Workload("t5_decoder_rpe_b8_h12_s2048_d64", 8, 12, 12, 2048, 2048, 64, "bf16",
                       MASK_CAUSAL, bias_kind=BIAS_T5U, seed=8100),
+    # the head-dim sweep at both ends (32 and 256) on the Mistral GQA causal shape
+    "c2d32": Workload("gqa_causal_d32_b4_s4096", 4, 32, 8, 4096, 4096, 32, "bf16",
+                      MASK_CAUSAL, seed=8200),
+    "c2d256": Workload("gqa_causal_d256_b4_s4096", 4, 32, 8, 4096, 4096, 256, "bf16",
+                       MASK_CAUSAL, seed=8300),
 }
 
 

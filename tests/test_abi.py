@@ -67,7 +67,8 @@ BAD_CASES = [
     ("Hkv=0", dict(Hkv=0), 2),
     ("Hq % Hkv", dict(Hq=6, Hkv=4), 3),
     ("D=96", dict(D=96), 4),
-    ("D=256", dict(D=256), 4),
+    ("D=512", dict(D=512), 4),
+    ("D=16", dict(D=16), 4),
     ("mask 3", dict(mask_kind=3), 5),
     ("mask -1", dict(mask_kind=-1), 5),
     ("sliding window 0", dict(mask_kind=2, window=0), 6),
@@ -124,7 +125,10 @@ def call_bwd(entry="sdpa_bwd", **kw):
                              a["bias_kind"], a["bias"], a["stream"])
 
 
-BWD_CASES = BAD_CASES + [
+# the gradient and decode kernels cover D = 64 and 128 only
+NARROW_D = [("D=32 (forward only)", dict(D=32), 4), ("D=256 (forward only)", dict(D=256), 4)]
+
+BWD_CASES = BAD_CASES + NARROW_D + [
     ("null dout", dict(dout=None), 1),
     ("null dq", dict(dq=None), 1),
     ("null dk", dict(dk=None), 1),
@@ -162,7 +166,7 @@ def call_dec(entry="sdpa_decode", **kw):
                                 a["bias_kind"], a["bias"], a["stream"])
 
 
-DEC_CASES = BAD_CASES + [
+DEC_CASES = BAD_CASES + NARROW_D + [
     ("null ws", dict(ws=None), 11),
     ("misaligned ws", dict(ws=P + 8), 11),
     ("small ws", dict(ws_bytes=16), 11),
@@ -183,6 +187,7 @@ def test_decode_workspace_size(lib):
     assert units % (16 * 8) == 0
     assert sdpa.decode_ws_bytes(1, 6, 4, 1, 100, 128) == 0
     assert sdpa.decode_ws_bytes(1, 8, 8, 1, 100, 96) == 0
+    assert sdpa.decode_ws_bytes(1, 8, 8, 1, 100, 256) == 0
     # the exact requirement is accepted, one byte less is not (validation only, no launch)
     need = sdpa.decode_ws_bytes(1, 4, 2, 8, 8, 64)
     assert call_dec(ws_bytes=need - 1) == 11
@@ -206,7 +211,7 @@ VL_CASES = [
     ("null q", dict(q=None), 1),
     ("no sequences", dict(n=0), 2), ("no query tokens", dict(tq=0), 2),
     ("no key tokens", dict(tk=0), 2), ("max len 0", dict(mq=0), 2),
-    ("heads", dict(Hq=6, Hkv=4), 3), ("head dim", dict(D=32), 4),
+    ("heads", dict(Hq=6, Hkv=4), 3), ("head dim", dict(D=96), 4),
     ("mask", dict(mask_kind=7), 5), ("window", dict(mask_kind=2, window=0), 6),
     ("full bias", dict(bias_kind=2, bias=P), 7), ("t5 without table", dict(bias_kind=1), 7),
     ("scale", dict(scale=math.inf), 8),

@@ -14,7 +14,8 @@ pytestmark = pytest.mark.gpu
 W = si.WORKLOADS
 
 
-@pytest.mark.parametrize("key", ["c5gqa", "c5mqa", "c2", "c3", "c4t5", "c4full"])
+@pytest.mark.parametrize("key", ["c5gqa", "c5mqa", "c2", "c3", "c4t5", "c4full", "c2d32",
+                                 "c2d256"])
 def test_bitwise_determinism_100_runs(gpu_lib, key):
     import torch
     wl = W[key]
@@ -47,9 +48,10 @@ def test_sliding_window_ge_seqlen_is_causal_bitwise(gpu_lib):
         assert torch.equal(o_s, o_c) and torch.equal(l_s, l_c), (S, w)
 
 
-def test_causal_row0_is_v0_bitwise(gpu_lib):
+@pytest.mark.parametrize("D", [32, 64, 128, 256])
+def test_causal_row0_is_v0_bitwise(gpu_lib, D):
     import torch
-    wl = si.small(W["c5gqa"], B=2, Hq=8, Hkv=2, Sq=300, Sk=300, name_suffix="row0")
+    wl = si.small(W["c5gqa"], B=2, Hq=8, Hkv=2, Sq=300, Sk=300, name_suffix="row0").replace(D=D)
     inp = si.make_inputs(wl)
     dev = to_device(inp)
     o, _ = run_gpu(gpu_lib, wl, dev)
@@ -58,9 +60,10 @@ def test_causal_row0_is_v0_bitwise(gpu_lib):
     assert torch.equal(o[:, 0], v[:, 0].repeat_interleave(G, dim=1))
 
 
-def test_window1_is_v_bitwise(gpu_lib):
+@pytest.mark.parametrize("D", [32, 64, 128, 256])
+def test_window1_is_v_bitwise(gpu_lib, D):
     import torch
-    wl = si.small(W["c2"], B=1, Hq=4, Hkv=2, Sq=200, Sk=200, window=1, name_suffix="w1")
+    wl = si.small(W["c2"], B=1, Hq=4, Hkv=2, Sq=200, Sk=200, window=1, name_suffix="w1").replace(D=D)
     dev = to_device(si.make_inputs(wl))
     o, _ = run_gpu(gpu_lib, wl, dev)
     assert torch.equal(o, dev[2].repeat_interleave(2, dim=2))

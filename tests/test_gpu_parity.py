@@ -77,6 +77,33 @@ SMALL_BF16 = [
         mask_kind=si.MASK_NONE),
     si.small(W["c4t5u"], B=1, Hq=4, Hkv=2, Sq=150, Sk=400, name_suffix="d128_q150_k400"
              ).replace(D=128),
+    # head dims 32 and 256: every mask and bias kind, GQA / MQA, ragged tails, Sq != Sk
+    si.small(W["c2d32"], B=2, Hq=8, Hkv=2, Sq=333, Sk=333, name_suffix="s333"),
+    si.small(W["c2d32"], B=1, Hq=4, Hkv=1, Sq=300, Sk=520, name_suffix="sliding_q300_k520"
+             ).replace(mask_kind=si.MASK_SLIDING, window=150),
+    si.small(W["c2d32"], B=1, Hq=3, Hkv=3, Sq=270, Sk=270, name_suffix="t5_none").replace(
+        mask_kind=si.MASK_NONE, bias_kind=si.BIAS_T5),
+    si.small(W["c2d32"], B=1, Hq=2, Hkv=2, Sq=200, Sk=264, name_suffix="full_none").replace(
+        mask_kind=si.MASK_NONE, bias_kind=si.BIAS_FULL),
+    si.small(W["c2d32"], B=1, Hq=4, Hkv=2, Sq=300, Sk=100, name_suffix="alibi_q300_k100"
+             ).replace(bias_kind=si.BIAS_ALIBI),
+    si.small(W["c2d32"], B=1, Hq=4, Hkv=4, Sq=260, Sk=260, name_suffix="t5u_neg").replace(
+        bias_kind=si.BIAS_T5U, scale_override=-0.15),
+    si.small(W["c2d256"], B=2, Hq=8, Hkv=2, Sq=333, Sk=333, name_suffix="s333"),
+    si.small(W["c2d256"], B=1, Hq=4, Hkv=1, Sq=300, Sk=520, name_suffix="sliding_q300_k520"
+             ).replace(mask_kind=si.MASK_SLIDING, window=150),
+    si.small(W["c2d256"], B=1, Hq=3, Hkv=3, Sq=270, Sk=270, name_suffix="t5_none").replace(
+        mask_kind=si.MASK_NONE, bias_kind=si.BIAS_T5),
+    si.small(W["c2d256"], B=1, Hq=2, Hkv=2, Sq=200, Sk=264, name_suffix="full_none").replace(
+        mask_kind=si.MASK_NONE, bias_kind=si.BIAS_FULL),
+    si.small(W["c2d256"], B=1, Hq=2, Hkv=1, Sq=130, Sk=197, name_suffix="full_causal_odd_sk"
+             ).replace(bias_kind=si.BIAS_FULL),
+    si.small(W["c2d256"], B=1, Hq=4, Hkv=2, Sq=300, Sk=100, name_suffix="alibi_q300_k100"
+             ).replace(bias_kind=si.BIAS_ALIBI),
+    si.small(W["c2d256"], B=1, Hq=4, Hkv=4, Sq=260, Sk=260, name_suffix="t5u_neg").replace(
+        bias_kind=si.BIAS_T5U, scale_override=-0.15),
+    si.small(W["c2d256"], B=1, Hq=2, Hkv=1, Sq=150, Sk=150, name_suffix="zero_scale").replace(
+        scale_override=0.0),
 ]
 
 SMALL_F32 = [
@@ -92,6 +119,12 @@ SMALL_F32 = [
     W["c1"].replace(name="c1_zero_scale", scale_override=0.0),
     W["c1"].replace(name="c1_alibi_gqa", Hq=4, Hkv=2, bias_kind=si.BIAS_ALIBI),
     W["c1"].replace(name="c1_t5u_none", mask_kind=si.MASK_NONE, bias_kind=si.BIAS_T5U, Sk=170),
+    W["c1"].replace(name="c1_d32_sliding_gqa", Hq=4, Hkv=2, Sq=150, Sk=150, D=32,
+                    mask_kind=si.MASK_SLIDING, window=40),
+    W["c1"].replace(name="c1_d32_t5", D=32, bias_kind=si.BIAS_T5),
+    W["c1"].replace(name="c1_d256_causal", D=256, Sq=150, Sk=150),
+    W["c1"].replace(name="c1_d256_full_none", D=256, mask_kind=si.MASK_NONE,
+                    bias_kind=si.BIAS_FULL, Sq=90, Sk=130),
 ]
 
 
@@ -134,7 +167,8 @@ def test_parity_f32(gpu_lib, wl):
     assert mo <= F32_MAX_ABS and ml <= F32_MAX_ABS
 
 
-FULL = ["c2", "c3", "c3c", "c4t5", "c4full", "c5mha", "c5gqa", "c5mqa", "c2alibi", "c4t5u"]
+FULL = ["c2", "c3", "c3c", "c4t5", "c4full", "c5mha", "c5gqa", "c5mqa", "c2alibi", "c4t5u", "c2d32",
+        "c2d256"]
 
 
 @pytest.mark.parametrize("key", FULL)

@@ -82,6 +82,9 @@ SMALL = [
     small("vl_neg_scale", [260, 140], scale_override=-0.09),
     small("vl_alibi_causal", [400, 150, 300], bias_kind=si.BIAS_ALIBI),
     small("vl_t5u_d64", [300, 90], D=64, Hq=6, Hkv=3, bias_kind=si.BIAS_T5U),
+    small("vl_d32_ragged_mqa", [300, 1, 129, 257], D=32, Hq=4, Hkv=1),
+    small("vl_d256_sliding_t5", [260, 0, 190], [300, 20, 190], D=256, Hq=4, Hkv=2,
+          mask_kind=si.MASK_SLIDING, window=70, bias_kind=si.BIAS_T5),
 ]
 
 
