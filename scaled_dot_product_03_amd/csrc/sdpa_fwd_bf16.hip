@@ -27,7 +27,9 @@
 //     and row max of tile t+1 (phase B), so the matrix cores are fed while the VALU works;
 //   * online softmax in the log2 domain with a lazy rescale: the running reference max only
 //     moves (and O is only rescaled) when a row's max grows by more than 2^8; scale*log2(e)
-//     is folded into the exponent's FMA when the bias is constant over a tile.
+//     is folded into the exponent's FMA when the bias is constant over a tile. The row sum
+//     adds the bf16-rounded weights that enter P.V (v_dot2_f32_bf16 against (1, 1)), so the
+//     normaliser matches the numerator exactly (V = 1 gives O = 1).
 // Reduction order is fixed (ascending key tiles, fixed MFMA chains, no atomics): results are
 // bitwise reproducible run to run.
 #include <hip/hip_runtime.h>
@@ -523,6 +525,9 @@ void sdpa_fwd_bf16_kernel(const FwdParams p) {
         }
         u32x4 fb[4];
         float ext = -INFINITY;
+        bf16x2 ones2;
+        ones2[0] = (__bf16)1.0f;
+        ones2[1] = (__bf16)1.0f;
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             if constexpr (DO_PV) {
@@ -534,7 +539,14 @@ void sdpa_fwd_bf16_kernel(const FwdParams p) {
                 for (int c = 0; c < 4; ++c) {
                     const float p0 = cs[jb][8 * s + 2 * c], p1 = cs[jb][8 * s + 2 * c + 1];
                     pk[c] = pack_bf16x2(p0, p1);
-                    l_part += p0 + p1;
+                    // row sum of the bf16 weights the P.V product uses (one v_dot2 per pair).
+                    // The pair is rounded again here rather than taken from pk[c]: reading the
+                    // element of the packed vector made this compiler feed pk[0] to all four
+                    // dot products; the two roundings are one instruction after CSE.
+                    bf16x2 pr;
+                    pr[0] = (__bf16)p0;
+                    pr[1] = (__bf16)p1;
+                    l_part = __builtin_amdgcn_fdot2_f32_bf16(pr, ones2, l_part, false);
                 }
                 const bf16x8 pbf = __builtin_bit_cast(bf16x8, pk);
                 if (g + VPRE < 4) read_v(vb, g + VPRE, vfr[(g + VPRE) % (VPRE + 1)]);

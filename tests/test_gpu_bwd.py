@@ -15,7 +15,10 @@ import pytest
 import sdpa_inputs as si
 from bwd_check import check_grad, pair_reference
 from helpers import out_to_f64, to_device
-from test_gpu_parity import SMALL_BF16
+from test_gpu_parity import SMALL_BF16 as _SMALL_FWD
+
+# the gradient kernels take D = 64 and 128 (32 and 256 are refused with SDPA_ERR_HEADDIM)
+SMALL_BF16 = [w for w in _SMALL_FWD if w.D in (64, 128)]
 
 pytestmark = pytest.mark.gpu
 
@@ -123,3 +126,13 @@ def test_bwd_sliding_window_ge_seqlen_is_causal_bitwise(gpu_lib):
         b = gpu_lib.bwd(q, k, v, out, lse, dod, mask="sliding", window=w)
         for x, y in zip(a, b):
             assert torch.equal(x, y), w
+
+
+@pytest.mark.parametrize("D", [32, 256])
+def test_bwd_refuses_head_dims_outside_64_128(gpu_lib, D):
+    import torch
+    q = torch.zeros((1, 64, 2, D), dtype=torch.bfloat16, device="cuda")
+    lse = torch.zeros((1, 2, 64), dtype=torch.float32, device="cuda")
+    with pytest.raises(gpu_lib.SdpaError) as e:
+        gpu_lib.bwd(q, q, q, q, lse, q)
+    assert e.value.status == 4

@@ -125,3 +125,13 @@ def test_decode_bitwise_determinism_100_runs(gpu_lib):
         assert torch.equal(o, o0) and torch.equal(l, l0)
     torch.cuda.synchronize()
     print(f"{wl.name}: decode deterministic over 100 runs", flush=True)
+
+
+@pytest.mark.parametrize("D", [32, 256])
+def test_decode_refuses_head_dims_outside_64_128(gpu_lib, D):
+    import torch
+    q = torch.zeros((1, 1, 2, D), dtype=torch.bfloat16, device="cuda")
+    k = torch.zeros((1, 300, 2, D), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(gpu_lib.SdpaError) as e:
+        gpu_lib.decode(q, k, k)
+    assert e.value.status == 4
