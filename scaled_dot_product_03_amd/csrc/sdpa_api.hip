@@ -119,9 +119,10 @@ int decode_common(const void* q, const void* k, const void* v, void* out, float*
     if (D != 64 && D != 128) return SDPA_ERR_HEADDIM;   // decode kernels: D = 64 and 128
     const int G = Hq / Hkv;
     if ((long long)Sq * G >= (1LL << 30)) return SDPA_ERR_SHAPE;
-    const long long grid = (long long)B * Hkv * sdpa::dec_row_blocks(G, Sq) *
-                           sdpa::dec_splits(B, Hkv, G, Sq, Sk);
-    if (grid >= (1LL << 31)) return SDPA_ERR_SHAPE;
+    // grids: split kernel B * Hkv * row blocks * splits, merge kernel up to 4 per row block
+    const long long blocks = (long long)B * Hkv * sdpa::dec_row_blocks(G, Sq);
+    const long long splits = sdpa::dec_splits(B, Hkv, G, Sq, Sk);
+    if (blocks * (splits > 4 ? splits : 4) >= (1LL << 31)) return SDPA_ERR_SHAPE;
     if (!ws || !aligned(ws, 16) ||
         ws_bytes < sdpa::dec_ws_floats(B, Hkv, G, Sq, Sk, D) * sizeof(float))
         return SDPA_ERR_WORKSPACE;

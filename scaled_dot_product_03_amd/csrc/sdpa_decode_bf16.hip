@@ -331,36 +331,88 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void split_kernel(const DecP
 // ------------------------------------------------------------------------------------------
 // combine the splits of each (batch, KV head, row block) in split order
 // ------------------------------------------------------------------------------------------
+// Each thread merges 4 consecutive columns of one row: a workgroup covers kMergeRows rows, and
+// a 32-row block takes 32 / kMergeRows workgroups (enough of them to spread the reads).
+template <int D>
+constexpr int merge_rows() { return 256 / (D / 4); }
+
 template <int D, bool OUT_F32>
 __global__ __launch_bounds__(256) void merge_kernel(const DecParams p) {
+    constexpr int TPR = D / 4;                      // threads per row
+    constexpr int MR = merge_rows<D>();             // rows per workgroup
+    constexpr int SUB = 32 / MR;                    // workgroups per 32-row block
     const int tid = threadIdx.x;
-    const int row = tid >> 3, cc = tid & 7;
-    const int rb = blockIdx.x % p.n_rb, group = blockIdx.x / p.n_rb;
+    const int row = (blockIdx.x % SUB) * MR + tid / TPR, c0 = 4 * (tid % TPR);
+    const int blk = blockIdx.x / SUB;
+    const int rb = blk % p.n_rb, group = blk / p.n_rb;
     const int b = group / p.Hkv, kvh = group - b * p.Hkv;
     const int rg = 32 * rb + row;
     if (rg >= p.rows) return;
     const size_t units = (size_t)p.B * p.Hkv * p.n_rb * p.n_split;
     const size_t unit0 = ((size_t)group * p.n_rb + rb) * p.n_split;
     const float* ml = p.ws + units * 32 * D + unit0 * 64 + 2 * row;
+    const float* src0 = p.ws + unit0 * 32 * D + row * D + c0;
+    // Both passes run in split order. The partial results were written by workgroups on other
+    // XCDs (far away), so the loads of U splits are issued together before they are combined;
+    // the arithmetic, and so every bit of the result, is that of the plain loop.
+    const int ns = p.n_split;
     float ms = -INFINITY;
-    for (int s = 0; s < p.n_split; ++s) ms = fmaxf(ms, ml[64 * s]);
+#pragma unroll 8
+    for (int s = 0; s < ns; ++s) ms = fmaxf(ms, ml[64 * s]);
     float ls = 0.f;
-    float o[D / 8];
+    float o[4] = {0.f, 0.f, 0.f, 0.f};
+    auto combine = [&](float2 m_l, u32x4 v) {
+        float w = __builtin_amdgcn_exp2f(m_l.x - ms);
+        w = (ms == -INFINITY) ? 0.f : w;
+        ls = fmaf(m_l.y, w, ls);
 #pragma unroll
-    for (int c = 0; c < D / 8; ++c) o[c] = 0.f;
-    for (int s = 0; s < p.n_split; ++s) {
-        const float w = (ms == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ml[64 * s] - ms);
-        ls = fmaf(ml[64 * s + 1], w, ls);
-        const float* src = p.ws + (unit0 + s) * 32 * D + row * D + cc * (D / 8);
+        for (int e = 0; e < 4; ++e) o[e] = fmaf(__uint_as_float(v[e]), w, o[e]);
+    };
+    constexpr int U = 8;
+    int s = 0;
+    for (; s + U <= ns; s += U) {
+        float2 m_l[U];
+        u32x4 v[U];
 #pragma unroll
-        for (int c = 0; c < D / 8; c += 4) {
-            const u32x4 v = *(const u32x4*)(src + c);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) o[c + e] = fmaf(__uint_as_float(v[e]), w, o[c + e]);
+        for (int u = 0; u < U; ++u) {
+            m_l[u] = *(const float2*)(ml + 64 * (s + u));
+            v[u] = *(const u32x4*)(src0 + (size_t)(s + u) * 32 * D);
         }
+        __builtin_amdgcn_sched_barrier(0);   // every load of the batch is issued before any use
+#pragma unroll
+        for (int u = 0; u < U; ++u) combine(m_l[u], v[u]);
     }
-    store_out<D, OUT_F32>(p, b, kvh, rg, cc * (D / 8), o, ls > 0.f ? 1.f / ls : 0.f,
-                          ls > 0.f ? (ms + __builtin_amdgcn_logf(ls)) * kLn2 : -INFINITY);
+    if (s < ns) {                            // the last, partial batch, loaded the same way
+        float2 m_l[U];
+        u32x4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int su = min(s + u, ns - 1);   // past the end: re-read the last split, unused
+            m_l[u] = *(const float2*)(ml + 64 * su);
+            v[u] = *(const u32x4*)(src0 + (size_t)su * 32 * D);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (s + u < ns) combine(m_l[u], v[u]);
+    }
+    // store the 4 columns (and, from column 0, the row's log-sum-exp)
+    const float mul = ls > 0.f ? 1.f / ls : 0.f;
+    const int i = rg / p.G, hq = kvh * p.G + (rg - i * p.G);
+    const size_t orow = ((size_t)b * p.Sq + i) * p.Hq + hq;
+    if constexpr (OUT_F32) {
+        u32x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = __float_as_uint(o[e] * mul);
+        *(u32x4*)((float*)p.out + orow * D + c0) = w;
+    } else {
+        u32x2 w;
+        w[0] = pack_bf16x2(o[0] * mul, o[1] * mul);
+        w[1] = pack_bf16x2(o[2] * mul, o[3] * mul);
+        *(u32x2*)((uint16_t*)p.out + orow * D + c0) = w;
+    }
+    if (c0 == 0)
+        p.lse[((size_t)b * p.Hq + hq) * p.Sq + i] = ls > 0.f ? (ms + __builtin_amdgcn_logf(ls)) * kLn2 : -INFINITY;
 }
 
 template <int D, int MASK, int BIAS, bool OUT_F32>
@@ -369,7 +421,7 @@ static hipError_t launch_one(const DecParams& p, hipStream_t s) {
     hipLaunchKernelGGL((split_kernel<D, MASK, BIAS, OUT_F32>), dim3(grid), dim3(kThreads), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.n_split == 1) return e;
-    const unsigned gm = (unsigned)((size_t)p.B * p.Hkv * p.n_rb);
+    const unsigned gm = (unsigned)((size_t)p.B * p.Hkv * p.n_rb * (32 / merge_rows<D>()));
     hipLaunchKernelGGL((merge_kernel<D, OUT_F32>), dim3(gm), dim3(256), 0, s, p);
     return hipGetLastError();
 }
