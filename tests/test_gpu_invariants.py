@@ -69,16 +69,34 @@ def test_window1_is_v_bitwise(gpu_lib, D):
     assert torch.equal(o, dev[2].repeat_interleave(2, dim=2))
 
 
-def test_ones_value_gives_ones(gpu_lib):
+@pytest.mark.parametrize("key,D", [("c4t5", 64), ("c2", 128), ("c2d256", 256), ("c2d32", 32)])
+def test_ones_value_gives_ones(gpu_lib, key, D):
     import torch
-    wl = si.small(W["c4t5"], B=1, Hq=2, Hkv=2, Sq=300, Sk=300, name_suffix="v1")
+    wl = si.small(W[key], B=1, Hq=2, Hkv=2, Sq=300, Sk=300, name_suffix="v1").replace(D=D)
     q, k, v, bias = to_device(si.make_inputs(wl))
     v = torch.ones_like(v)
     o, _ = run_gpu(gpu_lib, wl, (q, k, v, bias), out_f32=True)
-    # P.V uses P rounded to bf16 (relative error <= 2^-9) while the normaliser sums the
-    # unrounded P, so O = sum(p_hat) / sum(p) lies within 2^-9 / (1 - 2^-9) of 1.
-    bound = 2.0 ** -9 / (1 - 2.0 ** -9) + 1e-6
-    assert torch.max(torch.abs(o - 1.0)).item() <= bound
+    o16, _ = run_gpu(gpu_lib, wl, (q, k, v, bias), out_f32=False)
+    # numerator (P.V) and normaliser both add the same bf16 weights p_hat, in fp32 and in
+    # different orders: O = 1 up to the rounding of two sums of <= 300 terms (< 3e-5), and the
+    # bf16 output is exactly 1
+    assert torch.max(torch.abs(o - 1.0)).item() <= 3e-5
+    assert torch.equal(o16, torch.ones_like(o16))
+
+
+def test_gqa_equals_mha_on_repeated_kv_bitwise(gpu_lib):
+    """Head sharing: each query head h reads KV head h // G; giving every query head its own
+    copy of that KV head (MHA on repeat_interleave'd K/V) must not change a bit."""
+    import torch
+    for key, Hq, Hkv in (("c5gqa", 8, 2), ("c5mqa", 8, 1), ("c4t5", 6, 2)):
+        wl = si.small(W[key], B=2, Hq=Hq, Hkv=Hkv, Sq=333, Sk=333, name_suffix="rep")
+        q, k, v, bias = to_device(si.make_inputs(wl))
+        G = Hq // Hkv
+        kr = k.repeat_interleave(G, dim=2).contiguous()
+        vr = v.repeat_interleave(G, dim=2).contiguous()
+        o1, l1 = run_gpu(gpu_lib, wl, (q, k, v, bias))
+        o2, l2 = run_gpu(gpu_lib, wl.replace(Hkv=Hq), (q, kr, vr, bias))
+        assert torch.equal(o1, o2) and torch.equal(l1, l2), key
 
 
 def test_zero_query_gives_visible_mean(gpu_lib):
