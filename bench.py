@@ -634,7 +634,7 @@ def main_decode(sdpa, wl: si.Workload, args) -> int:
         line["cpu_baseline"] = cpu_baseline_decode(wl)
     print(json.dumps(line), flush=True)
     if args.sweep:
-        for key in ["dec", "decmqa", "decsw"]:
+        for key in ["dec", "decmqa", "decsw", "decd256"]:
             w2 = si.WORKLOADS[key]
             t2 = time_workload(sdpa, w2, max(5, args.steps // 2), max(30, args.warmup),
                                decode=True)

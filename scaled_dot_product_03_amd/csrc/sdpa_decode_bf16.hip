@@ -9,7 +9,8 @@
 //   split_kernel : one workgroup = 4 waves = one 32-row block of the G * Sq query rows sharing
 //                  a KV head (row r = i * G + g: query row i of head kvh * G + g), and one
 //                  contiguous range of 64-key tiles. K and V tiles stream through a 4-slot LDS
-//                  ring with three tiles in flight. Wave (kh, dh) takes key half kh of every
+//                  ring with three tiles in flight (D = 256: 2 slots, one tile in flight, as
+//                  the LDS holds only two K/V tile pairs). Wave (kh, dh) takes key half kh of every
 //                  tile and head-dim half dh of O: S^T = K.Q^T (lane = query row), an online
 //                  softmax (running max m, sum l, both per row) and O^T += V^T.P^T with V^T
 //                  from transposing LDS reads. The two key halves' (m, l, O) are then combined
@@ -31,7 +32,8 @@ namespace dec {
 
 using namespace dev;
 
-constexpr int kWaves = 4, kThreads = 256, kBN = 64, kNS = 4;
+constexpr int kWaves = 4, kThreads = 256, kBN = 64;
+template <int D> constexpr int ring_slots() { return D == 256 ? 2 : 4; }
 constexpr float kLn2 = 0.6931471805599453f;
 
 // D / 8 output columns starting at col0 of query row r (= i * G + g) of (batch b, KV head kvh),
@@ -67,11 +69,14 @@ __device__ __forceinline__ void store_out(const DecParams& p, int b, int kvh, in
 // one (batch, KV head, 32-row block, key split)
 // ------------------------------------------------------------------------------------------
 template <int D, int MASK, int BIAS, bool OUT_F32>
-__global__ __launch_bounds__(256, D == 128 ? 1 : 2) void split_kernel(const DecParams p) {
+__global__ __launch_bounds__(256, D >= 128 ? 1 : 2) void split_kernel(const DecParams p) {
     constexpr int KS = D / 16, DB = D / 32, TILE = kBN * D, CH = D / 8;
     constexpr bool FB = BIAS == BIAS_FULL;
     // slot u of the ring: K tile at [2u], V tile at [2u + 1]; reused for the wave merge
-    __shared__ __attribute__((aligned(16))) uint16_t smem[kNS * 2 * TILE];
+    constexpr int kNS = ring_slots<D>();
+    // the ring, and after the last tile the buffer that merges the two key halves
+    constexpr int RING = kNS * 2 * TILE, MERGE = (kWaves * 32 * D + 4 * 32) * 2;
+    __shared__ __attribute__((aligned(16))) uint16_t smem[RING > MERGE ? RING : MERGE];
     constexpr bool IS_T5 = BIAS == BIAS_T5 || BIAS == BIAS_T5U;
     __shared__ float t5s[IS_T5 ? 32 * kT5Buckets : 1];   // [row of block][bucket]
 
@@ -239,25 +244,26 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void split_kernel(const DecP
         }
     };
 
-    // Ring of kNS = 4 tiles, three in flight: tile u + 3 is requested while tile u is computed,
-    // and each iteration waits only for tile u + 1 (the DMA requests of the two younger tiles,
-    // 2 * XPW per tile and wave, may stay outstanding).
-    static_assert(kNS == 4, "three tiles in flight");
+    // Ring of kNS tiles, F = kNS - 1 in flight: tile u + F is requested while tile u is
+    // computed, and each iteration waits only for tile u + 1 (the DMA requests of the younger
+    // tiles, 2 * XPW per tile and wave, may stay outstanding).
+    constexpr int F = kNS - 1;
+    static_assert(F >= 1 && F <= 3, "tiles in flight");
     constexpr int PT = 2 * XPW;                      // DMA requests per tile and wave
     auto wait_tile = [&](int younger) {              // younger tiles still allowed in flight
         if (younger >= 2) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * PT) : "memory");
         else if (younger == 1) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(PT) : "memory");
         else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     };
-    for (int u = 0; u < 3; ++u)
+    for (int u = 0; u < F; ++u)
         if (u < nt) dma_tile(u);
-    wait_tile(min(nt, 3) - 1);
+    wait_tile(min(nt, F) - 1);
     __syncthreads();
 #pragma unroll 1
     for (int u = 0; u < nt; ++u) {
-        if (u + 3 < nt) dma_tile(u + 3);
+        if (u + F < nt) dma_tile(u + F);
         compute(u);
-        wait_tile(min(nt - 1, u + 3) - (u + 1));
+        wait_tile(min(nt - 1, u + F) - (u + 1));
         __syncthreads();
     }
 
@@ -266,7 +272,7 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void split_kernel(const DecP
     float* obuf = (float*)smem;                      // [wave][row][D], half of D used per wave
     float* mbuf = obuf + kWaves * 32 * D;            // [key half][row]
     float* lbuf = mbuf + 2 * 32;                     // [key half][row]
-    static_assert((kWaves * 32 * D + 4 * 32) * 4 <= kNS * 2 * TILE * 2, "merge buffer");
+    static_assert((kWaves * 32 * D + 4 * 32) * 4 <= sizeof(smem), "merge buffer");
     {
         const float l_row = partner_sum(l);
         float* orow = obuf + (wave * 32 + r32) * D;
@@ -445,6 +451,8 @@ hipError_t launch_decode_bf16(DecParams p, int D, int mask, int bias, bool out_f
     p.rows = p.G * p.Sq;
     p.n_rb = dec_row_blocks(p.G, p.Sq);
     p.n_split = dec_splits(p.B, p.Hkv, p.G, p.Sq, p.Sk);
+    if (D == 256)
+        return out_f32 ? dec::launch_d<256, true>(p, mask, bias, s) : dec::launch_d<256, false>(p, mask, bias, s);
     if (D == 128)
         return out_f32 ? dec::launch_d<128, true>(p, mask, bias, s) : dec::launch_d<128, false>(p, mask, bias, s);
     if (D == 64)

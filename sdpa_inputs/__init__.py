@@ -116,6 +116,8 @@ WORKLOADS = {
                        MASK_CAUSAL, seed=6100),
     "decsw": Workload("mistral_gqa_decode_b8_q4_k32768_sliding4096", 8, 32, 8, 4, 32768, 128,
                       "bf16", MASK_SLIDING, window=4096, seed=6200),
+    "decd256": Workload("gqa_decode_d256_b16_q1_k16384", 16, 32, 8, 1, 16384, 256, "bf16",
+                        MASK_CAUSAL, seed=6300),
     # more index-generated biases: ALiBi on the Mistral GQA shape, and the
     # T5 decoder's unidirectional buckets on T5-small decoder self-attention
     "c2alibi": Workload("mistral_gqa_causal_alibi_b4_s4096", 4, 32, 8, 4096, 4096, 128, "bf16",

@@ -51,6 +51,16 @@ SMALL = [
                  mask_kind=si.MASK_NONE, bias_kind=si.BIAS_ALIBI),
     BASE.replace(name="dec_t5u_d64_q2_k3000", B=1, Hq=6, Hkv=2, Sq=2, Sk=3000, D=64,
                  bias_kind=si.BIAS_T5U),
+    # D = 256 (two-slot ring): one and several splits, several row blocks, masks and biases
+    BASE.replace(name="dec_d256_b2_g4_q1_k5000", B=2, Hq=8, Hkv=2, Sk=5000, D=256),
+    BASE.replace(name="dec_d256_q9_k3000_two_blocks", B=1, Hq=8, Hkv=1, Sq=9, Sk=3000, D=256),
+    BASE.replace(name="dec_d256_single_split_k200", B=1, Hq=4, Hkv=2, Sq=2, Sk=200, D=256),
+    BASE.replace(name="dec_d256_sliding_t5_q4_k4100", B=1, Hq=8, Hkv=2, Sq=4, Sk=4100, D=256,
+                 mask_kind=si.MASK_SLIDING, window=300, bias_kind=si.BIAS_T5),
+    BASE.replace(name="dec_d256_full_bias_none_q3_k2001", B=1, Hq=4, Hkv=2, Sq=3, Sk=2001,
+                 D=256, mask_kind=si.MASK_NONE, bias_kind=si.BIAS_FULL),
+    BASE.replace(name="dec_d256_alibi_neg_q2_k3000", B=1, Hq=8, Hkv=2, Sq=2, Sk=3000, D=256,
+                 bias_kind=si.BIAS_ALIBI, scale_override=-0.05),
 ]
 
 
@@ -90,7 +100,7 @@ def test_decode_parity_small(gpu_lib, wl):
     check(gpu_lib, wl, ref_o, ref_l)
 
 
-@pytest.mark.parametrize("key", ["dec", "decmqa", "decsw"])
+@pytest.mark.parametrize("key", ["dec", "decmqa", "decsw", "decd256"])
 def test_decode_parity_full_size_sampled(gpu_lib, key):
     """Full-size decode workload as the benchmark launches it; the oracle on sampled heads
     (all query rows of each)."""
@@ -127,8 +137,8 @@ def test_decode_bitwise_determinism_100_runs(gpu_lib):
     print(f"{wl.name}: decode deterministic over 100 runs", flush=True)
 
 
-@pytest.mark.parametrize("D", [32, 256])
-def test_decode_refuses_head_dims_outside_64_128(gpu_lib, D):
+@pytest.mark.parametrize("D", [32])
+def test_decode_refuses_head_dim_32(gpu_lib, D):
     import torch
     q = torch.zeros((1, 1, 2, D), dtype=torch.bfloat16, device="cuda")
     k = torch.zeros((1, 300, 2, D), dtype=torch.bfloat16, device="cuda")
