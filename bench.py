@@ -57,18 +57,22 @@ METRIC_BWD = ("attention bwd (dQ, dK, dV) effective TFLOP/s, 10*D flop per visib
               "(masked tiles excluded) + % of bf16 MFMA peak")
 PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0           # MI355X HBM3E, published
+# kernel sources and the C ABI (which picks the kernel variant) of each profiled path
 KERNEL_SOURCES = ["scaled_dot_product_03_amd/csrc/sdpa_fwd_bf16.hip",
-                  "scaled_dot_product_03_amd/csrc/sdpa_params.h"]
+                  "scaled_dot_product_03_amd/csrc/sdpa_params.h",
+                  "scaled_dot_product_03_amd/csrc/sdpa_api.hip"]
 TRAFFIC_FILE = "profiles/sdpa_fwd_bf16_c2_traffic.json"
 KERNEL_SOURCES_BWD = ["scaled_dot_product_03_amd/csrc/sdpa_bwd_bf16.hip",
                       "scaled_dot_product_03_amd/csrc/sdpa_device.h",
-                      "scaled_dot_product_03_amd/csrc/sdpa_params.h"]
+                      "scaled_dot_product_03_amd/csrc/sdpa_params.h",
+                      "scaled_dot_product_03_amd/csrc/sdpa_api.hip"]
 TRAFFIC_FILE_BWD = "profiles/sdpa_bwd_bf16_c2_traffic.json"
 METRIC_DEC = "attention decode HBM GB/s (visible K/V range + q, out, lse) + % of HBM peak"
 KERNEL_SOURCES_DEC = ["scaled_dot_product_03_amd/csrc/sdpa_decode_bf16.hip",
                       "scaled_dot_product_03_amd/csrc/sdpa_decode.h",
                       "scaled_dot_product_03_amd/csrc/sdpa_device.h",
-                      "scaled_dot_product_03_amd/csrc/sdpa_params.h"]
+                      "scaled_dot_product_03_amd/csrc/sdpa_params.h",
+                      "scaled_dot_product_03_amd/csrc/sdpa_api.hip"]
 TRAFFIC_FILE_DEC = "profiles/sdpa_decode_bf16_dec_traffic.json"
 
 

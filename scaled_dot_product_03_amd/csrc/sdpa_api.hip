@@ -56,6 +56,14 @@ int validate(const void* q, const void* k, const void* v, const void* out, const
     return SDPA_OK;
 }
 
+// The mask kind the kernels run. A sliding window at least as wide as the key range hides
+// nothing the causal mask shows (a visible key has pos - j <= Sk - 1 < window), so it runs the
+// causal kernels: exactly the causal result and the causal speed, which the transformers issue
+// on the SDPA mask fix asks of a window equal to the sequence length.
+int kernel_mask(int mask_kind, int window, int Sk) {
+    return (mask_kind == SDPA_MASK_SLIDING && window >= Sk) ? SDPA_MASK_CAUSAL : mask_kind;
+}
+
 sdpa::FwdParams make_params(const void* q, const void* k, const void* v, void* out, float* lse,
                             int B, int Hq, int Hkv, int Sq, int Sk, float scale, int mask_kind,
                             int window, const void* bias_tbl) {
@@ -133,7 +141,7 @@ int decode_common(const void* q, const void* k, const void* v, void* out, float*
     p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.Sq = Sq; p.Sk = Sk;
     p.G = f.G; p.off = f.off; p.window = f.window;
     p.scale = f.scale; p.scale_log2 = f.scale_log2;
-    hipError_t e = sdpa::launch_decode_bf16(p, D, mask_kind, bias_kind, out_f32,
+    hipError_t e = sdpa::launch_decode_bf16(p, D, kernel_mask(mask_kind, window, Sk), bias_kind, out_f32,
                                             (hipStream_t)stream);
     return e == hipSuccess ? SDPA_OK : SDPA_ERR_LAUNCH;
 }
@@ -158,7 +166,8 @@ int varlen_common(const void* q, const void* k, const void* v, void* out, float*
     p.cu_k = cu_k;
     p.total_q = total_q;
     p.total_k = total_k;
-    hipError_t e = sdpa::launch_fwd_bf16(p, D, mask_kind, bias_kind, out_f32, (hipStream_t)stream);
+    hipError_t e = sdpa::launch_fwd_bf16(p, D, kernel_mask(mask_kind, window, max_k), bias_kind, out_f32,
+                                         (hipStream_t)stream);
     return e == hipSuccess ? SDPA_OK : SDPA_ERR_LAUNCH;
 }
 
@@ -214,7 +223,8 @@ int sdpa_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
     if (st != SDPA_OK) return st;
     sdpa::FwdParams p = make_params(q, k, v, out, lse, B, Hq, Hkv, Sq, Sk, scale, mask_kind,
                                     window, bias_tbl);
-    hipError_t e = sdpa::launch_fwd_bf16(p, D, mask_kind, bias_kind, false, (hipStream_t)stream);
+    hipError_t e = sdpa::launch_fwd_bf16(p, D, kernel_mask(mask_kind, window, Sk), bias_kind, false,
+                                         (hipStream_t)stream);
     return e == hipSuccess ? SDPA_OK : SDPA_ERR_LAUNCH;
 }
 
@@ -227,7 +237,8 @@ int sdpa_fwd_bf16_f32out(const void* q, const void* k, const void* v, float* out
     if (st != SDPA_OK) return st;
     sdpa::FwdParams p = make_params(q, k, v, out, lse, B, Hq, Hkv, Sq, Sk, scale, mask_kind,
                                     window, bias_tbl);
-    hipError_t e = sdpa::launch_fwd_bf16(p, D, mask_kind, bias_kind, true, (hipStream_t)stream);
+    hipError_t e = sdpa::launch_fwd_bf16(p, D, kernel_mask(mask_kind, window, Sk), bias_kind, true,
+                                         (hipStream_t)stream);
     return e == hipSuccess ? SDPA_OK : SDPA_ERR_LAUNCH;
 }
 
@@ -239,7 +250,7 @@ int sdpa_fwd_f32(const float* q, const float* k, const float* v, float* out, flo
     if (st != SDPA_OK) return st;
     sdpa::FwdParams p = make_params(q, k, v, out, lse, B, Hq, Hkv, Sq, Sk, scale, mask_kind,
                                     window, bias_tbl);
-    hipError_t e = sdpa::launch_fwd_f32(p, D, mask_kind, bias_kind, (hipStream_t)stream);
+    hipError_t e = sdpa::launch_fwd_f32(p, D, kernel_mask(mask_kind, window, Sk), bias_kind, (hipStream_t)stream);
     return e == hipSuccess ? SDPA_OK : SDPA_ERR_LAUNCH;
 }
 
@@ -252,7 +263,8 @@ int sdpa_bwd(const void* q, const void* k, const void* v, const void* out, const
     if (st != SDPA_OK) return st;
     sdpa::BwdParams p = make_bwd_params(q, k, v, out, lse, dout, dq, dk, dv, ws, B, Hq, Hkv, Sq,
                                         Sk, scale, mask_kind, window, bias_tbl);
-    hipError_t e = sdpa::launch_bwd_bf16(p, D, mask_kind, bias_kind, false, (hipStream_t)stream);
+    hipError_t e = sdpa::launch_bwd_bf16(p, D, kernel_mask(mask_kind, window, Sk), bias_kind, false,
+                                         (hipStream_t)stream);
     return e == hipSuccess ? SDPA_OK : SDPA_ERR_LAUNCH;
 }
 
@@ -266,7 +278,8 @@ int sdpa_bwd_f32out(const void* q, const void* k, const void* v, const void* out
     if (st != SDPA_OK) return st;
     sdpa::BwdParams p = make_bwd_params(q, k, v, out, lse, dout, dq, dk, dv, ws, B, Hq, Hkv, Sq,
                                         Sk, scale, mask_kind, window, bias_tbl);
-    hipError_t e = sdpa::launch_bwd_bf16(p, D, mask_kind, bias_kind, true, (hipStream_t)stream);
+    hipError_t e = sdpa::launch_bwd_bf16(p, D, kernel_mask(mask_kind, window, Sk), bias_kind, true,
+                                         (hipStream_t)stream);
     return e == hipSuccess ? SDPA_OK : SDPA_ERR_LAUNCH;
 }
 
