@@ -138,9 +138,11 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(const BwdParams p) {
         lse2 = (l == -INFINITY) ? INFINITY : l * kLog2e;
     }
 
-    // K and V tiles: 64 keys x D, row-major, swizzled chunks; 2 slots each
-    constexpr int ROWS_PER_XFER = 1024 / (D * 2), XFERS = (kBN * D * 2) / 1024, XPW = XFERS / kWaves;
-    static_assert(XPW * kWaves == XFERS, "dma split");
+    // K and V tiles: 64 keys x D, row-major, swizzled chunks; 2 slots each. The 1 KB transfers
+    // of a tile are spread over the waves (at D = 32 a tile is 4 transfers: waves 0-3 issue).
+    constexpr int ROWS_PER_XFER = 1024 / (D * 2), XFERS = (kBN * D * 2) / 1024;
+    constexpr int XPW = XFERS >= kWaves ? XFERS / kWaves : 1, NXW = XFERS / XPW;
+    static_assert(XPW * NXW == XFERS && NXW <= kWaves, "dma split");
     const uint32_t lds_base = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint16_t*)smem);
     // A full bias goes through LDS when its rows split into whole 16-byte chunks: tile
     // [256 rows][64 keys], 128-byte rows, chunk swizzle (row >> 1) & 7; keys past the end of a
@@ -151,14 +153,16 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(const BwdParams p) {
                              : nullptr;
     auto dma_tile = [&](int t) {
         const int sl = (t - t_begin) & 1, j0 = t * kBN;
+        if (NXW == kWaves || wave < NXW) {
 #pragma unroll
-        for (int n = 0; n < XPW; ++n) {
-            const int xi = wave * XPW + n;
-            const int row = xi * ROWS_PER_XFER + lane / CH;
-            const int j = min(j0 + row, Sk - 1);
-            const int ch = ((lane % CH) ^ swz<D>(row)) * 8;
-            dma16(kg + (size_t)j * kv_row + ch, lds_base + (uint32_t)((sl * TILE) * 2 + xi * 1024));
-            dma16(vg + (size_t)j * kv_row + ch, lds_base + (uint32_t)(((2 + sl) * TILE) * 2 + xi * 1024));
+            for (int n = 0; n < XPW; ++n) {
+                const int xi = wave * XPW + n;
+                const int row = xi * ROWS_PER_XFER + lane / CH;
+                const int j = min(j0 + row, Sk - 1);
+                const int ch = ((lane % CH) ^ swz<D>(row)) * 8;
+                dma16(kg + (size_t)j * kv_row + ch, lds_base + (uint32_t)((sl * TILE) * 2 + xi * 1024));
+                dma16(vg + (size_t)j * kv_row + ch, lds_base + (uint32_t)(((2 + sl) * TILE) * 2 + xi * 1024));
+            }
         }
         if constexpr (FB) {
             if (fb_dma) {
@@ -685,6 +689,8 @@ hipError_t launch_bwd_bf16(BwdParams p, int D, int mask, int bias, bool out_f32,
         return out_f32 ? bwd::launch_d<128, true>(p, mask, bias, s) : bwd::launch_d<128, false>(p, mask, bias, s);
     if (D == 64)
         return out_f32 ? bwd::launch_d<64, true>(p, mask, bias, s) : bwd::launch_d<64, false>(p, mask, bias, s);
+    if (D == 32)
+        return out_f32 ? bwd::launch_d<32, true>(p, mask, bias, s) : bwd::launch_d<32, false>(p, mask, bias, s);
     return hipErrorInvalidValue;
 }
 

@@ -31,11 +31,14 @@ __device__ __forceinline__ int perm32(int r) {
 // consecutive rows, chunks c + {0, 1, 2DB, 2DB + 1}). Row bits 0-1 (D = 128) or bit 1 (D = 64,
 // two rows per 256-byte bank line) pick distinct chunk pairs for the transposing reads; row
 // bits 2 and 4 fill the remaining swizzle bits so the 16 rows of a row-wise read land on 16
-// distinct chunks of the bank line.
+// distinct chunks of the bank line. D = 32 rows are 4 chunks (four rows per bank line): the
+// pattern takes row bits 2 and 4 and stays inside the row. D = 256 uses the D = 64 pattern.
 template <int D>
 __device__ __forceinline__ int swz(int row) {
     if constexpr (D == 128)
         return (2 * (row & 3)) | ((row >> 4) & 1) | (((row >> 2) & 1) << 3);
+    else if constexpr (D == 32)
+        return ((row >> 2) & 1) | (((row >> 4) & 1) << 1);
     else
         return (row & 2) | ((row >> 4) & 1) | (((row >> 2) & 1) << 2);
 }
