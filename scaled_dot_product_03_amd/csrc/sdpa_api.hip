@@ -114,7 +114,7 @@ sdpa::BwdParams make_bwd_params(const void* q, const void* k, const void* v, con
 
 bool dec_shape_ok(int B, int Hq, int Hkv, int Sq, int Sk, int D) {
     return B >= 1 && Hq >= 1 && Hkv >= 1 && Sq >= 1 && Sk >= 1 && Hq % Hkv == 0 &&
-           (D == 64 || D == 128 || D == 256) && (long long)Sq * (Hq / Hkv) < (1LL << 30);
+           (D == 32 || D == 64 || D == 128 || D == 256) && (long long)Sq * (Hq / Hkv) < (1LL << 30);
 }
 
 int decode_common(const void* q, const void* k, const void* v, void* out, float* lse, void* ws,
@@ -124,7 +124,6 @@ int decode_common(const void* q, const void* k, const void* v, void* out, float*
     int st = validate(q, k, v, out, lse, B, Hq, Hkv, Sq, Sk, D, scale, mask_kind, window,
                       bias_kind, bias_tbl, 2);
     if (st != SDPA_OK) return st;
-    if (D == 32) return SDPA_ERR_HEADDIM;   // decode kernels: D = 64, 128 and 256
     const int G = Hq / Hkv;
     if ((long long)Sq * G >= (1LL << 30)) return SDPA_ERR_SHAPE;
     // grids: split kernel B * Hkv * row blocks * splits, merge kernel up to 4 per row block
@@ -289,7 +288,7 @@ const char* sdpa_status_str(int status) {
         case SDPA_ERR_NULL: return "a required pointer is NULL";
         case SDPA_ERR_SHAPE: return "invalid or too large shape (B, Hq, Hkv, Sq, Sk)";
         case SDPA_ERR_HEADS: return "Hq is not a multiple of Hkv";
-        case SDPA_ERR_HEADDIM: return "head dim D must be 32, 64, 128 or 256 (not 256 for gradients, not 32 for decode)";
+        case SDPA_ERR_HEADDIM: return "head dim D must be 32, 64, 128 or 256 (not 256 for gradients)";
         case SDPA_ERR_MASK: return "unknown mask_kind";
         case SDPA_ERR_WINDOW: return "sliding window must be >= 1";
         case SDPA_ERR_BIAS: return "unknown bias_kind or bias_tbl inconsistent with it";

@@ -52,7 +52,7 @@ __device__ __forceinline__ void store_out(const DecParams& p, int b, int kvh, in
             for (int e = 0; e < 4; ++e) w[e] = __float_as_uint(o[c + e] * mul);
             *(u32x4*)(dst + c) = w;
         }
-    } else {
+    } else if constexpr (D / 8 >= 8) {
         uint16_t* dst = (uint16_t*)p.out + row * D + col0;
 #pragma unroll
         for (int c = 0; c < D / 8; c += 8) {
@@ -61,6 +61,12 @@ __device__ __forceinline__ void store_out(const DecParams& p, int b, int kvh, in
             for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(o[c + 2 * e] * mul, o[c + 2 * e + 1] * mul);
             *(u32x4*)(dst + c) = w;
         }
+    } else {                                         // D = 32: 4 columns
+        uint16_t* dst = (uint16_t*)p.out + row * D + col0;
+        u32x2 w;
+        w[0] = pack_bf16x2(o[0] * mul, o[1] * mul);
+        w[1] = pack_bf16x2(o[2] * mul, o[3] * mul);
+        *(u32x2*)dst = w;
     }
     if (col0 == 0) p.lse[((size_t)b * p.Hq + hq) * p.Sq + i] = lse;
 }
@@ -161,8 +167,10 @@ __global__ __launch_bounds__(256, D >= 128 ? 1 : 2) void split_kernel(const DecP
     // Each 64-key tile is computed by all four waves: wave (kh, dh) takes key half kh and
     // accumulates the head dims of fragment half dh, so both waves of a key half form the same
     // S and P (same instructions). Running state of this wave's rows: max m (log2 units), this
-    // lane half's part of the sum l, and its half of O^T (head dims x rows).
-    constexpr int DH = DB / 2;
+    // lane half's part of the sum l, and its half of O^T (head dims x rows). At D = 32 there is
+    // one fragment: the dh = 0 waves accumulate it, the dh = 1 waves only follow the softmax.
+    constexpr int DH = DB > 1 ? DB / 2 : 1;
+    constexpr bool ONE = DB == 1;
     const int kh = wave & 1, dh = wave >> 1;
     float m = -INFINITY, l = 0.f;
     f32x16 acc[DH];
@@ -237,10 +245,12 @@ __global__ __launch_bounds__(256, D >= 128 ? 1 : 2) void split_kernel(const DecP
             for (int c = 0; c < 4; ++c) pk[c] = pack_bf16x2(x[8 * sg + 2 * c], x[8 * sg + 2 * c + 1]);
             bf16x8 vt[DB];
             read_tr<D>(vb, 2 * kh + sg, lane, vt);
+            if (!ONE || dh == 0) {
 #pragma unroll
-            for (int db = 0; db < DH; ++db)
-                acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dh ? vt[DH + db] : vt[db],
-                                                                  __builtin_bit_cast(bf16x8, pk), acc[db], 0, 0, 0);
+                for (int db = 0; db < DH; ++db)
+                    acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16((!ONE && dh) ? vt[DH + db] : vt[db],
+                                                                      __builtin_bit_cast(bf16x8, pk), acc[db], 0, 0, 0);
+            }
         }
     };
 
@@ -277,7 +287,7 @@ __global__ __launch_bounds__(256, D >= 128 ? 1 : 2) void split_kernel(const DecP
         const float l_row = partner_sum(l);
         float* orow = obuf + (wave * 32 + r32) * D;
 #pragma unroll
-        for (int q = 0; q < DH; ++q) {
+        for (int q = 0; q < ((!ONE || dh == 0) ? DH : 0); ++q) {
             const int db = dh * DH + q;
             const int d0[2] = {16 * db + 8 * hh, 16 * (db + DB) + 8 * hh};
 #pragma unroll
@@ -457,6 +467,8 @@ hipError_t launch_decode_bf16(DecParams p, int D, int mask, int bias, bool out_f
         return out_f32 ? dec::launch_d<128, true>(p, mask, bias, s) : dec::launch_d<128, false>(p, mask, bias, s);
     if (D == 64)
         return out_f32 ? dec::launch_d<64, true>(p, mask, bias, s) : dec::launch_d<64, false>(p, mask, bias, s);
+    if (D == 32)
+        return out_f32 ? dec::launch_d<32, true>(p, mask, bias, s) : dec::launch_d<32, false>(p, mask, bias, s);
     return hipErrorInvalidValue;
 }
 

@@ -125,10 +125,10 @@ def call_bwd(entry="sdpa_bwd", **kw):
                              a["bias_kind"], a["bias"], a["stream"])
 
 
-# the gradient kernels cover D = 32, 64 and 128, decode D = 64, 128 and 256
-NARROW_D = [("D=32 (no decode)", dict(D=32), 4), ("D=256 (no gradients)", dict(D=256), 4)]
+# the gradient kernels cover D = 32, 64 and 128
+NARROW_D = [("D=256 (no gradients)", dict(D=256), 4)]
 
-BWD_CASES = BAD_CASES + NARROW_D[1:] + [
+BWD_CASES = BAD_CASES + NARROW_D + [
     ("null dout", dict(dout=None), 1),
     ("null dq", dict(dq=None), 1),
     ("null dk", dict(dk=None), 1),
@@ -166,7 +166,7 @@ def call_dec(entry="sdpa_decode", **kw):
                                 a["bias_kind"], a["bias"], a["stream"])
 
 
-DEC_CASES = BAD_CASES + NARROW_D[:1] + [
+DEC_CASES = BAD_CASES + [
     ("null ws", dict(ws=None), 11),
     ("misaligned ws", dict(ws=P + 8), 11),
     ("small ws", dict(ws_bytes=16), 11),
@@ -187,7 +187,7 @@ def test_decode_workspace_size(lib):
     assert units % (16 * 8) == 0
     assert sdpa.decode_ws_bytes(1, 6, 4, 1, 100, 128) == 0
     assert sdpa.decode_ws_bytes(1, 8, 8, 1, 100, 96) == 0
-    assert sdpa.decode_ws_bytes(1, 8, 8, 1, 100, 32) == 0
+    assert sdpa.decode_ws_bytes(1, 8, 8, 1, 100, 32) > 0
     assert sdpa.decode_ws_bytes(1, 8, 8, 1, 100, 256) > 0
     # the exact requirement is accepted, one byte less is not (validation only, no launch)
     need = sdpa.decode_ws_bytes(1, 4, 2, 8, 8, 64)

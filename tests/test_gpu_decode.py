@@ -61,6 +61,14 @@ SMALL = [
                  D=256, mask_kind=si.MASK_NONE, bias_kind=si.BIAS_FULL),
     BASE.replace(name="dec_d256_alibi_neg_q2_k3000", B=1, Hq=8, Hkv=2, Sq=2, Sk=3000, D=256,
                  bias_kind=si.BIAS_ALIBI, scale_override=-0.05),
+    # D = 32 (one head-dim fragment)
+    BASE.replace(name="dec_d32_b2_g4_q1_k5000", B=2, Hq=8, Hkv=2, Sk=5000, D=32),
+    BASE.replace(name="dec_d32_q9_k3000_two_blocks", B=1, Hq=8, Hkv=1, Sq=9, Sk=3000, D=32),
+    BASE.replace(name="dec_d32_single_split_k200", B=1, Hq=4, Hkv=2, Sq=2, Sk=200, D=32),
+    BASE.replace(name="dec_d32_sliding_t5u_q4_k4100", B=1, Hq=8, Hkv=2, Sq=4, Sk=4100, D=32,
+                 mask_kind=si.MASK_SLIDING, window=300, bias_kind=si.BIAS_T5U),
+    BASE.replace(name="dec_d32_full_bias_none_q3_k2001", B=1, Hq=4, Hkv=2, Sq=3, Sk=2001,
+                 D=32, mask_kind=si.MASK_NONE, bias_kind=si.BIAS_FULL),
 ]
 
 
@@ -136,12 +144,3 @@ def test_decode_bitwise_determinism_100_runs(gpu_lib):
     torch.cuda.synchronize()
     print(f"{wl.name}: decode deterministic over 100 runs", flush=True)
 
-
-@pytest.mark.parametrize("D", [32])
-def test_decode_refuses_head_dim_32(gpu_lib, D):
-    import torch
-    q = torch.zeros((1, 1, 2, D), dtype=torch.bfloat16, device="cuda")
-    k = torch.zeros((1, 300, 2, D), dtype=torch.bfloat16, device="cuda")
-    with pytest.raises(gpu_lib.SdpaError) as e:
-        gpu_lib.decode(q, k, k)
-    assert e.value.status == 4
