@@ -687,7 +687,7 @@ def main_bwd(sdpa, wl: si.Workload, args) -> int:
     print(json.dumps(line), flush=True)
     if args.sweep:
         for key in ["c2", "c3", "c3c", "c4t5", "c4full", "c5mha", "c5gqa", "c5mqa", "c2alibi",
-                    "c4t5u", "c2d32"]:
+                    "c4t5u", "c2d32", "c2d256"]:
             w2 = si.WORKLOADS[key]
             t2 = time_workload(sdpa, w2, max(5, args.steps // 2), max(30, args.warmup), bwd=True)
             f2, a2 = report(w2, t2, bwd=True)

@@ -53,9 +53,8 @@
  *     given shape (fixed tile shape chosen from the shape alone, fixed key order, no atomics),
  *     the determinism the transformers issue "Transformer models are not deterministic when
  *     using Flash Attention 2" asks of a fused kernel.
- *   - Validation: B, Hq, Hkv, Sq, Sk >= 1; Hq % Hkv == 0; D in {32, 64, 128, 256} for the
- *     forward entry points (the head-dim sweep the "jax-gpu-05-attention-gpu" codelab closes
- *     with), D in {32, 64, 128} for sdpa_bwd*; scale finite;
+ *   - Validation: B, Hq, Hkv, Sq, Sk >= 1; Hq % Hkv == 0; D in {32, 64, 128, 256} (the
+ *     head-dim sweep the "jax-gpu-05-attention-gpu" codelab closes with); scale finite;
  *     SLIDING needs window >= 1; bias_tbl non-NULL iff bias_kind != NONE; B*Hq*Sq*D,
  *     B*Hkv*Sk*D (and B*Hq*Sq*Sk for a full bias) below 2^40 elements.
  */
@@ -80,7 +79,7 @@ enum sdpa_status {
     SDPA_ERR_NULL = 1,      /* a required pointer is NULL */
     SDPA_ERR_SHAPE = 2,     /* B, Hq, Hkv, Sq or Sk < 1, or a tensor too large */
     SDPA_ERR_HEADS = 3,     /* Hq not a multiple of Hkv */
-    SDPA_ERR_HEADDIM = 4,   /* D not in {32, 64, 128, 256} (no 256: gradients) */
+    SDPA_ERR_HEADDIM = 4,   /* D not in {32, 64, 128, 256} */
     SDPA_ERR_MASK = 5,      /* unknown mask_kind */
     SDPA_ERR_WINDOW = 6,    /* SLIDING with window < 1 */
     SDPA_ERR_BIAS = 7,      /* unknown bias_kind, or bias_tbl NULL/non-NULL against it */

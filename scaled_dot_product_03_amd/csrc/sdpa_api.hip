@@ -88,9 +88,8 @@ int validate_bwd(const void* q, const void* k, const void* v, const void* out,
     int st = validate(q, k, v, out, lse, B, Hq, Hkv, Sq, Sk, D, scale, mask_kind, window,
                       bias_kind, bias_tbl, 2);
     if (st != SDPA_OK) return st;
-    if (D == 256) return SDPA_ERR_HEADDIM;   // gradient kernels: D = 32, 64 and 128
-    // grid of the dK/dV kernel: one workgroup per 128 keys of each (b, KV head)
-    if ((long long)B * Hkv * ((Sk + 127) / 128) >= (1LL << 31)) return SDPA_ERR_SHAPE;
+    // grid of the dK/dV kernel: one workgroup per 128 keys (64 at D = 256) of each (b, KV head)
+    if ((long long)B * Hkv * ((Sk + 63) / 64) >= (1LL << 31)) return SDPA_ERR_SHAPE;
     if (!aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
         !aligned(ws, 4))
         return SDPA_ERR_ALIGN;
@@ -288,7 +287,7 @@ const char* sdpa_status_str(int status) {
         case SDPA_ERR_NULL: return "a required pointer is NULL";
         case SDPA_ERR_SHAPE: return "invalid or too large shape (B, Hq, Hkv, Sq, Sk)";
         case SDPA_ERR_HEADS: return "Hq is not a multiple of Hkv";
-        case SDPA_ERR_HEADDIM: return "head dim D must be 32, 64, 128 or 256 (not 256 for gradients)";
+        case SDPA_ERR_HEADDIM: return "head dim D must be 32, 64, 128 or 256";
         case SDPA_ERR_MASK: return "unknown mask_kind";
         case SDPA_ERR_WINDOW: return "sliding window must be >= 1";
         case SDPA_ERR_BIAS: return "unknown bias_kind or bias_tbl inconsistent with it";

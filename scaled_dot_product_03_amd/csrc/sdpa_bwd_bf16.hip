@@ -41,18 +41,24 @@ using namespace dev;
 // ------------------------------------------------------------------------------------------
 // dQ: 256 query rows per workgroup, 64-key tiles
 // ------------------------------------------------------------------------------------------
+// waves per workgroup: 8 (two per SIMD); at D = 256 a wave needs the whole register file, so 4
+template <int D> constexpr int bwd_waves() { return D == 256 ? 4 : 8; }
+
 template <int D, int MASK, int BIAS, bool OUT_F32>
-__global__ __launch_bounds__(512, 1) void dq_kernel(const BwdParams p) {
-    constexpr int kWaves = 8, kThreads = 512, kBM = 256, kBN = 64;
+__global__ __launch_bounds__(64 * bwd_waves<D>(), 1) void dq_kernel(const BwdParams p) {
+    constexpr int kWaves = bwd_waves<D>(), kThreads = 64 * kWaves, kBM = 32 * kWaves, kBN = 64;
     constexpr int CH = D / 8, KS = D / 16, DB = D / 32, TILE = kBN * D;
     constexpr bool FB = BIAS == BIAS_FULL;
     constexpr bool IS_T5 = BIAS == BIAS_T5 || BIAS == BIAS_T5U;
     constexpr bool ALIBI = BIAS == BIAS_ALIBI;
     constexpr int kSat = BIAS == BIAS_T5U ? kT5USat : kT5Sat;
     constexpr int kT5Pad = kSat + kBN + 31;
-    constexpr int BTILE = kBM * kBN;                 // full-bias tile: 256 rows x 64 keys
+    // full-bias tile: kBM rows x 64 keys through LDS (at D = 256 the K/V slots fill the LDS: the
+    // bias is read from HBM by each lane)
+    constexpr bool FB_LDS = FB && D != 256;
+    constexpr int BTILE = FB_LDS ? kBM * kBN : 0;
     // K slots 0-1, V slots 2-3, then (full bias) two bias slots
-    __shared__ __attribute__((aligned(16))) uint16_t smem[4 * TILE + (FB ? 2 * BTILE : 0)];
+    __shared__ __attribute__((aligned(16))) uint16_t smem[4 * TILE + 2 * BTILE];
     __shared__ float t5s[IS_T5 ? 2 * kT5Pad + 1 : 1];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -147,8 +153,8 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(const BwdParams p) {
     // A full bias goes through LDS when its rows split into whole 16-byte chunks: tile
     // [256 rows][64 keys], 128-byte rows, chunk swizzle (row >> 1) & 7; keys past the end of a
     // partial last tile re-read the last whole chunk (they are masked).
-    const bool fb_dma = FB && ((Sk & 7) == 0);
-    constexpr int XPB = FB ? (BTILE * 2 / 1024) / kWaves : 0;
+    const bool fb_dma = FB_LDS && ((Sk & 7) == 0);
+    constexpr int XPB = FB_LDS ? (BTILE * 2 / 1024) / kWaves : 0;
     const uint16_t* fbg = FB ? (const uint16_t*)p.bias + ((size_t)b * p.Hq + hq) * (size_t)Sq * Sk
                              : nullptr;
     auto dma_tile = [&](int t) {
@@ -164,7 +170,7 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(const BwdParams p) {
                 dma16(vg + (size_t)j * kv_row + ch, lds_base + (uint32_t)(((2 + sl) * TILE) * 2 + xi * 1024));
             }
         }
-        if constexpr (FB) {
+        if constexpr (FB_LDS) {
             if (fb_dma) {
                 const int nchunk = min(kBN, Sk - j0) / 8;
 #pragma unroll
@@ -244,7 +250,7 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(const BwdParams p) {
                     for (int v = 0; v < 16; ++v) x[v] = fmaf(s[v], c_scale, bconst);
                 }
             } else if constexpr (FB) {
-                if (fb_dma) {
+                if (FB_LDS && fb_dma) {
                     // 16 keys from two chunks of this lane's bias row in LDS
                     const int lr = wave * 32 + r32, c0 = 4 * jb + 2 * hh, sw = (lr >> 1) & 7;
                     const uint16_t* brow = smem + 4 * TILE + sl * BTILE + lr * kBN;
@@ -323,25 +329,28 @@ __global__ __launch_bounds__(512, 1) void dq_kernel(const BwdParams p) {
 // same instructions (so their P agree bit for bit); the dK waves also form dP = dO.V^T.
 // ------------------------------------------------------------------------------------------
 template <int D, int MASK, int BIAS, bool OUT_F32>
-__global__ __launch_bounds__(512, 1) void dkdv_kernel(const BwdParams p) {
+__global__ __launch_bounds__(64 * bwd_waves<D>(), 1) void dkdv_kernel(const BwdParams p) {
     constexpr bool FB = BIAS == BIAS_FULL;
-    // 128 query rows per step; 64 with a full bias at D = 128 (its tiles share the LDS)
-    constexpr int kWaves = 8, kThreads = 512, kBK = 128, kBQ = (FB && D == 128) ? 64 : 128;
+    // keys per workgroup: 32 per dV / dK wave pair; query rows per step: 128 (64 with a full bias
+    // at D = 128, and at D = 256, whose tiles share the LDS)
+    constexpr int kWaves = bwd_waves<D>(), kThreads = 64 * kWaves, kBK = 32 * (kWaves / 2);
+    constexpr int kBQ = ((FB && D == 128) || D == 256) ? 64 : 128;
+    constexpr bool FB_LDS = FB && D != 256;      // D = 256: each lane reads its bias from HBM
     constexpr int NB = kBQ / 32;
-    constexpr int CH = D / 8, KS = D / 16, DB = D / 32, QT = kBQ * D, BTILE = kBQ * kBK;
+    constexpr int CH = D / 8, KS = D / 16, DB = D / 32, QT = kBQ * D, BTILE = FB_LDS ? kBQ * kBK : 0;
     constexpr bool IS_T5 = BIAS == BIAS_T5 || BIAS == BIAS_T5U;
     constexpr bool ALIBI = BIAS == BIAS_ALIBI;
     constexpr int kSat = BIAS == BIAS_T5U ? kT5USat : kT5Sat;
     constexpr int kT5Pad = kSat + 64 + 31;
     // LDS: slot sl holds the Q tile at [2 sl] and the dO tile at [2 sl + 1] (kBQ rows each),
     // then (full bias) two bias slots of kBQ rows x 128 keys
-    __shared__ __attribute__((aligned(16))) uint16_t smem[4 * QT + (FB ? 2 * BTILE : 0)];
+    __shared__ __attribute__((aligned(16))) uint16_t smem[4 * QT + 2 * BTILE];
     __shared__ __attribute__((aligned(16))) float rowc[2][2][kBQ];    // [slot][lse2, D][row]
     __shared__ float t5s[IS_T5 ? 2 * kT5Pad + 1 : 1];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int hh = lane >> 5, r32 = lane & 31;
-    const bool role_dk = uniform(wave >= 4);
+    const bool role_dk = uniform(wave >= kWaves / 2);
     // workgroup -> (batch, KV head, key tile); with xcd_remap all key tiles of one (batch,
     // KV head) run on one XCD (workgroup x is dispatched to XCD x % 8), where they share the
     // Q / dO rows in that XCD's L2
@@ -360,7 +369,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(const BwdParams p) {
     const int b = group / p.Hkv, kvh = group - b * p.Hkv;
     const int Sq = p.Sq, Sk = p.Sk, off = p.off, G = p.G;
     const int k0 = kt_idx * kBK;
-    const int kw0 = k0 + 32 * (wave & 3);      // first key of this wave
+    const int kw0 = k0 + 32 * (wave % (kWaves / 2));   // first key of this wave
     const int my_j = kw0 + r32;                // key of this lane
     const bool key_ok = my_j < Sk;
     const bool wave_ok = kw0 < Sk;
@@ -394,8 +403,8 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(const BwdParams p) {
     // A full bias goes through LDS when its rows split into whole 16-byte chunks: tile
     // [kBQ rows][128 keys], 256-byte rows, chunk swizzle 4 * ((row >> 4) & 1); keys past the end
     // of a partial last tile re-read the last whole chunk (they are masked).
-    const bool fb_dma = FB && ((Sk & 7) == 0);
-    constexpr int XPB = FB ? (BTILE * 2 / 1024) / kWaves : 0;
+    const bool fb_dma = FB_LDS && ((Sk & 7) == 0);
+    constexpr int XPB = FB_LDS ? (BTILE * 2 / 1024) / kWaves : 0;
     auto issue_step = [&](int n) {
         const int sl = n & 1;
         const int h = kvh * G + n / nqs;
@@ -411,7 +420,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(const BwdParams p) {
             dma16(qg + (size_t)i * q_row + ch, lds_base + (uint32_t)((2 * sl) * QT * 2 + xi * 1024));
             dma16(dg + (size_t)i * q_row + ch, lds_base + (uint32_t)((2 * sl + 1) * QT * 2 + xi * 1024));
         }
-        if constexpr (FB) {
+        if constexpr (FB_LDS) {
             if (fb_dma) {
                 const uint16_t* bg = (const uint16_t*)p.bias + ((size_t)b * p.Hq + h) * (size_t)Sq * Sk;
                 const int nchunk = min(kBK, Sk - k0) / 8;
@@ -545,7 +554,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(const BwdParams p) {
                     for (int v = 0; v < 16; ++v) x[v] = fmaf(s[v], c_scale, bconst);
                 }
             } else if constexpr (FB) {
-                if (fb_dma) {
+                if (FB_LDS && fb_dma) {
                     // column my_j of rows rl .. rl + 15 of the bias tile (row bit 4 = hh)
                     const int kk = my_j - k0;
                     const uint16_t* bcol = smem + 4 * QT + SL * BTILE + rl * kBK +
@@ -658,16 +667,19 @@ __global__ __launch_bounds__(512, 1) void dkdv_kernel(const BwdParams p) {
 template <int D, int MASK, int BIAS, bool OUT_F32>
 static hipError_t launch_grads(const BwdParams& p, hipStream_t s) {
     const unsigned gq = (unsigned)((size_t)p.B * p.Hq * p.n_qt);
-    hipLaunchKernelGGL((dq_kernel<D, MASK, BIAS, OUT_F32>), dim3(gq), dim3(512), 0, s, p);
+    hipLaunchKernelGGL((dq_kernel<D, MASK, BIAS, OUT_F32>), dim3(gq), dim3(64 * bwd_waves<D>()), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const unsigned gk = (unsigned)((size_t)p.B * p.Hkv * p.n_kt);
-    hipLaunchKernelGGL((dkdv_kernel<D, MASK, BIAS, OUT_F32>), dim3(gk), dim3(512), 0, s, p);
+    hipLaunchKernelGGL((dkdv_kernel<D, MASK, BIAS, OUT_F32>), dim3(gk), dim3(64 * bwd_waves<D>()), 0, s, p);
     return hipGetLastError();
 }
 
 template <int D, bool OUT_F32>
-static hipError_t launch_d(const BwdParams& p, int mask, int bias, hipStream_t s) {
+static hipError_t launch_d(BwdParams p, int mask, int bias, hipStream_t s) {
+    // dQ work items of 32 rows per wave, dK/dV work items of 32 keys per wave pair
+    p.n_qt = (p.Sq + 32 * bwd_waves<D>() - 1) / (32 * bwd_waves<D>());
+    p.n_kt = (p.Sk + 16 * bwd_waves<D>() - 1) / (16 * bwd_waves<D>());
 #define SDPA_CASE(M, Bk) \
     if (mask == M && bias == Bk) return launch_grads<D, M, Bk, OUT_F32>(p, s);
     SDPA_CASE(MASK_NONE, BIAS_NONE) SDPA_CASE(MASK_NONE, BIAS_T5) SDPA_CASE(MASK_NONE, BIAS_FULL)
@@ -682,8 +694,6 @@ static hipError_t launch_d(const BwdParams& p, int mask, int bias, hipStream_t s
 }  // namespace bwd
 
 hipError_t launch_bwd_bf16(BwdParams p, int D, int mask, int bias, bool out_f32, hipStream_t s) {
-    p.n_qt = (p.Sq + 255) / 256;
-    p.n_kt = (p.Sk + 127) / 128;
     p.xcd_remap = ((p.B * p.Hkv) % 8 == 0) ? 1 : 0;   // both kernels map (batch, KV head) groups to XCDs
     if (D == 128)
         return out_f32 ? bwd::launch_d<128, true>(p, mask, bias, s) : bwd::launch_d<128, false>(p, mask, bias, s);
@@ -691,6 +701,8 @@ hipError_t launch_bwd_bf16(BwdParams p, int D, int mask, int bias, bool out_f32,
         return out_f32 ? bwd::launch_d<64, true>(p, mask, bias, s) : bwd::launch_d<64, false>(p, mask, bias, s);
     if (D == 32)
         return out_f32 ? bwd::launch_d<32, true>(p, mask, bias, s) : bwd::launch_d<32, false>(p, mask, bias, s);
+    if (D == 256)
+        return out_f32 ? bwd::launch_d<256, true>(p, mask, bias, s) : bwd::launch_d<256, false>(p, mask, bias, s);
     return hipErrorInvalidValue;
 }
 
