@@ -16,13 +16,16 @@
 //                  through 2-slot LDS rings (LDS DMA). Per 32-key half: S^T = K.Q^T and
 //                  dP^T = V.dO^T (lane = query row, 16 keys per lane half), P and dS^T in
 //                  registers, then dQ^T += K^T.dS^T with K^T from transposing LDS reads.
-//   dkdv_kernel  : one workgroup = 4 waves = 128 keys of one (batch, KV head); each wave owns 32
-//                  keys and keeps their K and V fragments in VGPRs and their dK^T, dV^T
-//                  accumulators in the accumulation registers (one wave per SIMD). Q and dO
-//                  tiles of 64 query rows stream through a 2-slot LDS ring over the rows of the
-//                  G query heads sharing the KV head (heads ascending, rows ascending). Per
-//                  32-row block: S = Q.K^T and dP = dO.V^T (lane = key, 16 rows per lane half),
-//                  then dV^T += dO^T.P and dK^T += Q^T.dS with Q^T, dO^T from transposing reads.
+//   dkdv_kernel  : one workgroup = 8 waves = 128 keys of one (batch, KV head) (D = 256: 4 waves,
+//                  64 keys). The waves come in two roles over the same 32-key blocks: a dV wave
+//                  keeps its keys' K fragments in VGPRs and accumulates dV^T; a dK wave keeps K
+//                  and V fragments and accumulates dK^T (so each SIMD runs one wave of each
+//                  role). Q and dO tiles of 128 query rows (64 with a full bias at D = 128, and
+//                  at D = 256) stream through a 2-slot LDS ring over the rows of the G query
+//                  heads sharing the KV head (heads ascending, rows ascending). Per 32-row
+//                  block: S = Q.K^T in both roles and dP = dO.V^T in the dK role (lane = key, 16
+//                  rows per lane half), then dV^T += dO^T.P or dK^T += Q^T.dS with dO^T, Q^T
+//                  from transposing reads.
 // MFMA: v_mfma_f32_32x32x16_bf16 throughout; P and dS are rounded to bf16 (nearest even) as
 // MFMA operands, all sums are fp32.
 #include <hip/hip_runtime.h>
@@ -662,6 +665,333 @@ __global__ __launch_bounds__(64 * bwd_waves<D>(), 1) void dkdv_kernel(const BwdP
 }
 
 // ------------------------------------------------------------------------------------------
+// dK, dV with the scores formed once per (row, key) (D <= 128, no full bias): 128 keys of one
+// (batch, KV head) per workgroup, query rows in steps of 64 (128 at D = 32) through a 3-slot
+// LDS ring. Waves 0-3 (dV) form S = Q.K^T and P for their 32 keys, accumulate dV^T += dO^T.P
+// and leave P, rounded to bf16 as their MFMA operand, in LDS. Waves 4-7 (dK) run one step
+// behind on the same keys: dP = dO.V^T, dS = P (dP - D) with that P, dK^T += Q^T.dS; they
+// need neither the bias nor the mask (P is 0 wherever the mask hides a pair). Each step ends
+// with one barrier; after it the dK waves read what the dV waves wrote, and the ring slot of
+// the step two back is refilled (its last reader, a dK wave, finished before the barrier).
+// ------------------------------------------------------------------------------------------
+template <int D, int MASK, int BIAS, bool OUT_F32>
+__global__ __launch_bounds__(512, 1) void dkdv_lag_kernel(const BwdParams p) {
+    static_assert(D <= 128 && BIAS != BIAS_FULL, "P hand-off kernel: D <= 128, no full bias");
+    constexpr int kWaves = 8, kThreads = 512, kBK = 128, NS = 3;
+    constexpr int kBQ = D == 32 ? 128 : 64, NB = kBQ / 32;
+    constexpr int CH = D / 8, KS = D / 16, DB = D / 32, QT = kBQ * D;
+    constexpr bool IS_T5 = BIAS == BIAS_T5 || BIAS == BIAS_T5U;
+    constexpr bool ALIBI = BIAS == BIAS_ALIBI;
+    constexpr int kSat = BIAS == BIAS_T5U ? kT5USat : kT5Sat;
+    constexpr int kT5Pad = kSat + 64 + 31;
+    // LDS: slot sl holds the Q tile at [2 sl] and the dO tile at [2 sl + 1] (kBQ rows each);
+    // P of slot sl, key group kg (the dV wave), row block qb, 8-row group sg: pbuf[sl][kg][qb][sg]
+    // (lane-major, so every write and read is one conflict-free 16-byte access per lane)
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * NS * QT];
+    __shared__ __attribute__((aligned(16))) u32x4 pbuf[NS][4][NB][2][64];
+    __shared__ __attribute__((aligned(16))) float rowc[NS][2][kBQ];    // [slot][lse2, D][row]
+    __shared__ float t5s[IS_T5 ? 2 * kT5Pad + 1 : 1];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int hh = lane >> 5, r32 = lane & 31;
+    const bool role_dk = uniform(wave >= 4);
+    const int kg = wave & 3;                   // key group: the dV and dK waves of a SIMD share it
+    int group, kt_idx;
+    {
+        const int x = blockIdx.x;
+        if (p.xcd_remap) {
+            const int slot = x >> 3, gl = slot / p.n_kt;
+            kt_idx = slot - gl * p.n_kt;
+            group = gl * 8 + (x & 7);
+        } else {
+            group = x / p.n_kt;
+            kt_idx = x - group * p.n_kt;
+        }
+    }
+    const int b = group / p.Hkv, kvh = group - b * p.Hkv;
+    const int Sq = p.Sq, Sk = p.Sk, off = p.off, G = p.G;
+    const int k0 = kt_idx * kBK;
+    const int kw0 = k0 + 32 * kg;              // first key of this wave
+    const int my_j = kw0 + r32;                // key of this lane
+    const bool key_ok = my_j < Sk;
+    const bool wave_ok = kw0 < Sk;
+    const int kwe = min(kw0 + 31, Sk - 1);     // last valid key of the wave
+
+    const size_t q_row = (size_t)p.Hq * D, kv_row = (size_t)p.Hkv * D;
+    const size_t kv_off = ((size_t)b * Sk + (key_ok ? my_j : 0)) * kv_row + (size_t)kvh * D;
+    char* out_row = (char*)(role_dk ? p.dk : p.dv) + kv_off * (OUT_F32 ? 4 : 2);
+
+    // query rows the workgroup's keys can see (positions of the rows: i + off)
+    const int kend = min(k0 + kBK, Sk) - 1;
+    int qlo = 0, qhi = Sq;
+    if constexpr (MASK != MASK_NONE) qlo = max(0, k0 - off);
+    if constexpr (MASK == MASK_SLIDING) qhi = min(Sq, kend + p.window - off);
+    const int s_begin = qlo / kBQ;
+    const int s_end = (qhi <= qlo) ? s_begin : (qhi + kBQ - 1) / kBQ;
+    const int nqs = s_end - s_begin;
+    const int n_steps = G * nqs;
+
+    if (n_steps == 0) {        // no query row sees these keys: dK = dV = 0
+        if (key_ok) store_zero_row<D, OUT_F32>(out_row, hh);
+        return;
+    }
+    const bool neg = p.scale_log2 < 0.f;
+    const float c_scale = neg ? -p.scale_log2 : (p.scale_log2 == 0.f ? kTinyScale : p.scale_log2);
+
+    // Q / dO tiles of step n into slot sl: head h = kvh * G + n / nqs, rows kBQ s .. + kBQ - 1
+    // (clamped), and the rows' lse (log2 units) and D
+    constexpr int ROWS_PER_XFER = 1024 / (D * 2), XFERS = (kBQ * D * 2) / 1024, XPW = XFERS / kWaves;
+    static_assert(XPW * kWaves == XFERS, "dma split");
+    const uint32_t lds_base = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint16_t*)smem);
+    auto issue_step = [&](int n, int sl) {
+        const int h = kvh * G + n / nqs;
+        const int i0 = (s_begin + n % nqs) * kBQ;
+        const uint16_t* qg = (const uint16_t*)p.q + ((size_t)b * Sq * p.Hq + h) * D;
+        const uint16_t* dg = (const uint16_t*)p.dout + ((size_t)b * Sq * p.Hq + h) * D;
+#pragma unroll
+        for (int x = 0; x < XPW; ++x) {
+            const int xi = wave * XPW + x;
+            const int row = xi * ROWS_PER_XFER + lane / CH;
+            const int i = min(i0 + row, Sq - 1);
+            const int ch = ((lane % CH) ^ swz<D>(row)) * 8;
+            dma16(qg + (size_t)i * q_row + ch, lds_base + (uint32_t)((2 * sl) * QT * 2 + xi * 1024));
+            dma16(dg + (size_t)i * q_row + ch, lds_base + (uint32_t)((2 * sl + 1) * QT * 2 + xi * 1024));
+        }
+        if (tid < kBQ) {
+            const int i = i0 + tid;
+            float l2 = INFINITY, dd = 0.f;
+            if (i < Sq) {
+                const size_t ri = ((size_t)b * p.Hq + h) * Sq + i;
+                const float l = p.lse[ri];
+                l2 = (l == -INFINITY) ? INFINITY : l * kLog2e;
+                dd = p.delta[ri];
+            }
+            rowc[sl][0][tid] = l2;
+            rowc[sl][1][tid] = dd;
+        }
+    };
+
+    // Lane-dependent LDS byte offsets inside a tile (as in dkdv_kernel): row-wise reads for the
+    // A operands of S and dP, transposing reads for the A operands of the dV / dK products.
+    uint32_t rr_off[KS], tr_off[2 * DB];
+    {
+        const int row = perm32(r32);
+        const int sw = swz<D>(row);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) rr_off[ks] = (uint32_t)(row * D + (((2 * ks + hh) ^ sw) << 3)) * 2;
+        const int li = lane & 15, la = li & 3, gg = lane >> 4;
+        const int trow = 16 * hh + (li >> 2);
+        const int dlo = 16 * DB * (gg & 1) + 8 * (la & 1) + 4 * (la >> 1);
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const int r = trow + 4 * half;
+            const int sw2 = swz<D>(r);
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                const int d = 16 * db + dlo;
+                tr_off[2 * db + half] = (uint32_t)(r * D + ((((d >> 3) ^ sw2) << 3) | (d & 7))) * 2;
+            }
+        }
+    }
+    const char* lds = (const char*)smem;
+
+    auto run = [&](auto role) {
+        constexpr bool DK = decltype(role)::value;
+        // B operand fragments of this lane's key, dims 16 ks + 8 hh .. + 7: K (sign-flipped for a
+        // negative scale) for S = Q.K^T in the dV role, V for dP = dO.V^T in the dK role
+        bf16x8 bfr[KS];
+        {
+            const uint16_t* r = (const uint16_t*)(DK ? p.v : p.k) + kv_off + hh * 8;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                u32x4 x = *(const u32x4*)(r + ks * 16);
+                if (!key_ok) x = u32x4{0, 0, 0, 0};
+                if (!DK && neg) x ^= 0x80008000u;
+                bfr[ks] = __builtin_bit_cast(bf16x8, x);
+            }
+        }
+        f32x16 acc[DB];
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[db][v] = 0.f;
+
+        // one 32-row block (rows r0 = kBQ s + 32 QB ..) of step n in slot SL
+        auto compute_block = [&](int n, auto sl_tag, auto qb_tag) {
+            constexpr int SL = decltype(sl_tag)::value, QB = decltype(qb_tag)::value;
+            const int r0 = (s_begin + n % nqs) * kBQ + 32 * QB;
+            const int pa = r0 + off, pb = min(r0 + 31, Sq - 1) + off;
+            // the same test in both roles: a block the dV wave skips leaves no P, and the dK
+            // wave skips it too
+            bool skip = !wave_ok || r0 >= Sq;
+            if constexpr (MASK != MASK_NONE) skip = skip || (pb < kw0);
+            if constexpr (MASK == MASK_SLIDING) skip = skip || (pa - kwe >= p.window);
+            if (uniform(skip)) return;
+            constexpr uint32_t QTB = (2 * SL) * QT * 2, DTB = (2 * SL + 1) * QT * 2;   // tile bytes
+            constexpr uint32_t BLK = 32 * QB * D * 2;
+            const int rl = 32 * QB + 16 * hh;      // tile row of register 0 of this lane half
+            f32x16 s;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) s[v] = 0.f;
+            // S = Q.K^T (dV role) or dP = dO.V^T (dK role); register v of lane half hh: query
+            // row r0 + 16 hh + v, key my_j
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const bf16x8 a = *(const bf16x8*)(lds + rr_off[ks] + ((DK ? DTB : QTB) + BLK));
+                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bfr[ks], s, 0, 0, 0);
+            }
+            u32x4 pk[2];
+            if constexpr (!DK) {
+                const int h = kvh * G + n / nqs;
+                bool m = (r0 + 31 >= Sq) || (kw0 + 31 >= Sk);
+                if constexpr (MASK != MASK_NONE) m = m || (pa < kwe);
+                if constexpr (MASK == MASK_SLIDING) m = m || (pb - kw0 >= p.window);
+                const bool msk = uniform(m);
+                const int pos0 = r0 + 16 * hh + off;   // position of register 0's row
+                float x[16];
+                if constexpr (ALIBI) {
+                    // rel = my_j - position of row v
+                    const float aslope = ((const float*)p.bias)[h] * kLog2e;
+                    const float base = (float)(my_j - pos0);
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) x[v] = fmaf(s[v], c_scale, -aslope * fabsf(base - (float)v));
+                } else if constexpr (IS_T5) {
+                    const int rmin = kw0 - pb, rmax = kwe - pa;
+                    const int side = uniform(rmin >= kSat ? 1 : (rmax <= -kSat ? -1 : 0));
+                    if (side == 0) {
+                        // rel = my_j - position of row v; stays inside the padded table
+                        const float* trow = t5s + kT5Pad + (my_j - pos0);
+#pragma unroll
+                        for (int v = 0; v < 16; ++v) x[v] = fmaf(s[v], c_scale, trow[-v]);
+                    } else {
+                        const float bconst = side > 0 ? t5s[2 * kT5Pad] : t5s[0];
+#pragma unroll
+                        for (int v = 0; v < 16; ++v) x[v] = fmaf(s[v], c_scale, bconst);
+                    }
+                } else {
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) x[v] = s[v] * c_scale;
+                }
+                if (msk) {
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        const int pos = pos0 + v;
+                        bool vis = key_ok & (pos - off < Sq);
+                        if constexpr (MASK != MASK_NONE) vis = vis & (my_j <= pos);
+                        if constexpr (MASK == MASK_SLIDING) vis = vis & (pos - my_j < p.window);
+                        x[v] = vis ? x[v] : -INFINITY;
+                    }
+                }
+                float pv[16];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const u32x4 lr = *(const u32x4*)(&rowc[SL][0][rl + 4 * c]);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) pv[4 * c + e] = __builtin_amdgcn_exp2f(x[4 * c + e] - __uint_as_float(lr[e]));
+                }
+#pragma unroll
+                for (int sg = 0; sg < 2; ++sg) {
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) pk[sg][c] = pack_bf16x2(pv[8 * sg + 2 * c], pv[8 * sg + 2 * c + 1]);
+                    pbuf[SL][kg][QB][sg][lane] = pk[sg];
+                }
+            } else {
+                // dS = P (dP - D) with the dV wave's P of the same (row, key)
+#pragma unroll
+                for (int sg = 0; sg < 2; ++sg) {
+                    const u32x4 pin = pbuf[SL][kg][QB][sg][lane];
+                    const u32x4 dr0 = *(const u32x4*)(&rowc[SL][1][rl + 8 * sg]);
+                    const u32x4 dr1 = *(const u32x4*)(&rowc[SL][1][rl + 8 * sg + 4]);
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        const int v = 8 * sg + 2 * c;
+                        const float d0 = __uint_as_float(c < 2 ? dr0[2 * c] : dr1[2 * c - 4]);
+                        const float d1 = __uint_as_float(c < 2 ? dr0[2 * c + 1] : dr1[2 * c - 3]);
+                        const float p0 = bf16_to_f32(pin[c] & 0xffffu), p1 = bf16_to_f32(pin[c] >> 16);
+                        pk[sg][c] = pack_bf16x2(p0 * (s[v] - d0), p1 * (s[v + 1] - d1));
+                    }
+                }
+            }
+            // dV^T += dO^T P  or  dK^T += Q^T dS, over the two 8-row groups of each lane half
+            constexpr uint32_t TTB = DK ? QTB : DTB;
+#pragma unroll
+            for (int sg = 0; sg < 2; ++sg) {
+                const bf16x8 bp = __builtin_bit_cast(bf16x8, pk[sg]);
+                const uint32_t gofs = TTB + (uint32_t)((32 * QB + 8 * sg) * D * 2);
+#pragma unroll
+                for (int db = 0; db < DB; ++db) {
+                    const s16x4 lo = lds_read_tr((const uint16_t*)(lds + tr_off[2 * db] + gofs));
+                    const s16x4 hi = lds_read_tr((const uint16_t*)(lds + tr_off[2 * db + 1] + gofs));
+                    u32x4 av;
+                    av[0] = __builtin_bit_cast(u32x2, lo)[0];
+                    av[1] = __builtin_bit_cast(u32x2, lo)[1];
+                    av[2] = __builtin_bit_cast(u32x2, hi)[0];
+                    av[3] = __builtin_bit_cast(u32x2, hi)[1];
+                    acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), bp, acc[db], 0, 0, 0);
+                }
+            }
+        };
+
+        // iteration it: the dV waves take step it (slot SL), the dK waves step it - 1 (slot
+        // (SL + 2) % 3), and step it + 1 streams into slot (SL + 1) % 3. Both roles run the same
+        // iterations and barriers.
+        auto iter = [&](int it, auto sl_tag) {
+            constexpr int SL = decltype(sl_tag)::value, SP = (SL + 2) % NS, SN = (SL + 1) % NS;
+            if constexpr (IS_T5) {
+                // table of the dV waves' head when it changes (its readers of the previous table
+                // finished before the last barrier; one more barrier after the writes)
+                if (it < n_steps) {
+                    const int h = kvh * G + it / nqs;
+                    if (it == 0 || h != kvh * G + (it - 1) / nqs) {
+                        const float* tbl = (const float*)p.bias + (size_t)h * kT5Buckets;
+                        for (int i = tid; i < 2 * kT5Pad + 1; i += kThreads)
+                            t5s[i] = tbl[BIAS == BIAS_T5U ? t5u_bucket(i - kT5Pad) : t5_bucket(i - kT5Pad)] * kLog2e;
+                        __syncthreads();
+                    }
+                }
+            }
+            const bool has_next = it + 1 < n_steps;
+            if (has_next) issue_step(it + 1, SN);
+            if constexpr (DK) {
+                if (it >= 1) {
+                    compute_block(it - 1, std::integral_constant<int, SP>{}, std::integral_constant<int, 0>{});
+                    compute_block(it - 1, std::integral_constant<int, SP>{}, std::integral_constant<int, 1>{});
+                    if constexpr (NB == 4) {
+                        compute_block(it - 1, std::integral_constant<int, SP>{}, std::integral_constant<int, 2>{});
+                        compute_block(it - 1, std::integral_constant<int, SP>{}, std::integral_constant<int, 3>{});
+                    }
+                }
+            } else {
+                if (it < n_steps) {
+                    compute_block(it, std::integral_constant<int, SL>{}, std::integral_constant<int, 0>{});
+                    compute_block(it, std::integral_constant<int, SL>{}, std::integral_constant<int, 1>{});
+                    if constexpr (NB == 4) {
+                        compute_block(it, std::integral_constant<int, SL>{}, std::integral_constant<int, 2>{});
+                        compute_block(it, std::integral_constant<int, SL>{}, std::integral_constant<int, 3>{});
+                    }
+                }
+            }
+            static_assert(NB == 2 || NB == 4, "two or four 32-row blocks per step");
+            if (has_next) dma_wait();
+            __syncthreads();
+        };
+#pragma unroll 1
+        for (int it = 0; it <= n_steps; it += NS) {
+            iter(it, std::integral_constant<int, 0>{});
+            if (it + 1 <= n_steps) iter(it + 1, std::integral_constant<int, 1>{});
+            if (it + 2 <= n_steps) iter(it + 2, std::integral_constant<int, 2>{});
+        }
+        if (key_ok) store_row<D, OUT_F32>(out_row, acc, DK ? p.scale : 1.f, hh);
+    };
+
+    issue_step(0, 0);
+    dma_wait();
+    __syncthreads();
+    if (role_dk) run(std::true_type{});
+    else run(std::false_type{});
+}
+
+// ------------------------------------------------------------------------------------------
 // host-side launch
 // ------------------------------------------------------------------------------------------
 template <int D, int MASK, int BIAS, bool OUT_F32>
@@ -671,7 +1001,10 @@ static hipError_t launch_grads(const BwdParams& p, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const unsigned gk = (unsigned)((size_t)p.B * p.Hkv * p.n_kt);
-    hipLaunchKernelGGL((dkdv_kernel<D, MASK, BIAS, OUT_F32>), dim3(gk), dim3(64 * bwd_waves<D>()), 0, s, p);
+    if constexpr (D <= 128 && BIAS != BIAS_FULL)
+        hipLaunchKernelGGL((dkdv_lag_kernel<D, MASK, BIAS, OUT_F32>), dim3(gk), dim3(512), 0, s, p);
+    else
+        hipLaunchKernelGGL((dkdv_kernel<D, MASK, BIAS, OUT_F32>), dim3(gk), dim3(64 * bwd_waves<D>()), 0, s, p);
     return hipGetLastError();
 }
 

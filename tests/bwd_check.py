@@ -5,7 +5,11 @@ derived from the kernel's arithmetic, with u = 2^-8 (unit roundoff of bf16, roun
 even) and f = 2^-24 (fp32):
 
   * P and dS are rounded to bf16 once each as matrix-core operands (relative error <= u);
-    every product and sum after that is fp32. The row constant rowsum(dO * O) uses the bf16
+    every product and sum after that is fp32. Where the dK/dV kernel forms P once and hands
+    it from the dV product to the dK product (head dims up to 128 without a full bias), the
+    dS of dK is formed from that bf16 P: its P carries the extra rounding, so dK's bound
+    uses the relative error of the rounded P in place of that of the fp32 P; dQ's dS is
+    formed from the fp32 P. The row constant rowsum(dO * O) uses the bf16
     forward output O~ that the caller passes in, so its error is sum_d |dO| |O~ - O| plus fp32
     rounding. P is recomputed from the forward's fp32 LSE, whose error |lse~ - lse| enters P
     as a relative error, as do the fp32 rounding of the score (D f sum |q k| |scale|) and of
@@ -15,7 +19,8 @@ even) and f = 2^-24 (fp32):
     gives an element-wise bound: every element must lie within it (check 1).
   * The rounding errors of distinct terms are independent and of either sign, so the
     root-mean-square error of a whole gradient tensor stays below u / sqrt(3) of its rms value
-    plus the (smaller) row-constant terms: check 2 requires ||err||_2 <= u ||ref||_2.
+    plus the (smaller) row-constant terms (u sqrt(2/3) for a dK whose dS takes two roundings,
+    the bf16 P and the bf16 dS): check 2 requires ||err||_2 <= u ||ref||_2.
 The bf16-output entry point must return exactly the round-to-nearest-even of the fp32-output
 entry point's values (same kernels, same fp32 results, one final rounding) -- check 3 lives
 in the tests.
@@ -57,6 +62,8 @@ def pair_reference(q, k, v, dout, o_gpu, lse_gpu, b, kvh, *, scale, mask_kind, w
     B, Sq, Hq, D = q.shape
     Sk, Hkv = k.shape[1], k.shape[2]
     G = Hq // Hkv
+    # the dK/dV kernel that hands the bf16 P from the dV product to the dK product
+    p_handoff = D <= 128 and bias_kind != oracle.BIAS_FULL
     dq_ref, dk_ref, dv_ref = oracle.sdpa_backward(
         q, k, v, dout, scale=scale, mask_kind=mask_kind, window=window, bias_kind=bias_kind,
         bias=bias, kv_heads=[(b, kvh)])
@@ -95,10 +102,16 @@ def pair_reference(q, k, v, dout, o_gpu, lse_gpu, b, kvh, *, scale, mask_kind, w
         d_ds = eps_p * p * np.abs(dp - delta[:, None]) + p * (e_dp + e_delta[:, None])
         e_ds = (1 + U_BF16) * d_ds + U_BF16 * np.abs(ds)
         e_p = (eps_p + U_BF16 * (1 + eps_p)) * p
+        if p_handoff:
+            # dK's dS = rnd(rnd(P) (dP - D)): P's relative error is that of the bf16 operand
+            d_ds_k = e_p * np.abs(dp - delta[:, None]) + p * (e_dp + e_delta[:, None])
+            e_ds_k = (1 + U_BF16) * d_ds_k + U_BF16 * np.abs(ds)
+        else:
+            e_ds_k = e_ds
         ads = np.abs(ds) + e_ds
         bq[:, g] = sc * (e_ds @ ak + Sk * F32 * (ads @ ak)) + F32 * np.abs(dq_ref[b, :, h])
         aq = np.abs(q_h)
-        bk += sc * (e_ds.T @ aq + n_kv_terms * F32 * (ads.T @ aq))
+        bk += sc * (e_ds_k.T @ aq + n_kv_terms * F32 * ((np.abs(ds) + e_ds_k).T @ aq))
         bv += e_p.T @ ado + n_kv_terms * F32 * ((p + e_p).T @ ado)
     bk += F32 * np.abs(dk_ref[b, :, kvh])
     bv += F32 * np.abs(dv_ref[b, :, kvh])
