@@ -333,20 +333,25 @@ def bwd_tile_mfmas(wl: si.Workload):
     """MFMA instructions (v_mfma_f32_32x32x16_bf16) the two gradient kernels issue, following
     their tile plans: (dq kernel, dk/dv kernel) per launch.
 
-    dq kernel: work items of 256 query rows, 64-key tiles over the item's key range; a 32-row
-    wave computes a tile unless the mask hides it completely, issuing per 32-key half D/16
-    MFMAs for S, D/16 for dP and 2 * D/32 for dQ. dk/dv kernel: 128 keys per workgroup, steps
-    of 128 query rows (64 with a full bias at D = 128) over the G query heads; each 32-key
-    group has a dV wave (D/16 for S, 2 * D/32 for dV per 32-row block) and a dK wave (2 * D/16
-    for S and dP, 2 * D/32 for dK), which skip blocks the mask hides completely."""
+    dq kernel: work items of 256 query rows (128 at D = 256), 64-key tiles over the item's key
+    range; a 32-row wave computes a tile unless the mask hides it completely, issuing per
+    32-key half D/16 MFMAs for S, D/16 for dP and 2 * D/32 for dQ. dk/dv kernel: 128 keys per
+    workgroup (64 at D = 256), steps of query rows over the G query heads; each 32-key group
+    has a dV wave and a dK wave, which skip the 32-row blocks the mask hides completely. Up to
+    D = 128 without a full bias (steps of 64 rows, 128 at D = 32) the dV wave forms S and P
+    (D/16, then 2 * D/32 for dV) and the dK wave takes that P (D/16 for dP, 2 * D/32 for dK);
+    otherwise (steps of 128 rows, 64 with a full bias at D = 128 and at D = 256) the dK wave
+    forms S itself as well (2 * D/16, then 2 * D/32)."""
     off, D, W = wl.Sk - wl.Sq, wl.D, wl.window
     G = wl.Hq // wl.Hkv
     causal = wl.mask_kind != si.MASK_NONE
     sliding = wl.mask_kind == si.MASK_SLIDING
+    full_bias = wl.bias_kind == si.BIAS_FULL
+    rows = 128 if D == 256 else 256
     per_half = 2 * (D // 16) + 2 * (D // 32)
     dq = 0
-    for q0 in range(0, wl.Sq, 256):
-        pa, pb = q0 + off, min(q0 + 256, wl.Sq) - 1 + off
+    for q0 in range(0, wl.Sq, rows):
+        pa, pb = q0 + off, min(q0 + rows, wl.Sq) - 1 + off
         khi, klo = wl.Sk - 1, 0
         if causal:
             khi = min(khi, pb)
@@ -354,7 +359,7 @@ def bwd_tile_mfmas(wl: si.Workload):
             klo = max(0, pa - W + 1)
         if khi < klo:
             continue
-        for wq0 in range(q0, min(q0 + 256, wl.Sq), 32):
+        for wq0 in range(q0, min(q0 + rows, wl.Sq), 32):
             pwa, pwb = wq0 + off, min(wq0 + 31, wl.Sq - 1) + off
             for t in range(klo // 64, khi // 64 + 1):
                 j0 = 64 * t
@@ -363,11 +368,17 @@ def bwd_tile_mfmas(wl: si.Workload):
                 if sliding and j0 + 63 <= pwa - W:
                     continue
                 dq += 2 * per_half
-    kbq = 64 if (wl.bias_kind == si.BIAS_FULL and D == 128) else 128
-    per_dv, per_dk = D // 16 + 2 * (D // 32), 2 * (D // 16) + 2 * (D // 32)
+    handoff = D <= 128 and not full_bias
+    if handoff:
+        kbq = 128 if D == 32 else 64
+    else:
+        kbq = 64 if ((full_bias and D == 128) or D == 256) else 128
+    kbk = 64 if D == 256 else 128
+    per_dv = D // 16 + 2 * (D // 32)
+    per_dk = (1 if handoff else 2) * (D // 16) + 2 * (D // 32)
     dkdv = 0
-    for k0 in range(0, wl.Sk, 128):
-        kend = min(k0 + 128, wl.Sk) - 1
+    for k0 in range(0, wl.Sk, kbk):
+        kend = min(k0 + kbk, wl.Sk) - 1
         qlo, qhi = 0, wl.Sq
         if causal:
             qlo = max(0, k0 - off)
@@ -375,7 +386,7 @@ def bwd_tile_mfmas(wl: si.Workload):
             qhi = min(wl.Sq, kend + min(W, wl.Sk + 1) - off)
         if qhi <= qlo:
             continue
-        for kw0 in range(k0, min(k0 + 128, wl.Sk), 32):
+        for kw0 in range(k0, min(k0 + kbk, wl.Sk), 32):
             kwe = min(kw0 + 31, wl.Sk - 1)
             for s0 in range((qlo // kbq) * kbq, qhi, kbq):
                 for r0 in range(s0, s0 + kbq, 32):

@@ -67,6 +67,14 @@ def test_blocks_are_exactly_those_with_a_visible_pair(mask, w, sq, sk):
 # ------------------------------------------------------------------------------------------
 # gradient kernels: MFMA instructions of the tile plans (bench.bwd_tile_mfmas)
 # ------------------------------------------------------------------------------------------
+def _kv_per_block(D, bias_kind):
+    # MFMAs of one 32-row x 32-key block in the dk/dv kernel: the dV wave forms S (D/16) and
+    # dV (2 D/32); the dK wave forms dP (D/16) and dK (2 D/32), plus S itself (D/16) where P is
+    # not handed over (full bias, or D = 256)
+    handoff = D <= 128 and bias_kind != si.BIAS_FULL
+    return (D // 16 + 2 * (D // 32)) + ((1 if handoff else 2) * (D // 16) + 2 * (D // 32))
+
+
 def test_bwd_unmasked_closed_form():
     for D in (64, 128):
         wl = si.WORKLOADS["c4t5"].replace(B=2, Hq=4, Hkv=2, Sq=512, Sk=768, D=D,
@@ -75,8 +83,7 @@ def test_bwd_unmasked_closed_form():
         G = wl.Hq // wl.Hkv
         per_half = 2 * (D // 16) + 2 * (D // 32)
         assert dq == wl.B * wl.Hq * (wl.Sq // 32) * (wl.Sk // 64) * 2 * per_half
-        per_pair = (D // 16 + 2 * (D // 32)) + (2 * (D // 16) + 2 * (D // 32))
-        assert dkdv == wl.B * wl.Hkv * (wl.Sk // 32) * (wl.Sq // 32) * G * per_pair
+        assert dkdv == wl.B * wl.Hkv * (wl.Sk // 32) * (wl.Sq // 32) * G * _kv_per_block(D, wl.bias_kind)
 
 
 @pytest.mark.parametrize("mask,w,sq,sk,bias", [
@@ -103,5 +110,4 @@ def test_bwd_blocks_are_exactly_those_with_a_visible_pair(mask, w, sq, sk, bias)
     D, G = wl.D, 2
     dq, dkdv = bench.bwd_tile_mfmas(wl)
     assert dq == len(dq_blocks) * 2 * (2 * (D // 16) + 2 * (D // 32)) * wl.Hq
-    per_pair = (D // 16 + 2 * (D // 32)) + (2 * (D // 16) + 2 * (D // 32))
-    assert dkdv == len(kv_blocks) * per_pair * G
+    assert dkdv == len(kv_blocks) * _kv_per_block(D, bias) * G
