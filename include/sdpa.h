@@ -124,8 +124,9 @@ int sdpa_fwd_f32(const float* q, const float* k, const float* v, float* out, flo
  *   dq : [B][Sq][Hq][D]   dk, dv : [B][Sk][Hkv][D]   (bf16 here, fp32 for sdpa_bwd_f32out)
  *   ws : caller-owned device workspace of B*Hq*Sq floats (4-byte aligned); receives
  *        rowsum(dout * out) per query row; its contents on entry do not matter.
- * Two launches on `stream`: dq with the row sums (one workgroup per 256 query rows), then dk and
- * dv (one workgroup per 128 keys of one KV head, looping over the query rows of its G heads).
+ * Two launches on `stream`: dq with the row sums (one workgroup per 256 query rows, 128 at
+ * D = 256), then dk and dv (one workgroup per 128 keys of one KV head, 64 at D = 256, looping
+ * over the query rows of its G heads).
  * Every output element has exactly one writer and a fixed summation order (query heads
  * ascending, query rows ascending): bitwise reproducible, no atomics. Validation as for
  * sdpa_fwd, plus dout, dq, dk, dv 16-byte aligned and non-NULL, ws non-NULL.
