@@ -16,16 +16,19 @@
 //                  through 2-slot LDS rings (LDS DMA). Per 32-key half: S^T = K.Q^T and
 //                  dP^T = V.dO^T (lane = query row, 16 keys per lane half), P and dS^T in
 //                  registers, then dQ^T += K^T.dS^T with K^T from transposing LDS reads.
-//   dkdv_kernel  : one workgroup = 8 waves = 128 keys of one (batch, KV head) (D = 256: 4 waves,
-//                  64 keys). The waves come in two roles over the same 32-key blocks: a dV wave
-//                  keeps its keys' K fragments in VGPRs and accumulates dV^T; a dK wave keeps K
-//                  and V fragments and accumulates dK^T (so each SIMD runs one wave of each
-//                  role). Q and dO tiles of 128 query rows (64 with a full bias at D = 128, and
-//                  at D = 256) stream through a 2-slot LDS ring over the rows of the G query
-//                  heads sharing the KV head (heads ascending, rows ascending). Per 32-row
-//                  block: S = Q.K^T in both roles and dP = dO.V^T in the dK role (lane = key, 16
-//                  rows per lane half), then dV^T += dO^T.P or dK^T += Q^T.dS with dO^T, Q^T
-//                  from transposing reads.
+//   dkdv_lag_kernel (no full bias) and dkdv_kernel (full bias): one workgroup = 8 waves = 128
+//                  keys of one (batch, KV head) (D = 256: 4 waves, 64 keys). The waves come in
+//                  two roles over the same 32-key blocks: a dV wave keeps its keys' K fragments
+//                  in VGPRs and accumulates dV^T; a dK wave keeps V (and, in dkdv_kernel, K)
+//                  fragments and accumulates dK^T. Q and dO tiles stream through an LDS ring
+//                  over the rows of the G query heads sharing the KV head (heads ascending,
+//                  rows ascending). Per 32-row block (lane = key, 16 rows per lane half): the
+//                  dV wave forms S = Q.K^T and P, then dV^T += dO^T.P with dO^T from
+//                  transposing reads; the dK wave forms dP = dO.V^T and dS = P (dP - D), then
+//                  dK^T += Q^T.dS with Q^T from transposing reads. In dkdv_lag_kernel the dK
+//                  wave takes P from the dV wave through LDS, one step behind (3-slot ring);
+//                  in dkdv_kernel it forms S itself (2-slot ring; the full-bias tile shares
+//                  the LDS, which leaves no room for the P hand-off).
 // MFMA: v_mfma_f32_32x32x16_bf16 throughout; P and dS are rounded to bf16 (nearest even) as
 // MFMA operands, all sums are fp32.
 #include <hip/hip_runtime.h>
@@ -326,10 +329,11 @@ __global__ __launch_bounds__(64 * bwd_waves<D>(), 1) void dq_kernel(const BwdPar
 }
 
 // ------------------------------------------------------------------------------------------
-// dK, dV: 128 keys of one (batch, KV head) per workgroup, query rows in steps of 128.
-// Waves 0-3 accumulate dV and waves 4-7 dK for the same four 32-key groups, so each wave holds
-// one 32 x D accumulator and two waves share every SIMD. Both roles form S = Q.K^T with the
-// same instructions (so their P agree bit for bit); the dK waves also form dP = dO.V^T.
+// dK, dV with a full bias: 128 keys of one (batch, KV head) per workgroup (64 at D = 256),
+// query rows in steps of 128 (64 at D = 128 and 256). The first half of the waves accumulate
+// dV and the second half dK for the same 32-key groups, so each wave holds one 32 x D
+// accumulator. Both roles form S = Q.K^T with the same instructions (so their P agree bit for
+// bit); the dK waves also form dP = dO.V^T. (Without a full bias, dkdv_lag_kernel below.)
 // ------------------------------------------------------------------------------------------
 template <int D, int MASK, int BIAS, bool OUT_F32>
 __global__ __launch_bounds__(64 * bwd_waves<D>(), 1) void dkdv_kernel(const BwdParams p) {
@@ -665,20 +669,22 @@ __global__ __launch_bounds__(64 * bwd_waves<D>(), 1) void dkdv_kernel(const BwdP
 }
 
 // ------------------------------------------------------------------------------------------
-// dK, dV with the scores formed once per (row, key) (D <= 128, no full bias): 128 keys of one
-// (batch, KV head) per workgroup, query rows in steps of 64 (128 at D = 32) through a 3-slot
-// LDS ring. Waves 0-3 (dV) form S = Q.K^T and P for their 32 keys, accumulate dV^T += dO^T.P
-// and leave P, rounded to bf16 as their MFMA operand, in LDS. Waves 4-7 (dK) run one step
-// behind on the same keys: dP = dO.V^T, dS = P (dP - D) with that P, dK^T += Q^T.dS; they
-// need neither the bias nor the mask (P is 0 wherever the mask hides a pair). Each step ends
+// dK, dV with the scores formed once per (row, key) (no full bias): 128 keys of one (batch, KV
+// head) per workgroup (64 at D = 256), query rows in steps of 64 (128 at D = 32, 32 at D = 256)
+// through a 3-slot LDS ring. The first half of the waves (dV) form S = Q.K^T and P for their
+// 32 keys each, accumulate dV^T += dO^T.P and leave P, rounded to bf16 as their MFMA operand,
+// in LDS. The second half (dK) run one step behind on the same keys: dP = dO.V^T,
+// dS = P (dP - D) with that P, dK^T += Q^T.dS; they need neither the bias nor the mask (P is
+// 0 wherever the mask hides a pair). Each step ends
 // with one barrier; after it the dK waves read what the dV waves wrote, and the ring slot of
 // the step two back is refilled (its last reader, a dK wave, finished before the barrier).
 // ------------------------------------------------------------------------------------------
 template <int D, int MASK, int BIAS, bool OUT_F32>
-__global__ __launch_bounds__(512, 1) void dkdv_lag_kernel(const BwdParams p) {
-    static_assert(D <= 128 && BIAS != BIAS_FULL, "P hand-off kernel: D <= 128, no full bias");
-    constexpr int kWaves = 8, kThreads = 512, kBK = 128, NS = 3;
-    constexpr int kBQ = D == 32 ? 128 : 64, NB = kBQ / 32;
+__global__ __launch_bounds__(64 * bwd_waves<D>(), 1) void dkdv_lag_kernel(const BwdParams p) {
+    static_assert(BIAS != BIAS_FULL, "P hand-off kernel: no full bias");
+    constexpr int kWaves = bwd_waves<D>(), kThreads = 64 * kWaves, KG = kWaves / 2;
+    constexpr int kBK = 32 * KG, NS = 3;       // keys per workgroup, ring slots
+    constexpr int kBQ = D == 256 ? 32 : (D == 32 ? 128 : 64), NB = kBQ / 32;
     constexpr int CH = D / 8, KS = D / 16, DB = D / 32, QT = kBQ * D;
     constexpr bool IS_T5 = BIAS == BIAS_T5 || BIAS == BIAS_T5U;
     constexpr bool ALIBI = BIAS == BIAS_ALIBI;
@@ -688,14 +694,14 @@ __global__ __launch_bounds__(512, 1) void dkdv_lag_kernel(const BwdParams p) {
     // P of slot sl, key group kg (the dV wave), row block qb, 8-row group sg: pbuf[sl][kg][qb][sg]
     // (lane-major, so every write and read is one conflict-free 16-byte access per lane)
     __shared__ __attribute__((aligned(16))) uint16_t smem[2 * NS * QT];
-    __shared__ __attribute__((aligned(16))) u32x4 pbuf[NS][4][NB][2][64];
+    __shared__ __attribute__((aligned(16))) u32x4 pbuf[NS][KG][NB][2][64];
     __shared__ __attribute__((aligned(16))) float rowc[NS][2][kBQ];    // [slot][lse2, D][row]
     __shared__ float t5s[IS_T5 ? 2 * kT5Pad + 1 : 1];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int hh = lane >> 5, r32 = lane & 31;
-    const bool role_dk = uniform(wave >= 4);
-    const int kg = wave & 3;                   // key group: the dV and dK waves of a SIMD share it
+    const bool role_dk = uniform(wave >= KG);
+    const int kg = wave % KG;                  // key group: one dV and one dK wave share it
     int group, kt_idx;
     {
         const int x = blockIdx.x;
@@ -955,7 +961,8 @@ __global__ __launch_bounds__(512, 1) void dkdv_lag_kernel(const BwdParams p) {
             if constexpr (DK) {
                 if (it >= 1) {
                     compute_block(it - 1, std::integral_constant<int, SP>{}, std::integral_constant<int, 0>{});
-                    compute_block(it - 1, std::integral_constant<int, SP>{}, std::integral_constant<int, 1>{});
+                    if constexpr (NB >= 2)
+                        compute_block(it - 1, std::integral_constant<int, SP>{}, std::integral_constant<int, 1>{});
                     if constexpr (NB == 4) {
                         compute_block(it - 1, std::integral_constant<int, SP>{}, std::integral_constant<int, 2>{});
                         compute_block(it - 1, std::integral_constant<int, SP>{}, std::integral_constant<int, 3>{});
@@ -964,14 +971,15 @@ __global__ __launch_bounds__(512, 1) void dkdv_lag_kernel(const BwdParams p) {
             } else {
                 if (it < n_steps) {
                     compute_block(it, std::integral_constant<int, SL>{}, std::integral_constant<int, 0>{});
-                    compute_block(it, std::integral_constant<int, SL>{}, std::integral_constant<int, 1>{});
+                    if constexpr (NB >= 2)
+                        compute_block(it, std::integral_constant<int, SL>{}, std::integral_constant<int, 1>{});
                     if constexpr (NB == 4) {
                         compute_block(it, std::integral_constant<int, SL>{}, std::integral_constant<int, 2>{});
                         compute_block(it, std::integral_constant<int, SL>{}, std::integral_constant<int, 3>{});
                     }
                 }
             }
-            static_assert(NB == 2 || NB == 4, "two or four 32-row blocks per step");
+            static_assert(NB == 1 || NB == 2 || NB == 4, "one, two or four 32-row blocks per step");
             if (has_next) dma_wait();
             __syncthreads();
         };
@@ -1001,8 +1009,8 @@ static hipError_t launch_grads(const BwdParams& p, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const unsigned gk = (unsigned)((size_t)p.B * p.Hkv * p.n_kt);
-    if constexpr (D <= 128 && BIAS != BIAS_FULL)
-        hipLaunchKernelGGL((dkdv_lag_kernel<D, MASK, BIAS, OUT_F32>), dim3(gk), dim3(512), 0, s, p);
+    if constexpr (BIAS != BIAS_FULL)
+        hipLaunchKernelGGL((dkdv_lag_kernel<D, MASK, BIAS, OUT_F32>), dim3(gk), dim3(64 * bwd_waves<D>()), 0, s, p);
     else
         hipLaunchKernelGGL((dkdv_kernel<D, MASK, BIAS, OUT_F32>), dim3(gk), dim3(64 * bwd_waves<D>()), 0, s, p);
     return hipGetLastError();

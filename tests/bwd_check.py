@@ -6,7 +6,7 @@ even) and f = 2^-24 (fp32):
 
   * P and dS are rounded to bf16 once each as matrix-core operands (relative error <= u);
     every product and sum after that is fp32. Where the dK/dV kernel forms P once and hands
-    it from the dV product to the dK product (head dims up to 128 without a full bias), the
+    it from the dV product to the dK product (every head dim, without a full bias), the
     dS of dK is formed from that bf16 P: its P carries the extra rounding, so dK's bound
     uses the relative error of the rounded P in place of that of the fp32 P; dQ's dS is
     formed from the fp32 P. The row constant rowsum(dO * O) uses the bf16
@@ -63,7 +63,7 @@ def pair_reference(q, k, v, dout, o_gpu, lse_gpu, b, kvh, *, scale, mask_kind, w
     Sk, Hkv = k.shape[1], k.shape[2]
     G = Hq // Hkv
     # the dK/dV kernel that hands the bf16 P from the dV product to the dK product
-    p_handoff = D <= 128 and bias_kind != oracle.BIAS_FULL
+    p_handoff = bias_kind != oracle.BIAS_FULL
     dq_ref, dk_ref, dv_ref = oracle.sdpa_backward(
         q, k, v, dout, scale=scale, mask_kind=mask_kind, window=window, bias_kind=bias_kind,
         bias=bias, kv_heads=[(b, kvh)])

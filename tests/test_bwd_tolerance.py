@@ -56,9 +56,9 @@ def emulate(q, k, v, dout, o16, lse32, b, kvh, scale, mask, window, bias_kind, b
         dp = do_h @ v_h.T
         ds = p * (dp - delta[:, None])
         pb, dsb = bf16(p), bf16(ds)
-        # up to D = 128 without a full bias the dK/dV kernel forms P once and the dK product's
-        # dS takes that bf16 P
-        handoff = D <= 128 and bias_kind != oracle.BIAS_FULL
+        # without a full bias the dK/dV kernel forms P once and the dK product's dS takes that
+        # bf16 P
+        handoff = bias_kind != oracle.BIAS_FULL
         dsb_k = bf16(pb * (dp - delta[:, None])) if handoff else dsb
         kk = np.roll(k_h, 1, axis=0) if plant == "dq_key_shift" else k_h
         dq[:, g] = np.float32(scale) * (dsb @ kk)
