@@ -337,9 +337,12 @@ def bwd_tile_mfmas(wl: si.Workload):
     range; a 32-row wave computes a tile unless the mask hides it completely, issuing per
     32-key half D/16 MFMAs for S, D/16 for dP and 2 * D/32 for dQ. dk/dv kernel: 128 keys per
     workgroup (64 at D = 256), steps of query rows over the G query heads; each 32-key group
-    has a dV wave and a dK wave, which skip the 32-row blocks the mask hides completely, over
-    steps of 64 rows (128 at D = 32, 32 at D = 256): the dV wave forms S and P (D/16, then
-    2 * D/32 for dV) and the dK wave takes that P (D/16 for dP, 2 * D/32 for dK)."""
+    has a dV wave and a dK wave, which skip the 32-row blocks the mask hides completely.
+    Without a full bias, and with one at D = 64 (steps of 64 rows; 128 at D = 32, 32 at
+    D = 256), the dV wave forms S and P (D/16, then 2 * D/32 for dV) and the dK wave takes
+    that P (D/16 for dP, 2 * D/32 for dK); with a full bias at D = 32, 128 and 256 (steps of
+    128 rows, 64 at D = 128 and 256) the dK wave forms S itself as well (2 * D/16, then
+    2 * D/32)."""
     off, D, W = wl.Sk - wl.Sq, wl.D, wl.window
     G = wl.Hq // wl.Hkv
     causal = wl.mask_kind != si.MASK_NONE
@@ -365,10 +368,14 @@ def bwd_tile_mfmas(wl: si.Workload):
                 if sliding and j0 + 63 <= pwa - W:
                     continue
                 dq += 2 * per_half
-    kbq = 32 if D == 256 else (128 if D == 32 else 64)
+    handoff = wl.bias_kind != si.BIAS_FULL or D == 64
+    if handoff:
+        kbq = 32 if D == 256 else (128 if D == 32 else 64)
+    else:
+        kbq = 64 if D in (128, 256) else 128
     kbk = 64 if D == 256 else 128
     per_dv = D // 16 + 2 * (D // 32)
-    per_dk = D // 16 + 2 * (D // 32)
+    per_dk = (1 if handoff else 2) * (D // 16) + 2 * (D // 32)
     dkdv = 0
     for k0 in range(0, wl.Sk, kbk):
         kend = min(k0 + kbk, wl.Sk) - 1

@@ -26,6 +26,9 @@
 //                  dO^T from transposing reads, and leaves P in LDS; the dK wave, one step
 //                  behind, forms dP = dO.V^T and dS = P (dP - D) with that P, then
 //                  dK^T += Q^T.dS with Q^T from transposing reads.
+//   dkdv_kernel  : a full bias at D = 32, 128 and 256, where a bias tile per slot does not
+//                  fit beside the 3-slot ring and the P buffers: the same roles over a 2-slot
+//                  ring with the bias tile in LDS, the dK wave forming S itself.
 // MFMA: v_mfma_f32_32x32x16_bf16 throughout; P and dS are rounded to bf16 (nearest even) as
 // MFMA operands, all sums are fp32.
 #include <hip/hip_runtime.h>
@@ -326,6 +329,348 @@ __global__ __launch_bounds__(64 * bwd_waves<D>(), 1) void dq_kernel(const BwdPar
 }
 
 // ------------------------------------------------------------------------------------------
+// dK, dV with a full bias at D = 32, 128 and 256: 128 keys of one (batch, KV head) per
+// workgroup (64 at D = 256), query rows in steps of 128 (64 at D = 128 and 256). The first half
+// of the waves accumulate dV and the second half dK for the same 32-key groups, so each wave
+// holds one 32 x D accumulator. Both roles form S = Q.K^T with the same instructions (so their
+// P agree bit for bit); the dK waves also form dP = dO.V^T. The bias tile shares the 2-slot
+// ring's LDS; dkdv_lag_kernel below has no room for it at these head dims (reading the bias
+// per lane from HBM there instead made the call 2.7x to 4.5x slower).
+// ------------------------------------------------------------------------------------------
+template <int D, int MASK, int BIAS, bool OUT_F32>
+__global__ __launch_bounds__(64 * bwd_waves<D>(), 1) void dkdv_kernel(const BwdParams p) {
+    constexpr bool FB = BIAS == BIAS_FULL;
+    // keys per workgroup: 32 per dV / dK wave pair; query rows per step: 128 (64 with a full bias
+    // at D = 128, and at D = 256, whose tiles share the LDS)
+    constexpr int kWaves = bwd_waves<D>(), kThreads = 64 * kWaves, kBK = 32 * (kWaves / 2);
+    constexpr int kBQ = ((FB && D == 128) || D == 256) ? 64 : 128;
+    constexpr bool FB_LDS = FB && D != 256;      // D = 256: each lane reads its bias from HBM
+    constexpr int NB = kBQ / 32;
+    constexpr int CH = D / 8, KS = D / 16, DB = D / 32, QT = kBQ * D, BTILE = FB_LDS ? kBQ * kBK : 0;
+    constexpr bool IS_T5 = BIAS == BIAS_T5 || BIAS == BIAS_T5U;
+    constexpr bool ALIBI = BIAS == BIAS_ALIBI;
+    constexpr int kSat = BIAS == BIAS_T5U ? kT5USat : kT5Sat;
+    constexpr int kT5Pad = kSat + 64 + 31;
+    // LDS: slot sl holds the Q tile at [2 sl] and the dO tile at [2 sl + 1] (kBQ rows each),
+    // then (full bias) two bias slots of kBQ rows x 128 keys
+    __shared__ __attribute__((aligned(16))) uint16_t smem[4 * QT + 2 * BTILE];
+    __shared__ __attribute__((aligned(16))) float rowc[2][2][kBQ];    // [slot][lse2, D][row]
+    __shared__ float t5s[IS_T5 ? 2 * kT5Pad + 1 : 1];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int hh = lane >> 5, r32 = lane & 31;
+    const bool role_dk = uniform(wave >= kWaves / 2);
+    // workgroup -> (batch, KV head, key tile); with xcd_remap all key tiles of one (batch,
+    // KV head) run on one XCD (workgroup x is dispatched to XCD x % 8), where they share the
+    // Q / dO rows in that XCD's L2
+    int group, kt_idx;
+    {
+        const int x = blockIdx.x;
+        if (p.xcd_remap) {
+            const int slot = x >> 3, gl = slot / p.n_kt;
+            kt_idx = slot - gl * p.n_kt;
+            group = gl * 8 + (x & 7);
+        } else {
+            group = x / p.n_kt;
+            kt_idx = x - group * p.n_kt;
+        }
+    }
+    const int b = group / p.Hkv, kvh = group - b * p.Hkv;
+    const int Sq = p.Sq, Sk = p.Sk, off = p.off, G = p.G;
+    const int k0 = kt_idx * kBK;
+    const int kw0 = k0 + 32 * (wave % (kWaves / 2));   // first key of this wave
+    const int my_j = kw0 + r32;                // key of this lane
+    const bool key_ok = my_j < Sk;
+    const bool wave_ok = kw0 < Sk;
+    const int kwe = min(kw0 + 31, Sk - 1);     // last valid key of the wave
+
+    const size_t q_row = (size_t)p.Hq * D, kv_row = (size_t)p.Hkv * D;
+    const size_t kv_off = ((size_t)b * Sk + (key_ok ? my_j : 0)) * kv_row + (size_t)kvh * D;
+    char* out_row = (char*)(role_dk ? p.dk : p.dv) + kv_off * (OUT_F32 ? 4 : 2);
+
+    // query rows the workgroup's keys can see (positions of the rows: i + off)
+    const int kend = min(k0 + kBK, Sk) - 1;
+    int qlo = 0, qhi = Sq;
+    if constexpr (MASK != MASK_NONE) qlo = max(0, k0 - off);
+    if constexpr (MASK == MASK_SLIDING) qhi = min(Sq, kend + p.window - off);
+    const int s_begin = qlo / kBQ;
+    const int s_end = (qhi <= qlo) ? s_begin : (qhi + kBQ - 1) / kBQ;
+    const int nqs = s_end - s_begin;
+    const int n_steps = G * nqs;
+
+    if (n_steps == 0) {        // no query row sees these keys: dK = dV = 0
+        if (key_ok) store_zero_row<D, OUT_F32>(out_row, hh);
+        return;
+    }
+    const bool neg = p.scale_log2 < 0.f;
+    const float c_scale = neg ? -p.scale_log2 : (p.scale_log2 == 0.f ? kTinyScale : p.scale_log2);
+
+    // Q / dO tiles of step n: head h = kvh * G + n / nqs, rows kBQ s .. + kBQ - 1 (clamped)
+    constexpr int ROWS_PER_XFER = 1024 / (D * 2), XFERS = (kBQ * D * 2) / 1024, XPW = XFERS / kWaves;
+    static_assert(XPW * kWaves == XFERS, "dma split");
+    const uint32_t lds_base = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint16_t*)smem);
+    // A full bias goes through LDS when its rows split into whole 16-byte chunks: tile
+    // [kBQ rows][128 keys], 256-byte rows, chunk swizzle 4 * ((row >> 4) & 1); keys past the end
+    // of a partial last tile re-read the last whole chunk (they are masked).
+    const bool fb_dma = FB_LDS && ((Sk & 7) == 0);
+    constexpr int XPB = FB_LDS ? (BTILE * 2 / 1024) / kWaves : 0;
+    auto issue_step = [&](int n) {
+        const int sl = n & 1;
+        const int h = kvh * G + n / nqs;
+        const int i0 = (s_begin + n % nqs) * kBQ;
+        const uint16_t* qg = (const uint16_t*)p.q + ((size_t)b * Sq * p.Hq + h) * D;
+        const uint16_t* dg = (const uint16_t*)p.dout + ((size_t)b * Sq * p.Hq + h) * D;
+#pragma unroll
+        for (int x = 0; x < XPW; ++x) {
+            const int xi = wave * XPW + x;
+            const int row = xi * ROWS_PER_XFER + lane / CH;
+            const int i = min(i0 + row, Sq - 1);
+            const int ch = ((lane % CH) ^ swz<D>(row)) * 8;
+            dma16(qg + (size_t)i * q_row + ch, lds_base + (uint32_t)((2 * sl) * QT * 2 + xi * 1024));
+            dma16(dg + (size_t)i * q_row + ch, lds_base + (uint32_t)((2 * sl + 1) * QT * 2 + xi * 1024));
+        }
+        if constexpr (FB_LDS) {
+            if (fb_dma) {
+                const uint16_t* bg = (const uint16_t*)p.bias + ((size_t)b * p.Hq + h) * (size_t)Sq * Sk;
+                const int nchunk = min(kBK, Sk - k0) / 8;
+#pragma unroll
+                for (int x = 0; x < XPB; ++x) {
+                    const int xi = wave * XPB + x;
+                    const int row = xi * 4 + (lane >> 4);
+                    const int c = min((lane & 15) ^ (4 * ((row >> 4) & 1)), nchunk - 1);
+                    dma16(bg + (size_t)min(i0 + row, Sq - 1) * Sk + k0 + 8 * c,
+                          lds_base + (uint32_t)((4 * QT + sl * BTILE) * 2 + xi * 1024));
+                }
+            }
+        }
+        if (tid < kBQ) {
+            const int i = i0 + tid;
+            float l2 = INFINITY, dd = 0.f;
+            if (i < Sq) {
+                const size_t ri = ((size_t)b * p.Hq + h) * Sq + i;
+                const float l = p.lse[ri];
+                l2 = (l == -INFINITY) ? INFINITY : l * kLog2e;
+                dd = p.delta[ri];
+            }
+            rowc[sl][0][tid] = l2;
+            rowc[sl][1][tid] = dd;
+        }
+    };
+
+    // Lane-dependent LDS byte offsets inside a tile; block, group and slot offsets are
+    // compile-time constants added on top. Row-wise reads (A operand of S and dP): row
+    // perm32(r32) + 32 qb, chunk (2 ks + hh) ^ swz. Transposing reads (A operand of the
+    // dV / dK products): rows 16 hh + (li >> 2) (+4) + 8 sg + 32 qb, see read_tr.
+    uint32_t rr_off[KS], tr_off[2 * DB];
+    {
+        const int row = perm32(r32);
+        const int sw = swz<D>(row);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) rr_off[ks] = (uint32_t)(row * D + (((2 * ks + hh) ^ sw) << 3)) * 2;
+        const int li = lane & 15, la = li & 3, gg = lane >> 4;
+        const int trow = 16 * hh + (li >> 2);
+        const int dlo = 16 * DB * (gg & 1) + 8 * (la & 1) + 4 * (la >> 1);
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const int r = trow + 4 * half;
+            const int sw2 = swz<D>(r);
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                const int d = 16 * db + dlo;
+                tr_off[2 * db + half] = (uint32_t)(r * D + ((((d >> 3) ^ sw2) << 3) | (d & 7))) * 2;
+            }
+        }
+    }
+    const char* lds = (const char*)smem;
+
+    // The whole row loop of one role. Both roles run the same number of steps and barriers.
+    auto run = [&](auto role) {
+        constexpr bool DK = decltype(role)::value;
+        // K fragments (sign-flipped for a negative scale) and, for dK, V fragments of this
+        // lane's key: dims 16 ks + 8 hh .. + 7 (B operands of S = Q.K^T and dP = dO.V^T)
+        bf16x8 kf[KS], vf[DK ? KS : 1];
+        {
+            const uint16_t* kr = (const uint16_t*)p.k + kv_off + hh * 8;
+            const uint16_t* vr = (const uint16_t*)p.v + kv_off + hh * 8;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                u32x4 x = *(const u32x4*)(kr + ks * 16);
+                if (!key_ok) x = u32x4{0, 0, 0, 0};
+                if (neg) x ^= 0x80008000u;
+                kf[ks] = __builtin_bit_cast(bf16x8, x);
+                if constexpr (DK) {
+                    u32x4 y = *(const u32x4*)(vr + ks * 16);
+                    if (!key_ok) y = u32x4{0, 0, 0, 0};
+                    vf[ks] = __builtin_bit_cast(bf16x8, y);
+                }
+            }
+        }
+        f32x16 acc[DB];
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[db][v] = 0.f;
+
+        // one 32-row block (rows r0 = kBQ s + 32 QB ..) of step n in slot SL
+        auto compute_block = [&](int n, auto sl_tag, auto qb_tag) {
+            constexpr int SL = decltype(sl_tag)::value, QB = decltype(qb_tag)::value;
+            const int h = kvh * G + n / nqs;
+            const int r0 = (s_begin + n % nqs) * kBQ + 32 * QB;
+            const int pa = r0 + off, pb = min(r0 + 31, Sq - 1) + off;
+            bool skip = !wave_ok || r0 >= Sq;
+            if constexpr (MASK != MASK_NONE) skip = skip || (pb < kw0);
+            if constexpr (MASK == MASK_SLIDING) skip = skip || (pa - kwe >= p.window);
+            if (uniform(skip)) return;
+            bool m = (r0 + 31 >= Sq) || (kw0 + 31 >= Sk);
+            if constexpr (MASK != MASK_NONE) m = m || (pa < kwe);
+            if constexpr (MASK == MASK_SLIDING) m = m || (pb - kw0 >= p.window);
+            const bool msk = uniform(m);
+            constexpr uint32_t QTB = (2 * SL) * QT * 2, DTB = (2 * SL + 1) * QT * 2;   // tile bytes
+            constexpr uint32_t BLK = 32 * QB * D * 2;
+            f32x16 s, dp;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) { s[v] = 0.f; dp[v] = 0.f; }
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const bf16x8 aq = *(const bf16x8*)(lds + rr_off[ks] + (QTB + BLK));
+                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kf[ks], s, 0, 0, 0);
+                if constexpr (DK) {
+                    const bf16x8 ad = *(const bf16x8*)(lds + rr_off[ks] + (DTB + BLK));
+                    dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, vf[ks], dp, 0, 0, 0);
+                }
+            }
+            // register v of lane half hh: query row r0 + 16 hh + v, key my_j
+            const int rl = 32 * QB + 16 * hh;                      // row of register 0 in the tile
+            const int pos0 = r0 + 16 * hh + off;                   // its position
+            float x[16];
+            if constexpr (ALIBI) {
+                // rel = my_j - position of row v
+                const float aslope = ((const float*)p.bias)[h] * kLog2e;
+                const float base = (float)(my_j - pos0);
+#pragma unroll
+                for (int v = 0; v < 16; ++v) x[v] = fmaf(s[v], c_scale, -aslope * fabsf(base - (float)v));
+            } else if constexpr (IS_T5) {
+                const int rmin = kw0 - pb, rmax = kwe - pa;
+                const int side = uniform(rmin >= kSat ? 1 : (rmax <= -kSat ? -1 : 0));
+                if (side == 0) {
+                    // rel = my_j - position of row v; stays inside the padded table
+                    const float* trow = t5s + kT5Pad + (my_j - pos0);
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) x[v] = fmaf(s[v], c_scale, trow[-v]);
+                } else {
+                    const float bconst = side > 0 ? t5s[2 * kT5Pad] : t5s[0];
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) x[v] = fmaf(s[v], c_scale, bconst);
+                }
+            } else if constexpr (FB) {
+                if (FB_LDS && fb_dma) {
+                    // column my_j of rows rl .. rl + 15 of the bias tile (row bit 4 = hh)
+                    const int kk = my_j - k0;
+                    const uint16_t* bcol = smem + 4 * QT + SL * BTILE + rl * kBK +
+                                           ((((kk >> 3) ^ (4 * hh)) << 3) | (kk & 7));
+#pragma unroll
+                    for (int v = 0; v < 16; ++v)
+                        x[v] = fmaf(bf16_to_f32(bcol[v * kBK]), kLog2e, s[v] * c_scale);
+                } else {
+                    const uint16_t* br = (const uint16_t*)p.bias + ((size_t)b * p.Hq + h) * Sq * (size_t)Sk;
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        const int i = r0 + 16 * hh + v;
+                        const float bv = (i < Sq && key_ok) ? bf16_to_f32(br[(size_t)i * Sk + my_j]) : 0.f;
+                        x[v] = fmaf(bv, kLog2e, s[v] * c_scale);
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int v = 0; v < 16; ++v) x[v] = s[v] * c_scale;
+            }
+            if (msk) {
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int pos = pos0 + v;
+                    bool vis = key_ok & (pos - off < Sq);
+                    if constexpr (MASK != MASK_NONE) vis = vis & (my_j <= pos);
+                    if constexpr (MASK == MASK_SLIDING) vis = vis & (pos - my_j < p.window);
+                    x[v] = vis ? x[v] : -INFINITY;
+                }
+            }
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const u32x4 lr = *(const u32x4*)(&rowc[SL][0][rl + 4 * c]);
+                u32x4 dr;
+                if constexpr (DK) dr = *(const u32x4*)(&rowc[SL][1][rl + 4 * c]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int v = 4 * c + e;
+                    const float pv = __builtin_amdgcn_exp2f(x[v] - __uint_as_float(lr[e]));
+                    if constexpr (DK) s[v] = pv * (dp[v] - __uint_as_float(dr[e]));   // dS
+                    else s[v] = pv;                                                     // P
+                }
+            }
+            // dV^T += dO^T P  or  dK^T += Q^T dS, over the two 16-row groups of the block
+            constexpr uint32_t TTB = DK ? QTB : DTB;
+#pragma unroll
+            for (int sg = 0; sg < 2; ++sg) {
+                u32x4 pk;
+#pragma unroll
+                for (int c = 0; c < 4; ++c) pk[c] = pack_bf16x2(s[8 * sg + 2 * c], s[8 * sg + 2 * c + 1]);
+                const bf16x8 bp = __builtin_bit_cast(bf16x8, pk);
+                const uint32_t gofs = TTB + (uint32_t)((32 * QB + 8 * sg) * D * 2);
+#pragma unroll
+                for (int db = 0; db < DB; ++db) {
+                    const s16x4 lo = lds_read_tr((const uint16_t*)(lds + tr_off[2 * db] + gofs));
+                    const s16x4 hi = lds_read_tr((const uint16_t*)(lds + tr_off[2 * db + 1] + gofs));
+                    u32x4 av;
+                    av[0] = __builtin_bit_cast(u32x2, lo)[0];
+                    av[1] = __builtin_bit_cast(u32x2, lo)[1];
+                    av[2] = __builtin_bit_cast(u32x2, hi)[0];
+                    av[3] = __builtin_bit_cast(u32x2, hi)[1];
+                    acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), bp, acc[db], 0, 0, 0);
+                }
+            }
+        };
+
+        auto step = [&](int n, auto sl_tag) {
+            constexpr int SL = decltype(sl_tag)::value;
+            if constexpr (IS_T5) {
+                // table of head h when the head changes (no reader of the previous table is
+                // still running: the barrier ending the previous step, and one after the writes)
+                const int h = kvh * G + n / nqs;
+                if (n == 0 || h != kvh * G + (n - 1) / nqs) {
+                    const float* tbl = (const float*)p.bias + (size_t)h * kT5Buckets;
+                    for (int i = tid; i < 2 * kT5Pad + 1; i += kThreads)
+                        t5s[i] = tbl[BIAS == BIAS_T5U ? t5u_bucket(i - kT5Pad) : t5_bucket(i - kT5Pad)] * kLog2e;
+                    __syncthreads();
+                }
+            }
+            const bool has_next = n + 1 < n_steps;
+            if (has_next) issue_step(n + 1);
+            compute_block(n, sl_tag, std::integral_constant<int, 0>{});
+            compute_block(n, sl_tag, std::integral_constant<int, 1>{});
+            if constexpr (NB == 4) {
+                compute_block(n, sl_tag, std::integral_constant<int, 2>{});
+                compute_block(n, sl_tag, std::integral_constant<int, 3>{});
+            }
+            static_assert(NB == 2 || NB == 4, "two or four 32-row blocks per step");
+            if (has_next) dma_wait();
+            __syncthreads();
+        };
+#pragma unroll 1
+        for (int n = 0; n < n_steps; n += 2) {
+            step(n, std::integral_constant<int, 0>{});
+            if (n + 1 < n_steps) step(n + 1, std::integral_constant<int, 1>{});
+        }
+        if (key_ok) store_row<D, OUT_F32>(out_row, acc, DK ? p.scale : 1.f, hh);
+    };
+
+    issue_step(0);
+    dma_wait();
+    __syncthreads();
+    if (role_dk) run(std::true_type{});
+    else run(std::false_type{});
+}
+
+// ------------------------------------------------------------------------------------------
 // dK, dV: 128 keys of one (batch, KV head) per workgroup (64 at D = 256), query rows in steps
 // of 64 (128 at D = 32, 32 at D = 256) through a 3-slot LDS ring, scores formed once per
 // (row, key). The first half of the waves (dV) form S = Q.K^T and P for their
@@ -347,10 +692,11 @@ __global__ __launch_bounds__(64 * bwd_waves<D>(), 1) void dkdv_lag_kernel(const 
     constexpr int kSat = BIAS == BIAS_T5U ? kT5USat : kT5Sat;
     constexpr int kT5Pad = kSat + 64 + 31;
     constexpr bool FB = BIAS == BIAS_FULL;
-    // A full bias goes through the ring at D = 64 (a [kBQ rows][128 keys] tile per slot); at
-    // the other head dims the slots and the P buffers leave no room, and the dV waves read it
-    // per lane from HBM.
-    constexpr bool FB_LDS = FB && D == 64;
+    // A full bias (D = 64 only; dkdv_kernel takes it at the other head dims, where the slots
+    // and the P buffers leave no room for it) goes through the ring: a [kBQ rows][128 keys]
+    // tile per slot.
+    static_assert(!FB || D == 64, "full bias: D = 64 only");
+    constexpr bool FB_LDS = FB;
     constexpr int BTILE = FB_LDS ? kBQ * kBK : 0;
     // LDS: slot sl holds the Q tile at [2 sl] and the dO tile at [2 sl + 1] (kBQ rows each), the
     // bias tiles follow at [2 NS QT + sl BTILE]; P of slot sl, key group kg (the dV wave), row
@@ -711,7 +1057,10 @@ static hipError_t launch_grads(const BwdParams& p, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const unsigned gk = (unsigned)((size_t)p.B * p.Hkv * p.n_kt);
-    hipLaunchKernelGGL((dkdv_lag_kernel<D, MASK, BIAS, OUT_F32>), dim3(gk), dim3(64 * bwd_waves<D>()), 0, s, p);
+    if constexpr (BIAS != BIAS_FULL || D == 64)
+        hipLaunchKernelGGL((dkdv_lag_kernel<D, MASK, BIAS, OUT_F32>), dim3(gk), dim3(64 * bwd_waves<D>()), 0, s, p);
+    else
+        hipLaunchKernelGGL((dkdv_kernel<D, MASK, BIAS, OUT_F32>), dim3(gk), dim3(64 * bwd_waves<D>()), 0, s, p);
     return hipGetLastError();
 }
 

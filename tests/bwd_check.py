@@ -5,10 +5,11 @@ derived from the kernel's arithmetic, with u = 2^-8 (unit roundoff of bf16, roun
 even) and f = 2^-24 (fp32):
 
   * P and dS are rounded to bf16 once each as matrix-core operands (relative error <= u);
-    every product and sum after that is fp32. The dK/dV kernel forms P once and hands it
-    from the dV product to the dK product, so the dS of dK is formed from that bf16 P: its P
-    carries the extra rounding, and dK's bound uses the relative error of the rounded P in
-    place of that of the fp32 P; dQ's dS is formed from the fp32 P. The row constant rowsum(dO * O) uses the bf16
+    every product and sum after that is fp32. Where the dK/dV kernel forms P once and hands
+    it from the dV product to the dK product (every case but a full bias at head dims other
+    than 64), the dS of dK is formed from that bf16 P: its P carries the extra rounding, and
+    dK's bound uses the relative error of the rounded P in place of that of the fp32 P; dQ's
+    dS is formed from the fp32 P. The row constant rowsum(dO * O) uses the bf16
     forward output O~ that the caller passes in, so its error is sum_d |dO| |O~ - O| plus fp32
     rounding. P is recomputed from the forward's fp32 LSE, whose error |lse~ - lse| enters P
     as a relative error, as do the fp32 rounding of the score (D f sum |q k| |scale|) and of
@@ -61,6 +62,8 @@ def pair_reference(q, k, v, dout, o_gpu, lse_gpu, b, kvh, *, scale, mask_kind, w
     B, Sq, Hq, D = q.shape
     Sk, Hkv = k.shape[1], k.shape[2]
     G = Hq // Hkv
+    # the dK/dV kernel hands the bf16 P from the dV product to the dK product
+    p_handoff = bias_kind != oracle.BIAS_FULL or D == 64
     dq_ref, dk_ref, dv_ref = oracle.sdpa_backward(
         q, k, v, dout, scale=scale, mask_kind=mask_kind, window=window, bias_kind=bias_kind,
         bias=bias, kv_heads=[(b, kvh)])
@@ -99,9 +102,12 @@ def pair_reference(q, k, v, dout, o_gpu, lse_gpu, b, kvh, *, scale, mask_kind, w
         d_ds = eps_p * p * np.abs(dp - delta[:, None]) + p * (e_dp + e_delta[:, None])
         e_ds = (1 + U_BF16) * d_ds + U_BF16 * np.abs(ds)
         e_p = (eps_p + U_BF16 * (1 + eps_p)) * p
-        # dK's dS = rnd(rnd(P) (dP - D)): P's relative error is that of the bf16 operand
-        d_ds_k = e_p * np.abs(dp - delta[:, None]) + p * (e_dp + e_delta[:, None])
-        e_ds_k = (1 + U_BF16) * d_ds_k + U_BF16 * np.abs(ds)
+        if p_handoff:
+            # dK's dS = rnd(rnd(P) (dP - D)): P's relative error is that of the bf16 operand
+            d_ds_k = e_p * np.abs(dp - delta[:, None]) + p * (e_dp + e_delta[:, None])
+            e_ds_k = (1 + U_BF16) * d_ds_k + U_BF16 * np.abs(ds)
+        else:
+            e_ds_k = e_ds
         ads = np.abs(ds) + e_ds
         bq[:, g] = sc * (e_ds @ ak + Sk * F32 * (ads @ ak)) + F32 * np.abs(dq_ref[b, :, h])
         aq = np.abs(q_h)

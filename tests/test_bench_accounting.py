@@ -69,8 +69,10 @@ def test_blocks_are_exactly_those_with_a_visible_pair(mask, w, sq, sk):
 # ------------------------------------------------------------------------------------------
 def _kv_per_block(D, bias_kind):
     # MFMAs of one 32-row x 32-key block in the dk/dv kernel: the dV wave forms S (D/16) and
-    # dV (2 D/32); the dK wave takes the dV wave's P and forms dP (D/16) and dK (2 D/32)
-    return 2 * (D // 16 + 2 * (D // 32))
+    # dV (2 D/32); the dK wave forms dP (D/16) and dK (2 D/32), plus S itself (D/16) where P is
+    # not handed over (a full bias at head dims other than 64)
+    handoff = bias_kind != si.BIAS_FULL or D == 64
+    return (D // 16 + 2 * (D // 32)) + ((1 if handoff else 2) * (D // 16) + 2 * (D // 32))
 
 
 def test_bwd_unmasked_closed_form():

@@ -1,8 +1,8 @@
 """CPU checks of the gradient error bars in bwd_check.py (no GPU).
 
 An fp32 / bf16 emulation of the gradient kernels' rounding (scores and sums in fp32, P and dS
-rounded to bf16 before their products, dK's dS formed from the bf16 P that the dK/dV kernel
-hands over, the row constant from a bf16 forward output, P from an fp32 LSE) must pass both
+rounded to bf16 before their products, dK's dS formed from the bf16 P where the dK/dV kernel
+hands it over, the row constant from a bf16 forward output, P from an fp32 LSE) must pass both
 bars against the fp64 oracle; the same emulation with a planted
 mistake must fail at least one of them. This pins the bars from both sides: not tighter than
 the arithmetic allows, not so loose that a wrong gradient passes.
@@ -56,8 +56,10 @@ def emulate(q, k, v, dout, o16, lse32, b, kvh, scale, mask, window, bias_kind, b
         dp = do_h @ v_h.T
         ds = p * (dp - delta[:, None])
         pb, dsb = bf16(p), bf16(ds)
-        # the dK/dV kernel forms P once and the dK product's dS takes that bf16 P
-        dsb_k = bf16(pb * (dp - delta[:, None]))
+        # the dK/dV kernel forms P once and the dK product's dS takes that bf16 P (except with
+        # a full bias at head dims other than 64)
+        handoff = bias_kind != oracle.BIAS_FULL or D == 64
+        dsb_k = bf16(pb * (dp - delta[:, None])) if handoff else dsb
         kk = np.roll(k_h, 1, axis=0) if plant == "dq_key_shift" else k_h
         dq[:, g] = np.float32(scale) * (dsb @ kk)
         dk += (np.float32(1.0) if plant == "dk_no_scale" else np.float32(scale)) * (dsb_k.T @ q_h)
