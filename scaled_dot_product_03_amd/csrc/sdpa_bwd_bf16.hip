@@ -339,23 +339,18 @@ __global__ __launch_bounds__(64 * bwd_waves<D>(), 1) void dq_kernel(const BwdPar
 // ------------------------------------------------------------------------------------------
 template <int D, int MASK, int BIAS, bool OUT_F32>
 __global__ __launch_bounds__(64 * bwd_waves<D>(), 1) void dkdv_kernel(const BwdParams p) {
-    constexpr bool FB = BIAS == BIAS_FULL;
-    // keys per workgroup: 32 per dV / dK wave pair; query rows per step: 128 (64 with a full bias
-    // at D = 128, and at D = 256, whose tiles share the LDS)
-    constexpr int kWaves = bwd_waves<D>(), kThreads = 64 * kWaves, kBK = 32 * (kWaves / 2);
-    constexpr int kBQ = ((FB && D == 128) || D == 256) ? 64 : 128;
-    constexpr bool FB_LDS = FB && D != 256;      // D = 256: each lane reads its bias from HBM
+    static_assert(BIAS == BIAS_FULL && D != 64, "full bias at D = 32, 128, 256 only");
+    // keys per workgroup: 32 per dV / dK wave pair; query rows per step: 128 (64 at D = 128 and
+    // 256, whose tiles share the LDS with the bias tiles)
+    constexpr int kWaves = bwd_waves<D>(), kBK = 32 * (kWaves / 2);
+    constexpr int kBQ = (D == 128 || D == 256) ? 64 : 128;
+    constexpr bool FB_LDS = D != 256;      // D = 256: each lane reads its bias from HBM
     constexpr int NB = kBQ / 32;
     constexpr int CH = D / 8, KS = D / 16, DB = D / 32, QT = kBQ * D, BTILE = FB_LDS ? kBQ * kBK : 0;
-    constexpr bool IS_T5 = BIAS == BIAS_T5 || BIAS == BIAS_T5U;
-    constexpr bool ALIBI = BIAS == BIAS_ALIBI;
-    constexpr int kSat = BIAS == BIAS_T5U ? kT5USat : kT5Sat;
-    constexpr int kT5Pad = kSat + 64 + 31;
     // LDS: slot sl holds the Q tile at [2 sl] and the dO tile at [2 sl + 1] (kBQ rows each),
-    // then (full bias) two bias slots of kBQ rows x 128 keys
+    // then two bias slots of kBQ rows x 128 keys
     __shared__ __attribute__((aligned(16))) uint16_t smem[4 * QT + 2 * BTILE];
     __shared__ __attribute__((aligned(16))) float rowc[2][2][kBQ];    // [slot][lse2, D][row]
-    __shared__ float t5s[IS_T5 ? 2 * kT5Pad + 1 : 1];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int hh = lane >> 5, r32 = lane & 31;
@@ -543,26 +538,7 @@ __global__ __launch_bounds__(64 * bwd_waves<D>(), 1) void dkdv_kernel(const BwdP
             const int rl = 32 * QB + 16 * hh;                      // row of register 0 in the tile
             const int pos0 = r0 + 16 * hh + off;                   // its position
             float x[16];
-            if constexpr (ALIBI) {
-                // rel = my_j - position of row v
-                const float aslope = ((const float*)p.bias)[h] * kLog2e;
-                const float base = (float)(my_j - pos0);
-#pragma unroll
-                for (int v = 0; v < 16; ++v) x[v] = fmaf(s[v], c_scale, -aslope * fabsf(base - (float)v));
-            } else if constexpr (IS_T5) {
-                const int rmin = kw0 - pb, rmax = kwe - pa;
-                const int side = uniform(rmin >= kSat ? 1 : (rmax <= -kSat ? -1 : 0));
-                if (side == 0) {
-                    // rel = my_j - position of row v; stays inside the padded table
-                    const float* trow = t5s + kT5Pad + (my_j - pos0);
-#pragma unroll
-                    for (int v = 0; v < 16; ++v) x[v] = fmaf(s[v], c_scale, trow[-v]);
-                } else {
-                    const float bconst = side > 0 ? t5s[2 * kT5Pad] : t5s[0];
-#pragma unroll
-                    for (int v = 0; v < 16; ++v) x[v] = fmaf(s[v], c_scale, bconst);
-                }
-            } else if constexpr (FB) {
+            {
                 if (FB_LDS && fb_dma) {
                     // column my_j of rows rl .. rl + 15 of the bias tile (row bit 4 = hh)
                     const int kk = my_j - k0;
@@ -580,9 +556,6 @@ __global__ __launch_bounds__(64 * bwd_waves<D>(), 1) void dkdv_kernel(const BwdP
                         x[v] = fmaf(bv, kLog2e, s[v] * c_scale);
                     }
                 }
-            } else {
-#pragma unroll
-                for (int v = 0; v < 16; ++v) x[v] = s[v] * c_scale;
             }
             if (msk) {
 #pragma unroll
@@ -631,18 +604,6 @@ __global__ __launch_bounds__(64 * bwd_waves<D>(), 1) void dkdv_kernel(const BwdP
         };
 
         auto step = [&](int n, auto sl_tag) {
-            constexpr int SL = decltype(sl_tag)::value;
-            if constexpr (IS_T5) {
-                // table of head h when the head changes (no reader of the previous table is
-                // still running: the barrier ending the previous step, and one after the writes)
-                const int h = kvh * G + n / nqs;
-                if (n == 0 || h != kvh * G + (n - 1) / nqs) {
-                    const float* tbl = (const float*)p.bias + (size_t)h * kT5Buckets;
-                    for (int i = tid; i < 2 * kT5Pad + 1; i += kThreads)
-                        t5s[i] = tbl[BIAS == BIAS_T5U ? t5u_bucket(i - kT5Pad) : t5_bucket(i - kT5Pad)] * kLog2e;
-                    __syncthreads();
-                }
-            }
             const bool has_next = n + 1 < n_steps;
             if (has_next) issue_step(n + 1);
             compute_block(n, sl_tag, std::integral_constant<int, 0>{});
