@@ -9,14 +9,18 @@ D=128, bf16, sliding window 4096 (= seqlen, i.e. exactly causal).
 
 Prints ONE JSON line on stdout. `value` is effective TFLOP/s: 4*D flop per visible
 (query, key) pair (Q.K^T and P.V), masked pairs excluded, exps not counted. Timing: W untimed
-warmup launches, then exactly K launches bracketed by device synchronisation (wall clock, plus
-one HIP event pair on the launch stream); then K more launches each bracketed by HIP events on
-that stream give the per-launch kernel duration used for the roofline (the
-repeat-with-device-sync method of the "jax-gpu-05-attention-gpu" codelab, section 8). The CPU
-baseline is the fp64 oracle timed on the same workload on this host's cores.
+warmup launches, then untimed settle launches in batches of 10 until two consecutive batch
+medians agree within 1 % (at least 0.5 s; the GPU clocks ramp up after idling), then exactly K
+launches bracketed by device synchronisation (wall clock: `value`, `ms_per_step`), each of them
+also bracketed by HIP events on the launch stream (average kernel duration: `roofline`). This
+is the repeat-with-device-sync method of the "jax-gpu-05-attention-gpu" codelab, section 8.
+The line's `sweep` object carries the same measurement for the other target workloads (the
+S = 8192 sliding window and its full-causal comparison, the T5 encoder with bucketed and full
+bias, the head-sharing sweep, the tiny fp32 case). The CPU baseline is the fp64 oracle timed on
+the same workload on this host's cores.
 
---sweep additionally times every other workload and prints one JSON line per workload on
-stderr.
+--sweep additionally times the extra bias kinds and head dims and prints one JSON line per
+workload on stderr; --no-sweep times the headline workload only.
 
 --decode measures the split-key decode instead (default workload: one new query row per head
 against a 16384-key cache, B16, Mistral-7B heads): a step is one sdpa_decode call (split
@@ -115,16 +119,69 @@ def to_device(inp: si.Inputs):
     return dev(inp.q), dev(inp.k), dev(inp.v), bias
 
 
+def settle(launch, stream, warmup: int, min_s: float = 0.5, max_s: float = 4.0,
+           batch: int = 10, tol: float = 0.01) -> int:
+    """Untimed launches until the GPU clocks have settled: `warmup` launches, then batches of
+    `batch` launches, each timed with HIP events on the launch stream, until two consecutive
+    batch medians agree within `tol` and at least `min_s` seconds have passed (at most
+    `max_s`). Clocks ramp up over the first launches after the GPU idles; without this the
+    ramp would fall inside the timed region. Returns the number of launches after `warmup`."""
+    import torch
+    for _ in range(warmup):
+        launch()
+    torch.cuda.synchronize()
+    n, prev = 0, None
+    t0 = time.perf_counter()
+    while True:
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(batch)]
+        ends = [torch.cuda.Event(enable_timing=True) for _ in range(batch)]
+        for i in range(batch):
+            starts[i].record(stream)
+            launch()
+            ends[i].record(stream)
+        torch.cuda.synchronize()
+        n += batch
+        med = float(np.median([a.elapsed_time(b) for a, b in zip(starts, ends)]))
+        el = time.perf_counter() - t0
+        if prev is not None and abs(med - prev) <= tol * prev and el >= min_s:
+            return n
+        if el >= max_s:
+            return n
+        prev = med
+
+
+def timed_launches(launch, stream, steps: int):
+    """Exactly `steps` launches between two device synchronisations (wall clock), each
+    bracketed by HIP events on the launch stream (per-launch kernel duration). The events are
+    recorded inside the timed region, so both statistics describe the same launches."""
+    import torch
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record(stream)
+        launch()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev = np.array([a.elapsed_time(b) for a, b in zip(starts, ends)])
+    return dict(ms_per_step=1e3 * wall / steps, kernel_ms_avg=float(ev.mean()),
+                kernel_ms_median=float(np.median(ev)), kernel_ms_min=float(ev.min()),
+                kernel_ms_max=float(ev.max()))
+
+
 def time_workload(sdpa, wl: si.Workload, steps: int, warmup: int, bwd: bool = False,
                   decode: bool = False):
-    """Returns dict with ms_per_step (wall, synchronised), kernel_ms_avg / median (events).
-    With bwd, a step is one gradient call (dQ, dK, dV) instead of one forward; with decode,
-    one split-key decode call."""
+    """Returns dict with ms_per_step (wall, synchronised), kernel_ms_avg / median (events over
+    the same launches) and the number of settle launches. With bwd, a step is one gradient
+    call (dQ, dK, dV) instead of one forward; with decode, one split-key decode call."""
     import torch
     inp = si.make_inputs(wl)
     q, k, v, bias = to_device(inp)
     del inp
-    out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    odt = torch.float32 if wl.dtype == "f32" else q.dtype
+    out = torch.empty(q.shape, dtype=odt, device=q.device)
     lse = torch.empty((wl.B, wl.Hq, wl.Sq), dtype=torch.float32, device=q.device)
     stream = torch.cuda.current_stream()
     kw = dict(scale=wl.scale, mask=wl.mask_kind, window=wl.window, bias_kind=wl.bias_kind,
@@ -148,36 +205,12 @@ def time_workload(sdpa, wl: si.Workload, steps: int, warmup: int, bwd: bool = Fa
         def launch():
             sdpa.fwd(q, k, v, out=out, lse=lse, **kw)
 
-    for _ in range(warmup):
-        launch()
-    torch.cuda.synchronize()
-    # timed region: exactly `steps` launches between two device synchronisations, plus one
-    # event pair on the launch stream around them
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(steps):
-        launch()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    region_ms = ev0.elapsed_time(ev1)
-    # per-launch durations (separate pass, events bracketing each launch on the same stream)
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    for i in range(steps):
-        starts[i].record(stream)
-        launch()
-        ends[i].record(stream)
-    torch.cuda.synchronize()
-    ev = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
+    n_settle = settle(launch, stream, warmup)
+    t = timed_launches(launch, stream, steps)
+    t["settle_launches"] = n_settle
     del q, k, v, bias, out, lse, launch
     torch.cuda.empty_cache()
-    return dict(ms_per_step=1e3 * wall / steps, region_ms_per_step=region_ms / steps,
-                kernel_ms_avg=float(ev.mean()), kernel_ms_median=float(np.median(ev)),
-                kernel_ms_min=float(ev.min()))
+    return t
 
 
 def cpu_baseline(wl: si.Workload, budget_s: float = 12.0):
@@ -303,9 +336,10 @@ def tile_flops(wl: si.Workload) -> float:
     """FLOP of the matrix work the bf16 kernel performs: 4*D per (row, key) slot of every block
     of 32 query rows x 64 keys it computes, masked slots included. Follows the kernel's tile
     plan: the key range of each 256-row work item, minus the 64-key tiles that a 32-row wave
-    skips because the mask hides them completely. One such block is 32*D/8 MFMAs of
-    v_mfma_f32_32x32x16_bf16 (32768 flop each), so rocprofv3's SQ_INSTS_MFMA times 32768 must
-    equal this count (the profile summary checks it)."""
+    skips because the mask hides them completely. One such block is D/4 MFMAs of
+    v_mfma_f32_32x32x16_bf16 (32768 flop each: D/8 for the two 32-key halves of S, D/8 for
+    the D/32 head-dim blocks of P.V over four 16-key groups), so rocprofv3's SQ_INSTS_MFMA
+    times 32768 must equal this count (the profile summaries check it)."""
     off = wl.Sk - wl.Sq
     blocks = 0
     for q0 in range(0, wl.Sq, 256):
@@ -414,7 +448,10 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=None, choices=sorted(si.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--sweep", action="store_true")
+    ap.add_argument("--sweep", action="store_true",
+                    help="also time the extra bias kinds and head dims (stderr)")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="time the headline workload only (no 'sweep' object in the line)")
     ap.add_argument("--bwd", action="store_true",
                     help="time the gradient call (dQ, dK, dV) instead of the forward")
     ap.add_argument("--decode", action="store_true",
@@ -468,6 +505,7 @@ def main(argv=None):
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_launches": t["settle_launches"],
         "ms_per_step": round(t["ms_per_step"], 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -478,44 +516,66 @@ def main(argv=None):
         "config": {**wl.describe(), "effective_gflop": round(flops / 1e9, 2),
                    "tile_gflop": round(tile_flops(wl) / 1e9, 2),
                    "tile_tflops": round(tile_flops(wl) / (t["kernel_ms_avg"] * 1e-3) / 1e12, 2),
+                   "kernel_ms_avg": round(t["kernel_ms_avg"], 4),
                    "kernel_ms_median": round(t["kernel_ms_median"], 4),
-                   "event_ms_per_step": round(t["region_ms_per_step"], 4),
+                   "wall_over_kernel": round(t["ms_per_step"] / t["kernel_ms_avg"], 4),
                    "hbm_gbs_algorithmic": round(si.algorithmic_bytes(wl) /
                                                 (t["kernel_ms_avg"] * 1e-3) / 1e9, 1)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic},
     }
+    if not args.no_sweep:
+        line["sweep"] = sweep_forward(sdpa, SWEEP_DEFAULT, args.steps, args.warmup)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(line), flush=True)
 
     if args.sweep:
-        ms = {}
-        for key in ["c2", "c2c", "c3", "c3c", "c4t5", "c4full", "c5mha", "c5gqa", "c5mqa",
-                    "c2alibi", "c4t5u", "c2d32", "c2d256"]:
-            w2 = si.WORKLOADS[key]
-            # at least 30 warmup launches: clocks ramp up over ~15 launches after the GPU idles
-            t2 = time_workload(sdpa, w2, max(5, args.steps // 2), max(30, args.warmup))
-            f2, a2 = report(w2, t2)
-            ms[key] = t2["kernel_ms_median"]
-            rec = {"workload": key, **w2.describe(), "kernel_ms_avg": round(t2["kernel_ms_avg"], 4),
-                   "kernel_ms_median": round(t2["kernel_ms_median"], 4),
-                   "effective_tflops": round(a2, 2),
-                   "pct_of_bf16_peak": round(100 * a2 / PEAK_BF16_TFLOPS, 2),
-                   "tile_tflops": round(tile_flops(w2) / (t2["kernel_ms_avg"] * 1e-3) / 1e12, 2),
-                   "hbm_gbs_algorithmic": round(si.algorithmic_bytes(w2) /
-                                                (t2["kernel_ms_avg"] * 1e-3) / 1e9, 1)}
-            print(json.dumps(rec), file=sys.stderr, flush=True)
-        # sliding window 4096 at S = 4096 is exactly causal: same work, same time expected;
-        # at S = 8192 the window keeps 0.750 of the causal pairs
-        for a, b, note in [("c2", "c2c", "sliding(4096) / causal at S=4096, expect 1.0"),
-                           ("c3", "c3c", "sliding(4096) / causal at S=8192; visible pairs 0.750")]:
-            print(json.dumps({"comparison": note, "time_ratio": round(ms[a] / ms[b], 4),
-                              "pairs_ratio": round(si.effective_flops(si.WORKLOADS[a]) /
-                                                   si.effective_flops(si.WORKLOADS[b]), 4)}),
+        for key in SWEEP_EXTRA:
+            rec = sweep_forward(sdpa, [key], args.steps, args.warmup)[key]
+            print(json.dumps({"workload": key, **si.WORKLOADS[key].describe(), **rec}),
                   file=sys.stderr, flush=True)
     return 0
+
+
+# the other target workloads, timed in the default run and carried in the line's "sweep"
+# object: c2c (the causal twin of the headline), the S = 8192 sliding window and its full-
+# causal comparison, the T5 encoder with bucketed and with full bias, the head-sharing sweep,
+# and the tiny fp32 case
+SWEEP_DEFAULT = ["c2c", "c3", "c3c", "c4t5", "c4full", "c5mha", "c5gqa", "c5mqa", "c1"]
+# more index-generated biases and head dims (--sweep, printed on stderr)
+SWEEP_EXTRA = ["c2alibi", "c4t5u", "c2d32", "c2d256"]
+
+
+def sweep_forward(sdpa, keys, steps: int, warmup: int) -> dict:
+    """Times each workload like the headline (settle, then `steps` launches with per-launch
+    events) and returns {key: record}; adds the sliding/causal time ratios when both sides
+    were timed."""
+    out = {}
+    for key in keys:
+        w2 = si.WORKLOADS[key]
+        t2 = time_workload(sdpa, w2, steps, warmup)
+        f2, a2 = report(w2, t2)
+        rec = {"kernel_ms_avg": round(t2["kernel_ms_avg"], 4),
+               "kernel_ms_median": round(t2["kernel_ms_median"], 4),
+               "effective_tflops": round(a2, 2),
+               "pct_of_bf16_peak": round(100 * a2 / PEAK_BF16_TFLOPS, 2),
+               "hbm_gbs_algorithmic": round(si.algorithmic_bytes(w2) /
+                                            (t2["kernel_ms_avg"] * 1e-3) / 1e9, 1),
+               "settle_launches": t2["settle_launches"]}
+        if w2.dtype == "bf16":
+            rec["tile_tflops"] = round(tile_flops(w2) / (t2["kernel_ms_avg"] * 1e-3) / 1e12, 2)
+        out[key] = rec
+    # a sliding window of 4096 at S = 8192 keeps 0.750 of the causal pairs
+    if "c3" in out and "c3c" in out:
+        out["c3_over_c3c"] = {
+            "time_ratio": round(out["c3"]["kernel_ms_avg"] / out["c3c"]["kernel_ms_avg"], 4),
+            "pairs_ratio": round(si.effective_flops(si.WORKLOADS["c3"]) /
+                                 si.effective_flops(si.WORKLOADS["c3c"]), 4),
+            "tile_ratio": round(tile_flops(si.WORKLOADS["c3"]) /
+                                tile_flops(si.WORKLOADS["c3c"]), 4)}
+    return out
 
 
 def time_varlen(sdpa, wl, steps: int, warmup: int):
@@ -534,24 +594,10 @@ def time_varlen(sdpa, wl, steps: int, warmup: int):
     def launch():
         sdpa.fwd_varlen(q, k, v, cq, ck, m, m, scale=wl.scale, mask=wl.mask_kind,
                         window=wl.window, out=out, lse=lse, stream=stream.cuda_stream)
-    for _ in range(warmup):
-        launch()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        launch()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    for i in range(steps):
-        starts[i].record(stream)
-        launch()
-        ends[i].record(stream)
-    torch.cuda.synchronize()
-    ev = np.array([a.elapsed_time(b) for a, b in zip(starts, ends)])
-    return dict(ms_per_step=1e3 * wall / steps, kernel_ms_avg=float(ev.mean()),
-                kernel_ms_median=float(np.median(ev)))
+    n_settle = settle(launch, stream, warmup)
+    t = timed_launches(launch, stream, steps)
+    t["settle_launches"] = n_settle
+    return t
 
 
 def cpu_baseline_varlen(wl, budget_s: float = 12.0):
@@ -602,7 +648,8 @@ def main_varlen(sdpa, wl, args) -> int:
         "metric": "attention fwd over packed sequences, effective TFLOP/s (visible pairs of "
                   "every sequence) + % of bf16 MFMA peak",
         "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(t["ms_per_step"], 4),
+        "warmup": args.warmup, "settle_launches": t["settle_launches"],
+        "ms_per_step": round(t["ms_per_step"], 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic", "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "config": {**wl.describe(), "effective_gflop": round(flops / 1e9, 2),
@@ -629,6 +676,7 @@ def main_decode(sdpa, wl: si.Workload, args) -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_launches": t["settle_launches"],
         "ms_per_step": round(t["ms_per_step"], 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -639,7 +687,7 @@ def main_decode(sdpa, wl: si.Workload, args) -> int:
         "config": {**wl.describe(), "pass": "decode (split keys + merge)",
                    "algorithmic_mb": round(nbytes / 1e6, 2),
                    "call_ms_median": round(t["kernel_ms_median"], 4),
-                   "event_ms_per_step": round(t["region_ms_per_step"], 4)},
+                   "call_ms_avg": round(t["kernel_ms_avg"], 4)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": load_traffic(wl.name, decode=True),
@@ -651,7 +699,7 @@ def main_decode(sdpa, wl: si.Workload, args) -> int:
     if args.sweep:
         for key in ["dec", "decmqa", "decsw", "decd256"]:
             w2 = si.WORKLOADS[key]
-            t2 = time_workload(sdpa, w2, max(5, args.steps // 2), max(30, args.warmup),
+            t2 = time_workload(sdpa, w2, args.steps, args.warmup,
                                decode=True)
             nb = si.algorithmic_bytes_decode(w2)
             rec = {"workload": key, "pass": "decode", **w2.describe(),
@@ -675,6 +723,7 @@ def main_bwd(sdpa, wl: si.Workload, args) -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_launches": t["settle_launches"],
         "ms_per_step": round(t["ms_per_step"], 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -685,7 +734,7 @@ def main_bwd(sdpa, wl: si.Workload, args) -> int:
         "config": {**wl.describe(), "pass": "backward (dQ, dK, dV)",
                    "effective_gflop": round(flops / 1e9, 2),
                    "call_ms_median": round(t["kernel_ms_median"], 4),
-                   "event_ms_per_step": round(t["region_ms_per_step"], 4),
+                   "call_ms_avg": round(t["kernel_ms_avg"], 4),
                    "hbm_gbs_algorithmic": round(si.algorithmic_bytes_bwd(wl) /
                                                 (t["kernel_ms_avg"] * 1e-3) / 1e9, 1)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
@@ -700,7 +749,7 @@ def main_bwd(sdpa, wl: si.Workload, args) -> int:
         for key in ["c2", "c3", "c3c", "c4t5", "c4full", "c5mha", "c5gqa", "c5mqa", "c2alibi",
                     "c4t5u", "c2d32", "c2d256"]:
             w2 = si.WORKLOADS[key]
-            t2 = time_workload(sdpa, w2, max(5, args.steps // 2), max(30, args.warmup), bwd=True)
+            t2 = time_workload(sdpa, w2, args.steps, args.warmup, bwd=True)
             f2, a2 = report(w2, t2, bwd=True)
             rec = {"workload": key, "pass": "backward", **w2.describe(),
                    "call_ms_avg": round(t2["kernel_ms_avg"], 4),

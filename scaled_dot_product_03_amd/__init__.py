@@ -159,9 +159,32 @@ def _check_qkv(q, k, v):
     if q.dtype != k.dtype or q.dtype != v.dtype:
         raise ValueError("q, k, v must share a dtype")
     for t in (q, k, v):
-        if not t.is_cuda or not t.is_contiguous():
-            raise ValueError("q, k, v must be contiguous cuda tensors")
+        if not t.is_cuda or not t.is_contiguous() or t.device != q.device:
+            raise ValueError("q, k, v must be contiguous cuda tensors on one device")
     return B, Sq, Hq, D, Sk, Hkv
+
+
+def _check_buf(t, name, shape, dtype, device):
+    """A caller-supplied output or workspace tensor: it must have exactly the shape and dtype
+    the entry point writes, live on the inputs' device and be contiguous. The C ABI only sees
+    a raw pointer, so this is the last place a wrong buffer can be caught before the kernels
+    write through it."""
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or t.device != device \
+            or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape "
+                         f"{list(shape)} on {device} (got {t.dtype} {list(t.shape)} on "
+                         f"{t.device}, contiguous={t.is_contiguous()})")
+    return t
+
+
+def _check_ws(t, name, nbytes, device):
+    """A caller-supplied workspace: contiguous, on the inputs' device, at least `nbytes`."""
+    have = t.numel() * t.element_size()
+    if t.device != device or not t.is_contiguous() or have < nbytes:
+        raise ValueError(f"{name} must be a contiguous tensor of at least {nbytes} bytes on "
+                         f"{device} (got {have} bytes on {t.device}, "
+                         f"contiguous={t.is_contiguous()})")
+    return t
 
 
 def _bias_ptr(bk, bias, dtype, B, Hq, Sq, Sk):
@@ -221,8 +244,10 @@ def fwd(q, k, v, *, scale: Optional[float] = None, mask="causal", window: int = 
     bias_ptr = _bias_ptr(bk, bias, q.dtype, B, Hq, Sq, Sk)
     if out is None:
         out = torch.empty((B, Sq, Hq, D), dtype=odt, device=q.device)
+    _check_buf(out, "out", (B, Sq, Hq, D), odt, q.device)
     if lse is None:
         lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    _check_buf(lse, "lse", (B, Hq, Sq), torch.float32, q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
     st = getattr(L, entry)(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
@@ -248,12 +273,9 @@ def bwd(q, k, v, out, lse, dout, *, scale: Optional[float] = None, mask="causal"
     B, Sq, Hq, D, Sk, Hkv = _check_qkv(q, k, v)
     if q.dtype != torch.bfloat16:
         raise ValueError("the backward takes bf16 q, k, v")
-    for t, name in ((out, "out"), (dout, "dout")):
-        if t.dtype != torch.bfloat16 or tuple(t.shape) != (B, Sq, Hq, D) or not t.is_cuda \
-                or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous cuda bf16 [B, Sq, Hq, D] tensor")
-    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, Sq) or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous fp32 [B, Hq, Sq] tensor")
+    _check_buf(out, "out", (B, Sq, Hq, D), torch.bfloat16, q.device)
+    _check_buf(dout, "dout", (B, Sq, Hq, D), torch.bfloat16, q.device)
+    _check_buf(lse, "lse", (B, Hq, Sq), torch.float32, q.device)
     mk = _kind(mask, _MASKS, "mask")
     bk = _kind(bias_kind, _BIASES, "bias kind")
     if scale is None:
@@ -269,8 +291,14 @@ def bwd(q, k, v, out, lse, dout, *, scale: Optional[float] = None, mask="causal"
         dk = torch.empty((B, Sk, Hkv, D), dtype=gdt, device=q.device)
     if dv is None:
         dv = torch.empty((B, Sk, Hkv, D), dtype=gdt, device=q.device)
+    _check_buf(dq, "dq", (B, Sq, Hq, D), gdt, q.device)
+    _check_buf(dk, "dk", (B, Sk, Hkv, D), gdt, q.device)
+    _check_buf(dv, "dv", (B, Sk, Hkv, D), gdt, q.device)
     if ws is None:
         ws = torch.empty((B * Hq * Sq,), dtype=torch.float32, device=q.device)
+    if ws.dtype != torch.float32:
+        raise ValueError("ws must be an fp32 tensor")
+    _check_ws(ws, "ws", 4 * B * Hq * Sq, q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
     st = getattr(L, entry)(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
@@ -306,10 +334,13 @@ def decode(q, k, v, *, scale: Optional[float] = None, mask="causal", window: int
     need = decode_ws_bytes(B, Hq, Hkv, Sq, Sk, D)
     if ws is None:
         ws = torch.empty((max(need, 16),), dtype=torch.uint8, device=q.device)
+    _check_ws(ws, "ws", need, q.device)
     if out is None:
         out = torch.empty((B, Sq, Hq, D), dtype=odt, device=q.device)
+    _check_buf(out, "out", (B, Sq, Hq, D), odt, q.device)
     if lse is None:
         lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    _check_buf(lse, "lse", (B, Hq, Sq), torch.float32, q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
     st = getattr(L, entry)(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
@@ -353,10 +384,14 @@ def fwd_varlen(q, k, v, cu_q, cu_k, max_seqlen_q: int, max_seqlen_k: int, *,
     if bk == BIAS_FULL:
         raise ValueError("packed sequences take no full bias")
     bias_ptr = _bias_ptr(bk, bias, q.dtype, 1, Hq, 1, 1)
+    if odt not in (torch.bfloat16, torch.float32):
+        raise ValueError("out_dtype must be bf16 or fp32")
     if out is None:
         out = torch.empty((total_q, Hq, D), dtype=odt, device=q.device)
+    _check_buf(out, "out", (total_q, Hq, D), odt, q.device)
     if lse is None:
         lse = torch.empty((Hq, total_q), dtype=torch.float32, device=q.device)
+    _check_buf(lse, "lse", (Hq, total_q), torch.float32, q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
     st = getattr(L, entry)(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),

@@ -14,9 +14,11 @@ pytestmark = pytest.mark.gpu
 W = si.WORKLOADS
 
 
-@pytest.mark.parametrize("key", ["c5gqa", "c5mqa", "c2", "c3", "c4t5", "c4full", "c2d32",
-                                 "c2d256"])
+@pytest.mark.parametrize("key", ["c1", "c2", "c3", "c3c", "c4t5", "c4full", "c5mha", "c5gqa",
+                                 "c5mqa", "c2d32", "c2d256"])
 def test_bitwise_determinism_100_runs(gpu_lib, key):
+    """Every workload at full size, in the launch the benchmark times (c1 runs the fp32
+    entry point, the others the bf16 one)."""
     import torch
     wl = W[key]
     inp = si.make_inputs(wl)
@@ -28,7 +30,8 @@ def test_bitwise_determinism_100_runs(gpu_lib, key):
         o, l = run_gpu(gpu_lib, wl, dev)
         same = same and torch.equal(o, o0) and torch.equal(l, l0)
     assert same
-    h = int(torch.sum(o0.view(torch.int16).to(torch.int64) * 1000003 % 65521).item())
+    words = o0.view(torch.int32) if o0.dtype == torch.float32 else o0.view(torch.int16)
+    h = int(torch.sum(words.to(torch.int64) * 1000003 % 65521).item())
     print(f"{key}: deterministic over 100 runs, out checksum {h}")
 
 

@@ -289,6 +289,72 @@ def check_invariants():
     assert np.max(np.abs(o1 - o2)) <= 1e-12
 
 
+def brute_force_weights(q_rows, k_head, q_pos, scale, mask, window, bias_rows):
+    """Softmax weights P [n, Sk] by plain Python loops (same visibility rules as brute_force)."""
+    n, D = q_rows.shape
+    Sk = k_head.shape[0]
+    P = np.zeros((n, Sk))
+    for i in range(n):
+        pos = int(q_pos[i])
+        vis = []
+        for j in range(Sk):
+            if mask == 1 and j > pos:
+                continue
+            if mask == 2 and (j > pos or pos - j >= window):
+                continue
+            s = sum(float(q_rows[i, d]) * float(k_head[j, d]) for d in range(D)) * scale
+            if bias_rows is not None:
+                s += float(bias_rows[i, j])
+            vis.append((j, s))
+        if not vis:
+            continue
+        mx = max(s for _, s in vis)
+        z = sum(math.exp(s - mx) for _, s in vis)
+        for j, s in vis:
+            P[i, j] = math.exp(s - mx) / z
+    return P
+
+
+WEIGHT_CASES = [
+    # (Sq, Sk, D, mask, window, bias_kind, scale)
+    (7, 7, 3, 0, 0, 0, 0.6),
+    (9, 9, 4, 1, 0, 2, 0.5),
+    (10, 10, 3, 2, 3, 1, 0.7),
+    (5, 11, 2, 2, 4, 2, 1.3),         # Sq < Sk, bottom-right
+    (9, 4, 2, 1, 0, 0, 0.5),          # Sq > Sk: rows without a key are all zero
+    (12, 12, 2, 0, 0, 1, -0.4),       # negative scale, T5
+]
+
+
+def check_weights():
+    """oracle.attention_weights (the P the gradient error bars use) against brute force, torch's
+    CPU softmax over scores built here, and the identity-V link P = attend_rows(V = I)."""
+    rng = np.random.default_rng(21)
+    for (Sq, Sk, D, mask, window, bk, scale) in WEIGHT_CASES:
+        q = rng.standard_normal((Sq, D))
+        k = rng.standard_normal((Sk, D))
+        pos = np.arange(Sq) + (Sk - Sq)
+        bias = None
+        if bk == 1:
+            tbl = rng.standard_normal(32)
+            bias = tbl[np.vectorize(t5_bucket_int)(np.arange(Sk)[None, :] - pos[:, None])]
+        elif bk == 2:
+            bias = 0.5 * rng.standard_normal((Sq, Sk))
+        got = sdpa_ref.attention_weights(q, k, pos, scale, mask, window, bias)
+        want = brute_force_weights(q, k, pos, scale, mask, window, bias)
+        assert np.max(np.abs(got - want)) <= TOL, (Sq, Sk, mask, window, bk)
+        # library special case: torch.softmax of the scores with an additive -inf band
+        sc = torch.from_numpy(q) @ torch.from_numpy(k).T * scale + torch_band(Sq, Sk, mask, window)
+        if bias is not None:
+            sc = sc + torch.from_numpy(bias)
+        tp = torch.softmax(sc, dim=-1).numpy()
+        tp = np.where(np.isnan(tp), 0.0, tp)          # rows without a visible key
+        assert np.max(np.abs(got - tp)) <= TOL
+        # the weights are what attend_rows averages V with: V = I returns them exactly
+        o, _ = oracle.attend_rows(q, k, np.eye(Sk), pos, scale, mask, window, bias)
+        assert np.max(np.abs(got - o)) <= TOL
+
+
 def check_sampled_rows_match_full():
     rng = np.random.default_rng(5)
     q, k, v, bias = rand_case(rng, 2, 70, 90, 4, 2, 8, 2)
@@ -324,6 +390,10 @@ def test_oracle_invariants():
     check_invariants()
 
 
+def test_oracle_attention_weights():
+    check_weights()
+
+
 def test_oracle_sampled_rows_match_full():
     check_sampled_rows_match_full()
 
@@ -340,7 +410,7 @@ def test_oracle_threads_same_result():
 # planted mistakes: each must be caught by at least one pin
 # ------------------------------------------------------------------------------------------
 ALL_CHECKS = [check_brute_force, check_torch_library, check_golden, check_t5_exhaustive,
-              check_invariants]
+              check_invariants, check_weights]
 
 
 def _caught(monkeypatch, name, fn):
@@ -428,3 +498,37 @@ def test_pins_catch_lse_log2(monkeypatch):
         o, l = orig(*a, **kw)
         return o, l / math.log(2)
     assert _caught(monkeypatch, "attend_rows", bad)
+
+
+# planted mistakes in the softmax weights (the P of the gradient error bars)
+def test_pins_catch_weights_dropped_scale(monkeypatch):
+    orig = sdpa_ref.attention_weights
+
+    def bad(q, k, pos, scale, *a, **kw):
+        return orig(q, k, pos, 1.0, *a, **kw)
+    assert _caught(monkeypatch, "attention_weights", bad)
+
+
+def test_pins_catch_weights_dropped_bias(monkeypatch):
+    orig = sdpa_ref.attention_weights
+
+    def bad(q, k, pos, scale, mask, window, bias_rows=None):
+        return orig(q, k, pos, scale, mask, window, None)
+    assert _caught(monkeypatch, "attention_weights", bad)
+
+
+def test_pins_catch_weights_wrong_window(monkeypatch):
+    orig = sdpa_ref.attention_weights
+
+    def bad(q, k, pos, scale, mask, window, bias_rows=None):
+        return orig(q, k, pos, scale, mask, window + 1, bias_rows)
+    assert _caught(monkeypatch, "attention_weights", bad)
+
+
+def test_pins_catch_weights_unnormalised(monkeypatch):
+    orig = sdpa_ref.attention_weights
+
+    def bad(*a, **kw):
+        p = orig(*a, **kw)
+        return p * 1.001
+    assert _caught(monkeypatch, "attention_weights", bad)
