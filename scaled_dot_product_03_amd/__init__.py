@@ -64,6 +64,11 @@ def load():
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: build it with "
                            "`python -m scaled_dot_product_03_amd.build`")
+    # torch first: the library must bind to the HIP runtime torch already uses (torch ships its
+    # own copy under the same soname). Loaded before torch, the library would pull in the
+    # system runtime and the process would end up with two HIP runtimes, whose streams, device
+    # state and errors are not each other's.
+    import torch  # noqa: F401
     L = ctypes.CDLL(path)
     fwd_args = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 6 + [ctypes.c_float] + \
                [ctypes.c_int] * 3 + [ctypes.c_void_p, ctypes.c_void_p]

@@ -221,3 +221,18 @@ VL_CASES = [
 @pytest.mark.parametrize("name,kw,code", VL_CASES, ids=[c[0] for c in VL_CASES])
 def test_varlen_invalid_arguments_return_status(lib, entry, name, kw, code):
     assert call_vl(entry, **kw) == code
+
+
+def test_library_binds_to_torch_hip_runtime():
+    """Loading the library before torch is imported must not bring a second HIP runtime into
+    the process: the binding imports torch first, so the library binds to torch's runtime."""
+    import subprocess
+    import sys
+    code = ("import scaled_dot_product_03_amd as sdpa; sdpa.load(); import torch; "
+            "maps = open('/proc/self/maps').read(); "
+            "print(sorted({l.split()[-1] for l in maps.splitlines() if 'libamdhip64' in l}))")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300,
+                       cwd=ROOT)
+    assert r.returncode == 0, r.stderr[-2000:]
+    libs = eval(r.stdout.strip().splitlines()[-1])
+    assert len(libs) == 1, libs
