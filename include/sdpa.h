@@ -43,13 +43,16 @@
  *
  * Conventions for every entry point:
  *   - All pointers are DEVICE pointers owned by the caller. The library allocates nothing,
- *     keeps nothing after returning, and writes every element of out and lse.
+ *     keeps nothing after returning, and writes every element of out and lse (the one
+ *     exception, sdpa_decode_noalloc, uses a static per-GPU scratch array instead).
  *   - q, k, v, out and a full bias must be 16-byte aligned; lse 4-byte aligned.
  *   - stream is a hipStream_t (NULL = the default stream). The call only enqueues work; inputs
  *     must stay alive until the stream has finished it.
  *   - Returns SDPA_OK or the first failed check; on error nothing is launched. No exception
  *     crosses this boundary. Launch failures return SDPA_ERR_LAUNCH.
- *   - Thread-safe: no mutable global state. Results are bitwise reproducible run to run for a
+ *   - Thread-safe: no mutable global state (besides the per-device scratch address that
+ *     sdpa_decode_noalloc resolves once under a lock). Results are bitwise reproducible run to
+ *     run for a
  *     given shape (fixed tile shape chosen from the shape alone, fixed key order, no atomics),
  *     the determinism the transformers issue "Transformer models are not deterministic when
  *     using Flash Attention 2" asks of a fused kernel.
@@ -67,7 +70,10 @@
 extern "C" {
 #endif
 
-#define SDPA_ABI_VERSION 2
+#define SDPA_ABI_VERSION 3
+
+/* Size of the device scratch buffer behind sdpa_decode_noalloc (per GPU): 16 MiB. */
+#define SDPA_DECODE_SCRATCH_BYTES (16u << 20)
 
 enum sdpa_mask_kind { SDPA_MASK_NONE = 0, SDPA_MASK_CAUSAL = 1, SDPA_MASK_SLIDING = 2 };
 enum sdpa_bias_kind {
@@ -86,7 +92,8 @@ enum sdpa_status {
     SDPA_ERR_SCALE = 8,     /* scale not finite */
     SDPA_ERR_ALIGN = 9,     /* a pointer is not aligned as required */
     SDPA_ERR_LAUNCH = 10,   /* the HIP launch reported an error */
-    SDPA_ERR_WORKSPACE = 11 /* workspace NULL, misaligned or smaller than required */
+    SDPA_ERR_WORKSPACE = 11, /* workspace NULL, misaligned or smaller than required */
+    SDPA_ERR_DEVICE = 12     /* current device unknown or its scratch buffer not resolved */
 };
 
 /*
@@ -198,6 +205,27 @@ int sdpa_decode_f32out(const void* q, const void* k, const void* v, float* out, 
                        void* ws, size_t ws_bytes, int B, int Hq, int Hkv, int Sq, int Sk, int D,
                        float scale, int mask_kind, int window, int bias_kind,
                        const void* bias_tbl, void* stream);
+
+/*
+ * sdpa_decode (bf16 out) for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc. Same arguments, kernels,
+ * arithmetic and results (bit for bit) as sdpa_decode, without the workspace: the per-split
+ * partial results go to a device scratch array of SDPA_DECODE_SCRATCH_BYTES that the library
+ * holds on each GPU it runs on, until the process ends. Its device address is looked up once
+ * per device (hipGetSymbolAddress) on the first call there; the current device must be the
+ * device of `stream` and of the tensors. The call allocates nothing.
+ *   A call whose partial results need more than SDPA_DECODE_SCRATCH_BYTES
+ *   (sdpa_decode_ws_bytes(...) > that size and more than one key split) returns
+ *   SDPA_ERR_WORKSPACE; SDPA_ERR_DEVICE if the device or its scratch address cannot be found.
+ *   The scratch keeps the last call's contents; every value the merge reads is written by the
+ *   same call first, so nothing needs clearing. Calls that overlap on one GPU (on different
+ *   streams, or from different host threads without ordering) share the scratch and race:
+ *   order them on one stream.
+ */
+int sdpa_decode_noalloc(const void* q, const void* k, const void* v, void* out, float* lse,
+                        int B, int Hq, int Hkv, int Sq, int Sk, int D, float scale,
+                        int mask_kind, int window, int bias_kind, const void* bias_tbl,
+                        void* stream);
 
 /* Static English text for a status code (never NULL). */
 const char* sdpa_status_str(int status);

@@ -33,14 +33,15 @@ SDPA_OK = 0
 STATUS_NAMES = {0: "SDPA_OK", 1: "SDPA_ERR_NULL", 2: "SDPA_ERR_SHAPE", 3: "SDPA_ERR_HEADS",
                 4: "SDPA_ERR_HEADDIM", 5: "SDPA_ERR_MASK", 6: "SDPA_ERR_WINDOW",
                 7: "SDPA_ERR_BIAS", 8: "SDPA_ERR_SCALE", 9: "SDPA_ERR_ALIGN",
-                10: "SDPA_ERR_LAUNCH", 11: "SDPA_ERR_WORKSPACE"}
+                10: "SDPA_ERR_LAUNCH", 11: "SDPA_ERR_WORKSPACE", 12: "SDPA_ERR_DEVICE"}
 
 # symbols exported by the library (must match include/sdpa.h)
 ENTRY_POINTS = ("sdpa_fwd", "sdpa_fwd_bf16_f32out", "sdpa_fwd_f32", "sdpa_bwd",
                 "sdpa_bwd_f32out", "sdpa_decode_ws_bytes", "sdpa_decode", "sdpa_decode_f32out",
-                "sdpa_fwd_varlen", "sdpa_fwd_varlen_f32out", "sdpa_status_str",
-                "sdpa_abi_version")
-ABI_VERSION = 2
+                "sdpa_fwd_varlen", "sdpa_fwd_varlen_f32out", "sdpa_decode_noalloc",
+                "sdpa_status_str", "sdpa_abi_version")
+ABI_VERSION = 3
+DECODE_SCRATCH_BYTES = 16 << 20     # SDPA_DECODE_SCRATCH_BYTES
 
 _lib = None
 
@@ -90,6 +91,8 @@ def load():
         fn = getattr(L, name)
         fn.argtypes = dec_args
         fn.restype = ctypes.c_int
+    L.sdpa_decode_noalloc.argtypes = fwd_args
+    L.sdpa_decode_noalloc.restype = ctypes.c_int
     vl_args = [ctypes.c_void_p] * 7 + [ctypes.c_int] * 8 + [ctypes.c_float] + \
               [ctypes.c_int] * 3 + [ctypes.c_void_p, ctypes.c_void_p]
     for name in ("sdpa_fwd_varlen", "sdpa_fwd_varlen_f32out"):
@@ -352,6 +355,36 @@ def decode(q, k, v, *, scale: Optional[float] = None, mask="causal", window: int
                            lse.data_ptr(), ws.data_ptr(), ws.numel() * ws.element_size(), B, Hq,
                            Hkv, Sq, Sk, D, ctypes.c_float(scale), mk, int(window), bk, bias_ptr,
                            stream)
+    if st != SDPA_OK:
+        raise SdpaError(st, L.sdpa_status_str(st).decode())
+    return out, lse
+
+
+def decode_noalloc(q, k, v, out, lse, *, scale: Optional[float] = None, mask="causal",
+                   window: int = 0, bias_kind="none", bias=None, stream=None):
+    """decode() for callers that cannot allocate: same results, bit for bit, as decode() with
+    bf16 output, but the per-split partials go to the library's static per-GPU scratch array
+    instead of a workspace. The caller passes the outputs: out [B, Sq, Hq, D] bf16 and
+    lse [B, Hq, Sq] fp32; nothing is allocated here or in the library. Calls that overlap on one
+    GPU share the scratch: issue them on one stream."""
+    import torch
+
+    L = load()
+    B, Sq, Hq, D, Sk, Hkv = _check_qkv(q, k, v)
+    if q.dtype != torch.bfloat16:
+        raise ValueError("decode takes bf16 q, k, v")
+    _check_buf(out, "out", (B, Sq, Hq, D), torch.bfloat16, q.device)
+    _check_buf(lse, "lse", (B, Hq, Sq), torch.float32, q.device)
+    mk = _kind(mask, _MASKS, "mask")
+    bk = _kind(bias_kind, _BIASES, "bias kind")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    bias_ptr = _bias_ptr(bk, bias, q.dtype, B, Hq, Sq, Sk)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = L.sdpa_decode_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                               lse.data_ptr(), B, Hq, Hkv, Sq, Sk, D, ctypes.c_float(scale), mk,
+                               int(window), bk, bias_ptr, stream)
     if st != SDPA_OK:
         raise SdpaError(st, L.sdpa_status_str(st).decode())
     return out, lse

@@ -14,6 +14,7 @@ hipError_t launch_fwd_bf16(FwdParams p, int D, int mask, int bias, bool out_f32,
 hipError_t launch_fwd_f32(FwdParams p, int D, int mask, int bias, hipStream_t s);
 hipError_t launch_bwd_bf16(BwdParams p, int D, int mask, int bias, bool out_f32, hipStream_t s);
 hipError_t launch_decode_bf16(DecParams p, int D, int mask, int bias, bool out_f32, hipStream_t s);
+hipError_t decode_scratch(void** ptr);
 }  // namespace sdpa
 
 namespace {
@@ -116,10 +117,11 @@ bool dec_shape_ok(int B, int Hq, int Hkv, int Sq, int Sk, int D) {
            (D == 32 || D == 64 || D == 128 || D == 256) && (long long)Sq * (Hq / Hkv) < (1LL << 30);
 }
 
-int decode_common(const void* q, const void* k, const void* v, void* out, float* lse, void* ws,
-                  size_t ws_bytes, int B, int Hq, int Hkv, int Sq, int Sk, int D, float scale,
-                  int mask_kind, int window, int bias_kind, const void* bias_tbl, void* stream,
-                  bool out_f32) {
+// Checks of a decode call that need no workspace; *splits receives the key-split count.
+int validate_decode(const void* q, const void* k, const void* v, const void* out,
+                    const float* lse, int B, int Hq, int Hkv, int Sq, int Sk, int D,
+                    float scale, int mask_kind, int window, int bias_kind, const void* bias_tbl,
+                    long long* splits) {
     int st = validate(q, k, v, out, lse, B, Hq, Hkv, Sq, Sk, D, scale, mask_kind, window,
                       bias_kind, bias_tbl, 2);
     if (st != SDPA_OK) return st;
@@ -127,11 +129,15 @@ int decode_common(const void* q, const void* k, const void* v, void* out, float*
     if ((long long)Sq * G >= (1LL << 30)) return SDPA_ERR_SHAPE;
     // grids: split kernel B * Hkv * row blocks * splits, merge kernel up to 4 per row block
     const long long blocks = (long long)B * Hkv * sdpa::dec_row_blocks(G, Sq);
-    const long long splits = sdpa::dec_splits(B, Hkv, G, Sq, Sk);
-    if (blocks * (splits > 4 ? splits : 4) >= (1LL << 31)) return SDPA_ERR_SHAPE;
-    if (!ws || !aligned(ws, 16) ||
-        ws_bytes < sdpa::dec_ws_floats(B, Hkv, G, Sq, Sk, D) * sizeof(float))
-        return SDPA_ERR_WORKSPACE;
+    *splits = sdpa::dec_splits(B, Hkv, G, Sq, Sk);
+    if (blocks * (*splits > 4 ? *splits : 4) >= (1LL << 31)) return SDPA_ERR_SHAPE;
+    return SDPA_OK;
+}
+
+// Launch of a validated decode call with its partial-result buffer `ws`.
+int run_decode(const void* q, const void* k, const void* v, void* out, float* lse, void* ws,
+               int B, int Hq, int Hkv, int Sq, int Sk, int D, float scale, int mask_kind,
+               int window, int bias_kind, const void* bias_tbl, void* stream, bool out_f32) {
     const sdpa::FwdParams f = make_params(q, k, v, out, lse, B, Hq, Hkv, Sq, Sk, scale,
                                           mask_kind, window, bias_tbl);
     sdpa::DecParams p{};
@@ -142,6 +148,21 @@ int decode_common(const void* q, const void* k, const void* v, void* out, float*
     hipError_t e = sdpa::launch_decode_bf16(p, D, kernel_mask(mask_kind, window, Sk), bias_kind, out_f32,
                                             (hipStream_t)stream);
     return e == hipSuccess ? SDPA_OK : SDPA_ERR_LAUNCH;
+}
+
+int decode_common(const void* q, const void* k, const void* v, void* out, float* lse, void* ws,
+                  size_t ws_bytes, int B, int Hq, int Hkv, int Sq, int Sk, int D, float scale,
+                  int mask_kind, int window, int bias_kind, const void* bias_tbl, void* stream,
+                  bool out_f32) {
+    long long splits = 0;
+    int st = validate_decode(q, k, v, out, lse, B, Hq, Hkv, Sq, Sk, D, scale, mask_kind, window,
+                             bias_kind, bias_tbl, &splits);
+    if (st != SDPA_OK) return st;
+    if (!ws || !aligned(ws, 16) ||
+        ws_bytes < sdpa::dec_ws_floats(B, Hkv, Hq / Hkv, Sq, Sk, D) * sizeof(float))
+        return SDPA_ERR_WORKSPACE;
+    return run_decode(q, k, v, out, lse, ws, B, Hq, Hkv, Sq, Sk, D, scale, mask_kind, window,
+                      bias_kind, bias_tbl, stream, out_f32);
 }
 
 int varlen_common(const void* q, const void* k, const void* v, void* out, float* lse,
@@ -170,6 +191,8 @@ int varlen_common(const void* q, const void* k, const void* v, void* out, float*
 }
 
 }  // namespace
+
+static_assert(sdpa::kDecodeScratchBytes == SDPA_DECODE_SCRATCH_BYTES, "scratch size");
 
 extern "C" {
 
@@ -281,6 +304,24 @@ int sdpa_bwd_f32out(const void* q, const void* k, const void* v, const void* out
     return e == hipSuccess ? SDPA_OK : SDPA_ERR_LAUNCH;
 }
 
+int sdpa_decode_noalloc(const void* q, const void* k, const void* v, void* out, float* lse,
+                        int B, int Hq, int Hkv, int Sq, int Sk, int D, float scale,
+                        int mask_kind, int window, int bias_kind, const void* bias_tbl,
+                        void* stream) {
+    long long splits = 0;
+    int st = validate_decode(q, k, v, out, lse, B, Hq, Hkv, Sq, Sk, D, scale, mask_kind, window,
+                             bias_kind, bias_tbl, &splits);
+    if (st != SDPA_OK) return st;
+    // a single split writes the output directly and leaves the partial-result buffer unused
+    if (splits > 1 && sdpa::dec_ws_floats(B, Hkv, Hq / Hkv, Sq, Sk, D) * sizeof(float) >
+                          (size_t)SDPA_DECODE_SCRATCH_BYTES)
+        return SDPA_ERR_WORKSPACE;
+    void* ws = nullptr;
+    if (sdpa::decode_scratch(&ws) != hipSuccess) return SDPA_ERR_DEVICE;
+    return run_decode(q, k, v, out, lse, ws, B, Hq, Hkv, Sq, Sk, D, scale, mask_kind, window,
+                      bias_kind, bias_tbl, stream, false);
+}
+
 const char* sdpa_status_str(int status) {
     switch (status) {
         case SDPA_OK: return "ok";
@@ -295,6 +336,7 @@ const char* sdpa_status_str(int status) {
         case SDPA_ERR_ALIGN: return "pointer misaligned (q/k/v/out/full bias need 16 bytes)";
         case SDPA_ERR_LAUNCH: return "HIP kernel launch failed";
         case SDPA_ERR_WORKSPACE: return "workspace NULL, misaligned (16 bytes) or too small";
+        case SDPA_ERR_DEVICE: return "current device unknown or its scratch buffer not found";
         default: return "unknown status";
     }
 }

@@ -6,6 +6,10 @@
 
 namespace sdpa {
 
+// Size of the static per-device scratch behind the no-allocation decode entry point (the
+// partial results of every split); the public header states the same value.
+constexpr size_t kDecodeScratchBytes = (size_t)16 << 20;
+
 struct DecParams {
     const void* q;       // [B][Sq][Hq][D] bf16
     const void* k;       // [B][Sk][Hkv][D] bf16

@@ -23,6 +23,9 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
+#include <stdio.h>
+
+#include <mutex>
 
 #include "sdpa_decode.h"
 #include "sdpa_device.h"
@@ -480,6 +483,41 @@ static hipError_t launch_d(const DecParams& p, int mask, int bias, hipStream_t s
 }
 
 }  // namespace dec
+
+// Partial results of the no-allocation decode entry point (callers that cannot allocate: HIP
+// graph capture, serving loops). Each GPU the library runs on holds its own copy until the
+// process ends. It lives in this file, with the kernels that use it, so that it belongs to a
+// code object the runtime loads for those kernels. In host code the name is only a stand-in
+// for the symbol: kernels get the device address that decode_scratch returns.
+static __device__ __align__(256) float scratch[kDecodeScratchBytes / sizeof(float)];
+
+// The device address of `scratch` on the current device, resolved with hipGetSymbolAddress on
+// the first call there and kept per device.
+hipError_t decode_scratch(void** ptr) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void* addr[kMaxDevices];
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        fprintf(stderr, "sdpa: current device not found (device %d): %s\n", dev,
+                hipGetErrorString(e));
+        return e != hipSuccess ? e : hipErrorInvalidDevice;
+    }
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* a = nullptr;
+        e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !a) {
+            fprintf(stderr, "sdpa: scratch of device %d not resolved: %s\n", dev,
+                    hipGetErrorString(e));
+            return e != hipSuccess ? e : hipErrorInvalidSymbol;
+        }
+        addr[dev] = a;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
+}
 
 hipError_t launch_decode_bf16(DecParams p, int D, int mask, int bias, bool out_f32, hipStream_t s) {
     p.rows = p.G * p.Sq;

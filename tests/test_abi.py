@@ -38,8 +38,8 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.sdpa_abi_version() == sdpa.ABI_VERSION == 2
-    for code in range(0, 12):
+    assert lib.sdpa_abi_version() == sdpa.ABI_VERSION == 3
+    for code in range(0, 13):
         s = sdpa.status_str(code)
         assert s and s != "unknown status"
     assert sdpa.status_str(999) == "unknown status"
