@@ -172,7 +172,7 @@ def timed_launches(launch, stream, steps: int):
 
 
 def time_workload(sdpa, wl: si.Workload, steps: int, warmup: int, bwd: bool = False,
-                  decode: bool = False):
+                  decode: bool = False, min_settle: float = 0.5):
     """Returns dict with ms_per_step (wall, synchronised), kernel_ms_avg / median (events over
     the same launches) and the number of settle launches. With bwd, a step is one gradient
     call (dQ, dK, dV) instead of one forward; with decode, one split-key decode call."""
@@ -205,7 +205,7 @@ def time_workload(sdpa, wl: si.Workload, steps: int, warmup: int, bwd: bool = Fa
         def launch():
             sdpa.fwd(q, k, v, out=out, lse=lse, **kw)
 
-    n_settle = settle(launch, stream, warmup)
+    n_settle = settle(launch, stream, warmup, min_s=min_settle)
     t = timed_launches(launch, stream, steps)
     t["settle_launches"] = n_settle
     del q, k, v, bias, out, lse, launch
@@ -448,6 +448,9 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=None, choices=sorted(si.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--min-settle", type=float, default=0.5, metavar="S",
+                    help="least seconds of settle launches before the timed region (counter "
+                         "runs use 0: the profiler serialises dispatches)")
     ap.add_argument("--sweep", action="store_true",
                     help="also time the extra bias kinds and head dims (stderr)")
     ap.add_argument("--no-sweep", action="store_true",
@@ -494,7 +497,7 @@ def main(argv=None):
         return main_bwd(sdpa, wl, args)
     if args.decode:
         return main_decode(sdpa, wl, args)
-    t = time_workload(sdpa, wl, args.steps, args.warmup)
+    t = time_workload(sdpa, wl, args.steps, args.warmup, min_settle=args.min_settle)
     flops, achieved = report(wl, t)
     value = flops / (t["ms_per_step"] * 1e-3) / 1e12
     traffic = load_traffic(wl.name)
@@ -526,14 +529,15 @@ def main(argv=None):
                      "traffic": traffic},
     }
     if not args.no_sweep:
-        line["sweep"] = sweep_forward(sdpa, SWEEP_DEFAULT, args.steps, args.warmup)
+        line["sweep"] = sweep_forward(sdpa, SWEEP_DEFAULT, args.steps, args.warmup,
+                                      args.min_settle)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(line), flush=True)
 
     if args.sweep:
         for key in SWEEP_EXTRA:
-            rec = sweep_forward(sdpa, [key], args.steps, args.warmup)[key]
+            rec = sweep_forward(sdpa, [key], args.steps, args.warmup, args.min_settle)[key]
             print(json.dumps({"workload": key, **si.WORKLOADS[key].describe(), **rec}),
                   file=sys.stderr, flush=True)
     return 0
@@ -548,14 +552,14 @@ SWEEP_DEFAULT = ["c2c", "c3", "c3c", "c4t5", "c4full", "c5mha", "c5gqa", "c5mqa"
 SWEEP_EXTRA = ["c2alibi", "c4t5u", "c2d32", "c2d256"]
 
 
-def sweep_forward(sdpa, keys, steps: int, warmup: int) -> dict:
+def sweep_forward(sdpa, keys, steps: int, warmup: int, min_settle: float = 0.5) -> dict:
     """Times each workload like the headline (settle, then `steps` launches with per-launch
     events) and returns {key: record}; adds the sliding/causal time ratios when both sides
     were timed."""
     out = {}
     for key in keys:
         w2 = si.WORKLOADS[key]
-        t2 = time_workload(sdpa, w2, steps, warmup)
+        t2 = time_workload(sdpa, w2, steps, warmup, min_settle=min_settle)
         f2, a2 = report(w2, t2)
         rec = {"kernel_ms_avg": round(t2["kernel_ms_avg"], 4),
                "kernel_ms_median": round(t2["kernel_ms_median"], 4),
@@ -578,7 +582,7 @@ def sweep_forward(sdpa, keys, steps: int, warmup: int) -> dict:
     return out
 
 
-def time_varlen(sdpa, wl, steps: int, warmup: int):
+def time_varlen(sdpa, wl, steps: int, warmup: int, min_settle: float = 0.5):
     import torch
     inp = si.make_varlen_inputs(wl)
 
@@ -594,7 +598,7 @@ def time_varlen(sdpa, wl, steps: int, warmup: int):
     def launch():
         sdpa.fwd_varlen(q, k, v, cq, ck, m, m, scale=wl.scale, mask=wl.mask_kind,
                         window=wl.window, out=out, lse=lse, stream=stream.cuda_stream)
-    n_settle = settle(launch, stream, warmup)
+    n_settle = settle(launch, stream, warmup, min_s=min_settle)
     t = timed_launches(launch, stream, steps)
     t["settle_launches"] = n_settle
     return t
@@ -640,7 +644,7 @@ def cpu_baseline_varlen(wl, budget_s: float = 12.0):
 
 
 def main_varlen(sdpa, wl, args) -> int:
-    t = time_varlen(sdpa, wl, args.steps, args.warmup)
+    t = time_varlen(sdpa, wl, args.steps, args.warmup, args.min_settle)
     flops = 4.0 * wl.D * wl.Hq * si.varlen_visible_pairs(wl)
     value = flops / (t["ms_per_step"] * 1e-3) / 1e12
     achieved = flops / (t["kernel_ms_avg"] * 1e-3) / 1e12
@@ -665,7 +669,8 @@ def main_varlen(sdpa, wl, args) -> int:
 
 
 def main_decode(sdpa, wl: si.Workload, args) -> int:
-    t = time_workload(sdpa, wl, args.steps, args.warmup, decode=True)
+    t = time_workload(sdpa, wl, args.steps, args.warmup, decode=True,
+                      min_settle=args.min_settle)
     nbytes = si.algorithmic_bytes_decode(wl)
     value = nbytes / (t["ms_per_step"] * 1e-3) / 1e9
     achieved = nbytes / (t["kernel_ms_avg"] * 1e-3) / 1e9
@@ -699,8 +704,8 @@ def main_decode(sdpa, wl: si.Workload, args) -> int:
     if args.sweep:
         for key in ["dec", "decmqa", "decsw", "decd256"]:
             w2 = si.WORKLOADS[key]
-            t2 = time_workload(sdpa, w2, args.steps, args.warmup,
-                               decode=True)
+            t2 = time_workload(sdpa, w2, args.steps, args.warmup, decode=True,
+                               min_settle=args.min_settle)
             nb = si.algorithmic_bytes_decode(w2)
             rec = {"workload": key, "pass": "decode", **w2.describe(),
                    "call_ms_avg": round(t2["kernel_ms_avg"], 4),
@@ -713,7 +718,7 @@ def main_decode(sdpa, wl: si.Workload, args) -> int:
 
 
 def main_bwd(sdpa, wl: si.Workload, args) -> int:
-    t = time_workload(sdpa, wl, args.steps, args.warmup, bwd=True)
+    t = time_workload(sdpa, wl, args.steps, args.warmup, bwd=True, min_settle=args.min_settle)
     flops, achieved = report(wl, t, bwd=True)
     value = flops / (t["ms_per_step"] * 1e-3) / 1e12
     line = {
@@ -749,7 +754,8 @@ def main_bwd(sdpa, wl: si.Workload, args) -> int:
         for key in ["c2", "c3", "c3c", "c4t5", "c4full", "c5mha", "c5gqa", "c5mqa", "c2alibi",
                     "c4t5u", "c2d32", "c2d256"]:
             w2 = si.WORKLOADS[key]
-            t2 = time_workload(sdpa, w2, args.steps, args.warmup, bwd=True)
+            t2 = time_workload(sdpa, w2, args.steps, args.warmup, bwd=True,
+                               min_settle=args.min_settle)
             f2, a2 = report(w2, t2, bwd=True)
             rec = {"workload": key, "pass": "backward", **w2.describe(),
                    "call_ms_avg": round(t2["kernel_ms_avg"], 4),
