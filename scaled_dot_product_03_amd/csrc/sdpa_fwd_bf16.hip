@@ -23,7 +23,8 @@
 //     through ds_read_b64_tr_b16 (transposing LDS read), P straight from the score registers
 //     (bf16, nearest even) as the B operand, so P never leaves the lane;
 //   * software pipeline inside each wave: iteration t runs the exponentials of tile t under
-//     the S^T MFMAs of tile t+1 (phase A), then the P.V MFMAs of tile t under the bias, mask
+//     the S^T MFMAs of tile t+1 (phase A; a first batch of exponentials before the first MFMA,
+//     while the first K fragments are read), then the P.V MFMAs of tile t under the bias, mask
 //     and row max of tile t+1 (phase B), so the matrix cores are fed while the VALU works;
 //   * online softmax in the log2 domain with a lazy rescale: the running reference max only
 //     moves (and O is only rescaled) when a row's max grows by more than 2^8; scale*log2(e)
@@ -475,9 +476,23 @@ void sdpa_fwd_bf16_kernel(const FwdParams p) {
 #pragma unroll
             for (int i = 0; i < KPRE; ++i) read_k(kb, i, ka[i]);
         }
-        constexpr int EPK = 32 / KS;      // exponentials per k-step
+        // The first E0 exponentials come before the first MFMAs: right after the barrier every
+        // wave reads its first K fragments at once, and this work needs no LDS data, so it
+        // covers that wait. The other exponentials are spread over the remaining k-steps.
+        constexpr int E0 = 8;
+        auto expo = [&](int e) {
+            float pe = __builtin_amdgcn_exp2f(fmaf(cs[e >> 4][e & 15], cc_c, nn));
+            pin(pe);
+            cs[e >> 4][e & 15] = pe;
+        };
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
+            if constexpr (DO_E) {
+                if (ks == 0) {
+#pragma unroll
+                    for (int e = 0; e < E0; ++e) expo(e);
+                }
+            }
             if constexpr (DO_S) {
                 const bf16x8 a0 = ka[ks % KPRE][0], a1 = ka[ks % KPRE][1];
                 if (ks + KPRE < KS) read_k(kb, ks + KPRE, ka[ks % KPRE]);
@@ -485,12 +500,11 @@ void sdpa_fwd_bf16_kernel(const FwdParams p) {
                 ns[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[ks], ns[1], 0, 0, 0);
             }
             if constexpr (DO_E) {
+                if (ks > 0) {
 #pragma unroll
-                for (int i = 0; i < EPK; ++i) {
-                    const int e = ks * EPK + i;
-                    float pe = __builtin_amdgcn_exp2f(fmaf(cs[e >> 4][e & 15], cc_c, nn));
-                    pin(pe);
-                    cs[e >> 4][e & 15] = pe;
+                    for (int e = E0 + ((ks - 1) * (32 - E0)) / (KS - 1);
+                         e < E0 + (ks * (32 - E0)) / (KS - 1); ++e)
+                        expo(e);
                 }
                 if (ks >= KS - VPRE) read_v(vb, ks - (KS - VPRE), vfr[ks - (KS - VPRE)]);
             }
