@@ -36,6 +36,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
 #include <type_traits>
 
 #include "sdpa_params.h"
@@ -57,6 +58,12 @@ template <int D, int BIAS> constexpr int waves_per_eu_of() {
     return D == 256 ? 1 : ((D == 32 && BIAS != BIAS_FULL) ? 3 : 2);
 }
 template <int D> constexpr int rows_of() { return 32 * waves_of<D>(); }   // query rows per workgroup
+// Instances that take a persistent grid: dense, no full bias, D = 64 and 128 (not T5 at 128).
+// The work loop costs ~15 VGPRs; the excluded instances would spill with it.
+template <int D, int BIAS, bool VARLEN> constexpr bool persist_of() {
+    return !VARLEN && BIAS != BIAS_FULL &&
+           (D == 64 || (D == 128 && BIAS != BIAS_T5 && BIAS != BIAS_T5U));
+}
 constexpr int kBN = 64;             // keys per tile
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -159,7 +166,9 @@ void sdpa_fwd_bf16_kernel(const FwdParams p) {
     const int lane = tid & 63, wave = tid >> 6;
     const int hh = lane >> 5, r32 = lane & 31;
 
-    const WorkItem w = decode_work(p, blockIdx.x);
+  // one work item = one query tile of one (batch, query head)
+  auto run_item = [&](const int item) {
+    const WorkItem w = decode_work(p, item);
     const int b = w.b, hq = w.hq, kvh = hq / p.G;
     int Sq = p.Sq, Sk = p.Sk, off = p.off;
     size_t q_base = (size_t)b * Sq, k_base = (size_t)b * Sk;   // first token of the sequence
@@ -762,14 +771,66 @@ void sdpa_fwd_bf16_kernel(const FwdParams p) {
         if (hh == 0)
             lse_row[my_i] = (l_tot > 0.f) ? (m_ref + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
     }
+  };
+
+    // ---- work items --------------------------------------------------------------------------
+    // One item per workgroup, or (p.n_items > 0) a persistent grid of one workgroup per CU:
+    // workgroup g runs on XCD g % 8 (round-robin dispatch) and takes that XCD's items (those
+    // with index % 8 == g % 8, in decode_work's order) in rounds of nw = grid / 8, alternating
+    // direction each round, so the heaviest and lightest causal tiles of a round pair up. The
+    // hardware dispatcher places workgroup i on XCD i % 8 in index order and holds every later
+    // workgroup while that XCD has no free CU; a persistent grid has no such gaps. Each item
+    // is computed by the same code either way: the results do not depend on the grid.
+    if constexpr (persist_of<D, BIAS, VARLEN>()) {
+        const bool persist = p.n_items > 0;
+        const int xcd = blockIdx.x & 7, l = blockIdx.x >> 3, nw = gridDim.x >> 3;
+        auto item_of = [&](int r) {
+            return persist ? (r * nw + ((r & 1) ? nw - 1 - l : l)) * 8 + xcd
+                           : (r == 0 ? (int)blockIdx.x : 0x7fffffff);
+        };
+        const int lim = persist ? p.n_items : 0x7fffffff;
+#pragma unroll 1
+        for (int r = 0;; ++r) {
+            const int x = item_of(r);
+            if (x >= lim) break;
+            run_item(x);
+        }
+    } else {
+        run_item(blockIdx.x);
+    }
 }
 
 // ------------------------------------------------------------------------------------------
 // host-side launch (called by the C ABI after validation)
 // ------------------------------------------------------------------------------------------
+// compute units of the current device (cached per device)
+static int cu_count() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+        cache[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
 template <int D, int MASK, int BIAS, bool OUT_F32, bool VARLEN>
-static hipError_t launch_one(const FwdParams& p, hipStream_t stream) {
-    const unsigned grid = (unsigned)((size_t)p.B * p.Hq * p.n_qt);
+static hipError_t launch_one(FwdParams p, hipStream_t stream) {
+    const int total = p.B * p.Hq * p.n_qt;
+    int grid = total;
+    p.n_items = 0;
+    // persistent grid when every XCD receives whole (batch, KV head) groups and there are at
+    // least two items per workgroup; one workgroup fits a CU (registers), so the grid is the
+    // CU count, rounded down to whole XCDs
+    if (persist_of<D, BIAS, VARLEN>() && p.xcd_remap) {
+        const int pg = (cu_count() / 8) * 8;
+        if (pg >= 8 && total >= 2 * pg) {
+            grid = pg;
+            p.n_items = total;
+        }
+    }
     hipLaunchKernelGGL((sdpa_fwd_bf16_kernel<D, MASK, BIAS, OUT_F32, VARLEN>), dim3(grid),
                        dim3(64 * waves_of<D>()), 0, stream, p);
     return hipGetLastError();

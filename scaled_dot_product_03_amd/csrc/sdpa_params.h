@@ -35,6 +35,8 @@ struct FwdParams {
     const int* cu_q;
     const int* cu_k;
     int total_q, total_k;
+    // > 0: persistent grid (one workgroup per CU) walking this many work items
+    int n_items;
 };
 
 // Backward: gradients of L = sum(dO * O) for the forward above.

@@ -163,3 +163,30 @@ def test_bitwise_same_in_a_fresh_process(gpu_lib):
     there = [x.split()[1] for x in r.stdout.splitlines() if x.startswith("HASH ")][0]
     print(f"in-process {here[:16]} fresh process {there[:16]}")
     assert here == there
+
+
+@pytest.mark.parametrize("key,split_kv", [("c2", 2), ("c3", 2), ("c4t5", 12), ("c5mha", 8),
+                                          ("c5mqa", 1)])
+def test_persistent_grid_equals_small_launches_bitwise(gpu_lib, key, split_kv):
+    """At these sizes a launch walks its work items on a persistent grid (one workgroup per
+    CU, a fixed order of items per workgroup). The same inputs cut into launches of one batch
+    and `split_kv` KV heads (with their query heads) are small enough for one workgroup per
+    item. Every item is computed by the same code, so out and LSE must agree bit for bit."""
+    import torch
+    wl = W[key]
+    inp = si.make_inputs(wl)
+    q, k, v, bias = to_device(inp)
+    o_all, l_all = run_gpu(gpu_lib, wl, (q, k, v, bias))
+    G = wl.Hq // wl.Hkv
+    same = True
+    for b in range(wl.B):
+        for h0 in range(0, wl.Hkv, split_kv):
+            qs = q[b:b + 1, :, h0 * G:(h0 + split_kv) * G].contiguous()
+            ks = k[b:b + 1, :, h0:h0 + split_kv].contiguous()
+            vs = v[b:b + 1, :, h0:h0 + split_kv].contiguous()
+            bs = bias[h0 * G:(h0 + split_kv) * G].contiguous() if bias is not None else None
+            sub = wl.replace(B=1, Hq=split_kv * G, Hkv=split_kv)
+            o, l = run_gpu(gpu_lib, sub, (qs, ks, vs, bs))
+            same = same and torch.equal(o[0], o_all[b, :, h0 * G:(h0 + split_kv) * G])
+            same = same and torch.equal(l[0], l_all[b, h0 * G:(h0 + split_kv) * G])
+    assert same
