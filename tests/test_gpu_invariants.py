@@ -165,15 +165,31 @@ def test_bitwise_same_in_a_fresh_process(gpu_lib):
     assert here == there
 
 
-@pytest.mark.parametrize("key,split_kv", [("c2", 2), ("c3", 2), ("c4t5", 12), ("c5mha", 8),
-                                          ("c5mqa", 1)])
-def test_persistent_grid_equals_small_launches_bitwise(gpu_lib, key, split_kv):
+_PERSIST_CASES = {
+    "c2": (W["c2"], 2), "c3": (W["c3"], 2), "c4t5": (W["c4t5"], 12), "c5mha": (W["c5mha"], 8),
+    "c5mqa": (W["c5mqa"], 1), "c2alibi": (W["c2alibi"], 2), "c4t5u": (W["c4t5u"], 12),
+    # ragged query tiles (Sq = 1000: 4 tiles, the last one 232 rows), 512 items
+    "ragged": (si.small(W["c5gqa"], B=8, Hq=16, Hkv=8, Sq=1000, Sk=1000, name_suffix="pragged"), 2),
+    # keys longer than queries (off = 800) under a sliding window, 768 items
+    "prefix_sliding": (si.small(W["c3"], B=16, Hq=16, Hkv=8, Sq=700, Sk=1500, window=600,
+                                name_suffix="pprefix"), 2),
+    # D = 64 without a bias, causal
+    "d64": (si.small(W["c5gqa"], B=8, Hq=16, Hkv=8, Sq=1024, Sk=1024,
+                     name_suffix="pd64").replace(D=64), 2),
+}
+
+
+@pytest.mark.parametrize("case", sorted(_PERSIST_CASES))
+def test_persistent_grid_equals_small_launches_bitwise(gpu_lib, case):
     """At these sizes a launch walks its work items on a persistent grid (one workgroup per
     CU, a fixed order of items per workgroup). The same inputs cut into launches of one batch
     and `split_kv` KV heads (with their query heads) are small enough for one workgroup per
     item. Every item is computed by the same code, so out and LSE must agree bit for bit."""
     import torch
-    wl = W[key]
+    wl, split_kv = _PERSIST_CASES[case]
+    tiles = -(-wl.Sq // (256 if wl.D in (64, 128) else 128))
+    assert wl.B * wl.Hq * tiles >= 512 and (wl.B * wl.Hkv) % 8 == 0   # a persistent launch
+    assert wl.Hq // wl.Hkv * split_kv * tiles < 512 or split_kv % 8  # small launches are not
     inp = si.make_inputs(wl)
     q, k, v, bias = to_device(inp)
     o_all, l_all = run_gpu(gpu_lib, wl, (q, k, v, bias))
