@@ -176,6 +176,13 @@ _PERSIST_CASES = {
     # D = 64 without a bias, causal
     "d64": (si.small(W["c5gqa"], B=8, Hq=16, Hkv=8, Sq=1024, Sk=1024,
                      name_suffix="pd64").replace(D=64), 2),
+    # fewer keys than queries under a causal mask (off = -724): the first two query tiles of
+    # every (batch, head) see no key and end early inside the work loop
+    "empty_items": (si.small(W["c5gqa"], B=8, Hq=16, Hkv=8, Sq=1024, Sk=300,
+                             name_suffix="pempty"), 2),
+    # a negative softmax scale (the Q fragment's sign is flipped per item)
+    "neg_scale": (si.small(W["c5gqa"], B=8, Hq=16, Hkv=8, Sq=1024, Sk=1024,
+                           name_suffix="pneg").replace(scale_override=-0.0625), 2),
 }
 
 
