@@ -213,3 +213,42 @@ def test_persistent_grid_equals_small_launches_bitwise(gpu_lib, case):
             same = same and torch.equal(o[0], o_all[b, :, h0 * G:(h0 + split_kv) * G])
             same = same and torch.equal(l[0], l_all[b, h0 * G:(h0 + split_kv) * G])
     assert same
+
+
+def _random_persistent_case(seed: int):
+    """A seeded random launch that takes the persistent grid: B * Hkv a multiple of 8 and at
+    least 512 work items, random head dim, mask, window, bias kind, ragged lengths and a key
+    prefix of either sign."""
+    rng = np.random.default_rng(seed)
+    D = int(rng.choice([64, 128]))
+    G = int(rng.choice([1, 2, 4, 8]))
+    Hkv = int(rng.choice([1, 2, 4, 8]))
+    Sq = int(rng.integers(300, 2500))
+    Sk = max(1, Sq + int(rng.integers(-200, 800)))
+    mask = int(rng.choice([si.MASK_NONE, si.MASK_CAUSAL, si.MASK_SLIDING]))
+    window = int(rng.integers(1, Sk + 300)) if mask == si.MASK_SLIDING else 0
+    bias = int(rng.choice([si.BIAS_NONE, si.BIAS_ALIBI] + ([si.BIAS_T5, si.BIAS_T5U] if D == 64 else [])))
+    tiles = -(-Sq // 256)
+    B = 8 // Hkv
+    while B * G * Hkv * tiles < 512:
+        B += 8 // Hkv
+    return W["c5gqa"].replace(name=f"persist_random_{seed}", B=B, Hq=G * Hkv, Hkv=Hkv, Sq=Sq,
+                              Sk=Sk, D=D, mask_kind=mask, window=window, bias_kind=bias,
+                              seed=9000 + seed % 1000)
+
+
+@pytest.mark.parametrize("seed", range(20261204, 20261216))
+def test_persistent_grid_random_shapes_bitwise(gpu_lib, seed):
+    """Random persistent launches against one launch per batch (one workgroup per item, or a
+    persistent grid over far fewer items): out and LSE agree bit for bit."""
+    import torch
+    wl = _random_persistent_case(seed)
+    q, k, v, bias = to_device(si.make_inputs(wl))
+    o_all, l_all = run_gpu(gpu_lib, wl, (q, k, v, bias))
+    sub = wl.replace(B=1)
+    same = True
+    for b in range(wl.B):
+        o, l = run_gpu(gpu_lib, sub, (q[b:b + 1].contiguous(), k[b:b + 1].contiguous(),
+                                      v[b:b + 1].contiguous(), bias))
+        same = same and torch.equal(o[0], o_all[b]) and torch.equal(l[0], l_all[b])
+    assert same, wl
