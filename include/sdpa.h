@@ -50,10 +50,12 @@
  *     must stay alive until the stream has finished it.
  *   - Returns SDPA_OK or the first failed check; on error nothing is launched. No exception
  *     crosses this boundary. Launch failures return SDPA_ERR_LAUNCH.
- *   - Thread-safe: no mutable global state (besides the per-device scratch address that
- *     sdpa_decode_noalloc resolves once under a lock). Results are bitwise reproducible run to
- *     run for a
- *     given shape (fixed tile shape chosen from the shape alone, fixed key order, no atomics),
+ *   - Thread-safe: no mutable global state besides two per-device caches, each written once:
+ *     the compute-unit count that sizes the forward's persistent grid (an atomic) and the
+ *     scratch address that sdpa_decode_noalloc resolves under a lock. Results are bitwise
+ *     reproducible run to run for a given shape (fixed tile shape chosen from the shape alone,
+ *     fixed key order, no atomics; the same bits whatever the grid: one workgroup per work item
+ *     or the persistent grid),
  *     the determinism the transformers issue "Transformer models are not deterministic when
  *     using Flash Attention 2" asks of a fused kernel.
  *   - Validation: B, Hq, Hkv, Sq, Sk >= 1; Hq % Hkv == 0; D in {32, 64, 128, 256} (the
