@@ -1,4 +1,4 @@
-"""Work accounting of bench.py (CPU): the tile-granular FLOP count against closed forms.
+"""Work accounting and run contract of bench.py (CPU): the tile-granular FLOP count against closed forms, and the exits that keep every timed number on one GPU.
 
 The count is the matrix work the bf16 kernel performs (32-row x 64-key blocks, masked slots
 included); the profile summary checks it against the MFMA instruction counter.
@@ -111,3 +111,18 @@ def test_bwd_blocks_are_exactly_those_with_a_visible_pair(mask, w, sq, sk, bias)
     dq, dkdv = bench.bwd_tile_mfmas(wl)
     assert dq == len(dq_blocks) * 2 * (2 * (D // 16) + 2 * (D // 32)) * wl.Hq
     assert dkdv == len(kv_blocks) * _kv_per_block(D, bias) * G
+
+
+def test_more_than_one_gpu_is_refused_with_a_message(capsys):
+    """One GPU only: --gpus N above 1 exits (status 2) and says why, before touching a GPU."""
+    assert bench.main(["--gpus", "2"]) == 2
+    assert "exactly one GPU" in capsys.readouterr().err
+
+
+def test_no_gpu_exits_instead_of_falling_back(capsys):
+    """Without a visible GPU the benchmark stops (status 1); it never times a CPU path."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible")
+    assert bench.main(["--no-cpu-baseline", "--no-sweep"]) == 1
+    assert "no GPU" in capsys.readouterr().err
