@@ -1,4 +1,5 @@
-"""Work accounting and run contract of bench.py (CPU): the tile-granular FLOP count against closed forms, and the exits that keep every timed number on one GPU.
+"""Work accounting and run contract of bench.py (CPU): the tile-granular FLOP count against
+closed forms, and the exits that keep every timed number on one GPU.
 
 The count is the matrix work the bf16 kernel performs (32-row x 64-key blocks, masked slots
 included); the profile summary checks it against the MFMA instruction counter.
