@@ -8,10 +8,12 @@
 // Version 4.40.0"; FAT5 README, T5-like relative position bias), and key tiles that a mask
 // hides completely are never visited.
 //
-// Work decomposition (one workgroup = one query tile of one (batch, head); 32 query rows per
-// wave; D = 64 and 128: 8 waves, two per SIMD; D = 32: 4 waves, up to four workgroups per CU;
-// D = 256: 4 waves, one per SIMD, whose O accumulators need the whole register file):
-//   * each wave owns 32 query rows; its Q fragment stays in VGPRs for the whole kernel;
+// Work decomposition (one work item = one query tile of one (batch, head), one workgroup per
+// item or, for large launches, a persistent grid of one workgroup per CU walking the items;
+// 32 query rows per wave; D = 64 and 128: 8 waves, two per SIMD; D = 32: 4 waves, up to four
+// workgroups per CU; D = 256: 4 waves, one per SIMD, whose O accumulators need the whole
+// register file):
+//   * each wave owns 32 query rows; its Q fragment stays in VGPRs for the whole item;
 //   * keys are visited in tiles of 64, ascending. K and V tiles are copied global -> LDS by
 //     the DMA path of the load unit (global_load_lds_dwordx4) into a K ring (2 slots; 3 for
 //     D = 64 with a full bias) and a 2-slot V ring, stored row-major ([key][d]) with

@@ -96,10 +96,11 @@ __host__ __device__ inline int t5u_bucket(int rel) {
     return b;
 }
 
-// Decode a workgroup index into (batch, query head, query tile). Query tiles of one
+// Decode a work item index into (batch, query head, query tile). Query tiles of one
 // (batch, KV head) are consecutive, heaviest (latest, for causal masks) first; with
-// xcd_remap, workgroup x runs on XCD x % 8 (round-robin dispatch), and every XCD receives
-// whole (batch, KV head) groups so the G query heads sharing K/V hit the same L2.
+// xcd_remap, item x runs on XCD x % 8 (workgroup x under round-robin dispatch, or the
+// persistent workgroup of that XCD), and every XCD receives whole (batch, KV head) groups so
+// the G query heads sharing K/V hit the same L2.
 struct WorkItem { int b, hq, qt; };
 
 template <class Params>
