@@ -72,7 +72,7 @@
 extern "C" {
 #endif
 
-#define SDPA_ABI_VERSION 3
+#define SDPA_ABI_VERSION 4
 
 /* Size of the device scratch buffer behind sdpa_decode_noalloc (per GPU): 16 MiB. */
 #define SDPA_DECODE_SCRATCH_BYTES (16u << 20)
@@ -112,6 +112,22 @@ int sdpa_fwd_bf16_f32out(const void* q, const void* k, const void* v, float* out
                          int B, int Hq, int Hkv, int Sq, int Sk, int D, float scale,
                          int mask_kind, int window, int bias_kind, const void* bias_tbl,
                          void* stream);
+
+/*
+ * Workgroups that sdpa_fwd and sdpa_fwd_bf16_f32out launch for this shape, mask and bias on the
+ * current device (nothing is read, written or launched). A call forms one output tile per
+ * (batch, query head, block of query rows; the block height depends on D); it launches one
+ * workgroup per tile, or, for the kinds built for it (D = 64, or D = 128 with neither
+ * SDPA_BIAS_T5 nor SDPA_BIAS_T5U; never SDPA_BIAS_FULL), when B*Hkv is a multiple
+ * of 8 and there are at least two tiles per workgroup, a persistent grid of the device's CU
+ * count rounded down to a multiple of 8, each workgroup walking the tiles of its XCD. With no
+ * device the CU count reads as 0 and the one-per-tile grid is reported. The result does not
+ * change the output: both grids give the same bits.
+ *   workgroups: host pointer, receives the count. Returns the status sdpa_fwd would give for
+ *   these arguments with valid buffers (SDPA_ERR_NULL if workgroups is NULL).
+ */
+int sdpa_fwd_launch_grid(int B, int Hq, int Hkv, int Sq, int Sk, int D, int mask_kind, int window,
+                         int bias_kind, long long* workgroups);
 
 /* fp32 forward (fp32 q, k, v, out, full bias): the high-precision path, fp32 FMA arithmetic. */
 int sdpa_fwd_f32(const float* q, const float* k, const float* v, float* out, float* lse,

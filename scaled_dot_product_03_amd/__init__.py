@@ -39,8 +39,8 @@ STATUS_NAMES = {0: "SDPA_OK", 1: "SDPA_ERR_NULL", 2: "SDPA_ERR_SHAPE", 3: "SDPA_
 ENTRY_POINTS = ("sdpa_fwd", "sdpa_fwd_bf16_f32out", "sdpa_fwd_f32", "sdpa_bwd",
                 "sdpa_bwd_f32out", "sdpa_decode_ws_bytes", "sdpa_decode", "sdpa_decode_f32out",
                 "sdpa_fwd_varlen", "sdpa_fwd_varlen_f32out", "sdpa_decode_noalloc",
-                "sdpa_status_str", "sdpa_abi_version")
-ABI_VERSION = 3
+                "sdpa_fwd_launch_grid", "sdpa_status_str", "sdpa_abi_version")
+ABI_VERSION = 4
 DECODE_SCRATCH_BYTES = 16 << 20     # SDPA_DECODE_SCRATCH_BYTES
 
 _lib = None
@@ -85,6 +85,8 @@ def load():
         fn.restype = ctypes.c_int
     L.sdpa_decode_ws_bytes.argtypes = [ctypes.c_int] * 6
     L.sdpa_decode_ws_bytes.restype = ctypes.c_size_t
+    L.sdpa_fwd_launch_grid.argtypes = [ctypes.c_int] * 9 + [ctypes.POINTER(ctypes.c_longlong)]
+    L.sdpa_fwd_launch_grid.restype = ctypes.c_int
     dec_args = [ctypes.c_void_p] * 6 + [ctypes.c_size_t] + [ctypes.c_int] * 6 + \
                [ctypes.c_float] + [ctypes.c_int] * 3 + [ctypes.c_void_p, ctypes.c_void_p]
     for name in ("sdpa_decode", "sdpa_decode_f32out"):
@@ -147,6 +149,18 @@ def call_raw_varlen(entry: str, q, k, v, out, lse, cu_q, cu_k, n_seqs, total_q, 
 def decode_ws_bytes(B, Hq, Hkv, Sq, Sk, D) -> int:
     """Workspace bytes sdpa_decode needs for this shape (0 for an invalid shape)."""
     return int(load().sdpa_decode_ws_bytes(B, Hq, Hkv, Sq, Sk, D))
+
+
+def fwd_launch_grid(B, Hq, Hkv, Sq, Sk, D, *, mask="causal", window=0, bias_kind="none") -> int:
+    """Workgroups the bf16 forward launches for this shape on the current device: one per
+    query tile, or the persistent grid (CU count rounded down to a multiple of 8)."""
+    L = load()
+    wg = ctypes.c_longlong(0)
+    st = L.sdpa_fwd_launch_grid(B, Hq, Hkv, Sq, Sk, D, _kind(mask, _MASKS, "mask"), window,
+                                _kind(bias_kind, _BIASES, "bias kind"), ctypes.byref(wg))
+    if st != 0:
+        raise SdpaError(st, L.sdpa_status_str(st).decode())
+    return int(wg.value)
 
 
 def _kind(val, table, what):

@@ -11,6 +11,7 @@
 
 namespace sdpa {
 hipError_t launch_fwd_bf16(FwdParams p, int D, int mask, int bias, bool out_f32, hipStream_t s);
+hipError_t fwd_bf16_workgroups(FwdParams p, int D, int bias, long long* workgroups);
 hipError_t launch_fwd_f32(FwdParams p, int D, int mask, int bias, hipStream_t s);
 hipError_t launch_bwd_bf16(BwdParams p, int D, int mask, int bias, bool out_f32, hipStream_t s);
 hipError_t launch_decode_bf16(DecParams p, int D, int mask, int bias, bool out_f32, hipStream_t s);
@@ -320,6 +321,24 @@ int sdpa_decode_noalloc(const void* q, const void* k, const void* v, void* out, 
     if (sdpa::decode_scratch(&ws) != hipSuccess) return SDPA_ERR_DEVICE;
     return run_decode(q, k, v, out, lse, ws, B, Hq, Hkv, Sq, Sk, D, scale, mask_kind, window,
                       bias_kind, bias_tbl, stream, false);
+}
+
+int sdpa_fwd_launch_grid(int B, int Hq, int Hkv, int Sq, int Sk, int D, int mask_kind,
+                         int window, int bias_kind, long long* workgroups) {
+    if (!workgroups) return SDPA_ERR_NULL;
+    // the shape checks of sdpa_fwd, with stand-in buffers (nothing is read or launched)
+    alignas(16) static const unsigned char stand_in[16] = {0};
+    const void* b = stand_in;
+    int st = validate(b, b, b, b, (const float*)b, B, Hq, Hkv, Sq, Sk, D, 1.0f, mask_kind,
+                      window, bias_kind, bias_kind == SDPA_BIAS_NONE ? nullptr : b, 2);
+    if (st != SDPA_OK) return st;
+    const sdpa::FwdParams p = make_params(b, b, b, const_cast<void*>(b), (float*)b, B, Hq, Hkv,
+                                          Sq, Sk, 1.0f, mask_kind, window,
+                                          bias_kind == SDPA_BIAS_NONE ? nullptr : b);
+    long long wg = 0;
+    if (sdpa::fwd_bf16_workgroups(p, D, bias_kind, &wg) != hipSuccess) return SDPA_ERR_HEADDIM;
+    *workgroups = wg;
+    return SDPA_OK;
 }
 
 const char* sdpa_status_str(int status) {

@@ -62,9 +62,12 @@ template <int D, int BIAS> constexpr int waves_per_eu_of() {
 template <int D> constexpr int rows_of() { return 32 * waves_of<D>(); }   // query rows per workgroup
 // Instances that take a persistent grid: dense, no full bias, D = 64 and 128 (not T5 at 128).
 // The work loop costs ~15 VGPRs; the excluded instances would spill with it.
+constexpr bool persist_ok(int D, int bias, bool varlen) {
+    return !varlen && bias != BIAS_FULL &&
+           (D == 64 || (D == 128 && bias != BIAS_T5 && bias != BIAS_T5U));
+}
 template <int D, int BIAS, bool VARLEN> constexpr bool persist_of() {
-    return !VARLEN && BIAS != BIAS_FULL &&
-           (D == 64 || (D == 128 && BIAS != BIAS_T5 && BIAS != BIAS_T5U));
+    return persist_ok(D, BIAS, VARLEN);
 }
 constexpr int kBN = 64;             // keys per tile
 constexpr float kLog2e = 1.4426950408889634f;
@@ -818,21 +821,26 @@ static int cu_count() {
     return n;
 }
 
-template <int D, int MASK, int BIAS, bool OUT_F32, bool VARLEN>
-static hipError_t launch_one(FwdParams p, hipStream_t stream) {
+// Workgroups of a launch (p.n_qt and p.xcd_remap set): one per work item, or a persistent grid
+// when the kind allows it, every XCD receives whole (batch, KV head) groups and there are at
+// least two items per workgroup; one workgroup fits a CU (registers), so that grid is the CU
+// count rounded down to whole XCDs. Sets p.n_items (0: one workgroup per item).
+static int fwd_grid(FwdParams& p, bool persist) {
     const int total = p.B * p.Hq * p.n_qt;
-    int grid = total;
     p.n_items = 0;
-    // persistent grid when every XCD receives whole (batch, KV head) groups and there are at
-    // least two items per workgroup; one workgroup fits a CU (registers), so the grid is the
-    // CU count, rounded down to whole XCDs
-    if (persist_of<D, BIAS, VARLEN>() && p.xcd_remap) {
+    if (persist && p.xcd_remap) {
         const int pg = (cu_count() / 8) * 8;
         if (pg >= 8 && total >= 2 * pg) {
-            grid = pg;
             p.n_items = total;
+            return pg;
         }
     }
+    return total;
+}
+
+template <int D, int MASK, int BIAS, bool OUT_F32, bool VARLEN>
+static hipError_t launch_one(FwdParams p, hipStream_t stream) {
+    const int grid = fwd_grid(p, persist_of<D, BIAS, VARLEN>());
     hipLaunchKernelGGL((sdpa_fwd_bf16_kernel<D, MASK, BIAS, OUT_F32, VARLEN>), dim3(grid),
                        dim3(64 * waves_of<D>()), 0, stream, p);
     return hipGetLastError();
@@ -867,15 +875,34 @@ static hipError_t launch_varlen_d(const FwdParams& p, int mask, int bias, hipStr
 
 template <int D>
 static hipError_t launch_dim(FwdParams p, int mask, int bias, bool out_f32, hipStream_t s) {
-    constexpr int bm = rows_of<D>();
-    p.n_qt = (p.Sq + bm - 1) / bm;
     if (p.cu_q)
         return out_f32 ? launch_varlen_d<D, true>(p, mask, bias, s) : launch_varlen_d<D, false>(p, mask, bias, s);
     return out_f32 ? launch_d<D, true>(p, mask, bias, s) : launch_d<D, false>(p, mask, bias, s);
 }
 
-hipError_t launch_fwd_bf16(FwdParams p, int D, int mask, int bias, bool out_f32, hipStream_t s) {
+// query tiles per (batch, head) and the XCD grouping of a launch
+static bool fwd_geometry(FwdParams& p, int D) {
+    int bm = 0;
+    switch (D) {
+        case 32: bm = rows_of<32>(); break;
+        case 64: bm = rows_of<64>(); break;
+        case 128: bm = rows_of<128>(); break;
+        case 256: bm = rows_of<256>(); break;
+        default: return false;
+    }
+    p.n_qt = (p.Sq + bm - 1) / bm;
     p.xcd_remap = ((p.B * p.Hkv) % 8 == 0) ? 1 : 0;
+    return true;
+}
+
+hipError_t fwd_bf16_workgroups(FwdParams p, int D, int bias, long long* workgroups) {
+    if (!fwd_geometry(p, D)) return hipErrorInvalidValue;
+    *workgroups = fwd_grid(p, persist_ok(D, bias, p.cu_q != nullptr));
+    return hipSuccess;
+}
+
+hipError_t launch_fwd_bf16(FwdParams p, int D, int mask, int bias, bool out_f32, hipStream_t s) {
+    if (!fwd_geometry(p, D)) return hipErrorInvalidValue;
     switch (D) {
         case 32: return launch_dim<32>(p, mask, bias, out_f32, s);
         case 64: return launch_dim<64>(p, mask, bias, out_f32, s);

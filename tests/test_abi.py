@@ -1,6 +1,7 @@
 """C-ABI checks that need no GPU: the library loads, exports every symbol include/sdpa.h
 declares, and every invalid call returns its status before any HIP call (so these calls are
 safe on a machine without a GPU: validation fails first and nothing is launched)."""
+import ctypes
 import math
 import os
 import re
@@ -38,7 +39,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.sdpa_abi_version() == sdpa.ABI_VERSION == 3
+    assert lib.sdpa_abi_version() == sdpa.ABI_VERSION == 4
     for code in range(0, 13):
         s = sdpa.status_str(code)
         assert s and s != "unknown status"
@@ -103,6 +104,45 @@ def test_first_failing_check_wins(lib):
     assert call(B=0, Hq=6, Hkv=4) == 2
     assert call(Hq=6, Hkv=4, D=96) == 3
     assert call(D=96, mask_kind=9) == 4
+
+
+def _grid(lib, **kw):
+    a = dict(GOOD)
+    a.update(kw)
+    wg = ctypes.c_longlong(-1)
+    st = lib.sdpa_fwd_launch_grid(a["B"], a["Hq"], a["Hkv"], a["Sq"], a["Sk"], a["D"],
+                                  a["mask_kind"], a["window"], a["bias_kind"], ctypes.byref(wg))
+    return st, wg.value
+
+
+# the query takes no buffers: the cases about shapes, mask, window and an unknown bias kind
+_SHAPE_KEYS = {"B", "Hq", "Hkv", "Sq", "Sk", "D", "mask_kind", "window"}
+GRID_BAD = [c for c in BAD_CASES
+            if set(c[1]) <= _SHAPE_KEYS or c[1].get("bias_kind", 0) not in range(5)]
+
+
+@pytest.mark.parametrize("name,kw,code", GRID_BAD, ids=[c[0] for c in GRID_BAD])
+def test_launch_grid_query_rejects_what_the_forward_rejects(lib, name, kw, code):
+    assert call(**kw) == code
+    assert _grid(lib, **kw) == (code, -1)
+
+
+def test_launch_grid_query_null_out_pointer(lib):
+    assert lib.sdpa_fwd_launch_grid(1, 4, 2, 8, 8, 64, 1, 0, 0, None) == 1
+
+
+@pytest.mark.parametrize("kw,tiles", [
+    # shapes that never take the persistent grid, so no device is asked for its CU count
+    (dict(B=2, Hq=8, Hkv=8, Sq=1000, D=256), 2 * 8 * 8),             # 128 query rows a tile
+    (dict(B=3, Hq=4, Hkv=4, Sq=129, D=32), 3 * 4 * 2),
+    (dict(B=1, Hq=4, Hkv=2, Sq=8, D=64), 4),                          # 256 rows a tile
+    (dict(B=1, Hq=6, Hkv=2, Sq=4097, D=128, bias_kind=1, bias=P), 6 * 17),   # T5 at D = 128
+    (dict(B=8, Hq=8, Hkv=8, Sq=4096, D=64, bias_kind=2, bias=P), 8 * 8 * 16),  # full bias
+])
+def test_launch_grid_query_one_workgroup_per_tile(lib, kw, tiles):
+    assert _grid(lib, **kw) == (0, tiles)
+    assert sdpa.fwd_launch_grid(kw["B"], kw["Hq"], kw["Hkv"], kw["Sq"], 8, kw["D"],
+                                bias_kind=kw.get("bias_kind", 0)) == tiles
 
 
 def test_binding_rejects_before_launch(lib):

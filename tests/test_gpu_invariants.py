@@ -186,6 +186,16 @@ _PERSIST_CASES = {
 }
 
 
+def _launch_grid(sdpa, wl):
+    return sdpa.fwd_launch_grid(wl.B, wl.Hq, wl.Hkv, wl.Sq, wl.Sk, wl.D, mask=wl.mask_kind,
+                                window=wl.window, bias_kind=wl.bias_kind)
+
+
+def _persistent_grid():
+    import torch
+    return torch.cuda.get_device_properties(0).multi_processor_count // 8 * 8
+
+
 @pytest.mark.parametrize("case", sorted(_PERSIST_CASES))
 def test_persistent_grid_equals_small_launches_bitwise(gpu_lib, case):
     """At these sizes a launch walks its work items on a persistent grid (one workgroup per
@@ -195,12 +205,13 @@ def test_persistent_grid_equals_small_launches_bitwise(gpu_lib, case):
     import torch
     wl, split_kv = _PERSIST_CASES[case]
     tiles = -(-wl.Sq // (256 if wl.D in (64, 128) else 128))
-    assert wl.B * wl.Hq * tiles >= 512 and (wl.B * wl.Hkv) % 8 == 0   # a persistent launch
-    assert wl.Hq // wl.Hkv * split_kv * tiles < 512 or split_kv % 8  # small launches are not
+    G = wl.Hq // wl.Hkv
+    sub = wl.replace(B=1, Hq=split_kv * G, Hkv=split_kv)
+    assert _launch_grid(gpu_lib, wl) == _persistent_grid()          # a persistent launch
+    assert _launch_grid(gpu_lib, sub) == split_kv * G * tiles       # one workgroup per item
     inp = si.make_inputs(wl)
     q, k, v, bias = to_device(inp)
     o_all, l_all = run_gpu(gpu_lib, wl, (q, k, v, bias))
-    G = wl.Hq // wl.Hkv
     same = True
     for b in range(wl.B):
         for h0 in range(0, wl.Hkv, split_kv):
@@ -208,7 +219,6 @@ def test_persistent_grid_equals_small_launches_bitwise(gpu_lib, case):
             ks = k[b:b + 1, :, h0:h0 + split_kv].contiguous()
             vs = v[b:b + 1, :, h0:h0 + split_kv].contiguous()
             bs = bias[h0 * G:(h0 + split_kv) * G].contiguous() if bias is not None else None
-            sub = wl.replace(B=1, Hq=split_kv * G, Hkv=split_kv)
             o, l = run_gpu(gpu_lib, sub, (qs, ks, vs, bs))
             same = same and torch.equal(o[0], o_all[b, :, h0 * G:(h0 + split_kv) * G])
             same = same and torch.equal(l[0], l_all[b, h0 * G:(h0 + split_kv) * G])
@@ -243,6 +253,7 @@ def test_persistent_grid_random_shapes_bitwise(gpu_lib, seed):
     persistent grid over far fewer items): out and LSE agree bit for bit."""
     import torch
     wl = _random_persistent_case(seed)
+    assert _launch_grid(gpu_lib, wl) == _persistent_grid()
     q, k, v, bias = to_device(si.make_inputs(wl))
     o_all, l_all = run_gpu(gpu_lib, wl, (q, k, v, bias))
     sub = wl.replace(B=1)
