@@ -125,6 +125,16 @@ SMALL_F32 = [
     W["c1"].replace(name="c1_d256_causal", D=256, Sq=150, Sk=150),
     W["c1"].replace(name="c1_d256_full_none", D=256, mask_kind=si.MASK_NONE,
                     bias_kind=si.BIAS_FULL, Sq=90, Sk=130),
+    # several row blocks and key tiles with ragged ends; in the key tiles at the window's edges
+    # some waves of a workgroup see no key of their share
+    W["c1"].replace(name="c1_mqa_sliding_t5_ragged", B=2, Hq=4, Hkv=1, Sq=300, Sk=333,
+                    mask_kind=si.MASK_SLIDING, window=100, bias_kind=si.BIAS_T5),
+    W["c1"].replace(name="c1_d128_full_gqa_none", Hq=4, Hkv=2, Sq=130, Sk=97, D=128,
+                    mask_kind=si.MASK_NONE, bias_kind=si.BIAS_FULL),
+    W["c1"].replace(name="c1_d256_t5u_sliding", Sq=100, Sk=140, D=256,
+                    mask_kind=si.MASK_SLIDING, window=50, bias_kind=si.BIAS_T5U),
+    W["c1"].replace(name="c1_d32_alibi_causal_long", Sq=257, Sk=513, D=32,
+                    bias_kind=si.BIAS_ALIBI),
 ]
 
 
