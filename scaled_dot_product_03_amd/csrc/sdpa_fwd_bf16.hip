@@ -163,6 +163,7 @@ void sdpa_fwd_bf16_kernel(const FwdParams p) {
     // pwb - pwa <= 31, so |rel| < kT5Pad. Beyond +-kSat the bucket is constant.
     constexpr bool IS_T5 = BIAS == BIAS_T5 || BIAS == BIAS_T5U;
     constexpr bool ALIBI = BIAS == BIAS_ALIBI;
+    constexpr bool ALIBI_LIN = ALIBI && MASK != MASK_NONE && D != 256;   // (D = 256: no registers to spare)
     constexpr int kSat = BIAS == BIAS_T5U ? kT5USat : kT5Sat;
     constexpr int kT5Pad = kSat + kBN + 31;
     __shared__ float t5s[IS_T5 ? 2 * kT5Pad + 1 : 1];
@@ -275,6 +276,14 @@ void sdpa_fwd_bf16_kernel(const FwdParams p) {
     }
     // the same positive scale in natural-log units (a full bias is added in those units)
     const float n_scale = (p.scale == 0.f) ? 1.17549435e-38f : fabsf(p.scale);
+    // Under a causal or sliding mask no visible key follows its query, so the bias is
+    // slope * (j - p): slope * (jl - p) per row and key block, folded into the row max and the
+    // exponent's offset, plus slope * k for the key's offset k = 0..15 in the lane's run of 16
+    // keys, added to the raw score as (slope / c) * k with the score scale c applied in the
+    // exponent. c is floored at |slope| 2^-96 so that slope / c stays finite (only a zero or
+    // vanishing softmax scale meets the floor; the scores then contribute below 2^-76 |slope|).
+    const float al_c = ALIBI_LIN ? fmaxf(c_scale, fabsf(aslope) * 0x1p-96f) : 0.f;
+    const float al_a = ALIBI_LIN ? aslope / al_c : 0.f;
 
     // ---- LDS-DMA staging -------------------------------------------------------------------
     // Each wave issues 1 KB global_load_lds_dwordx4 transfers (lane i lands at M0 + 16 i).
@@ -453,6 +462,8 @@ void sdpa_fwd_bf16_kernel(const FwdParams p) {
     // p = exp2(x * cc + bc - m): cc = scale*log2(e), bc = constant bias for raw scores x, or
     // cc = 1, bc = 0 for scores already in the log2 domain (per-element bias).
     float mt_c = -INFINITY, cc_c = 0.f, bc_c = 0.f;
+    // linear ALiBi: key block 1 of a lane starts 32 keys after block 0
+    const float a32 = 32.f * aslope;
     constexpr int KPRE = 2;               // k-steps of K fragments read ahead of their MFMAs
     constexpr int VPRE = 1;               // key groups of V^T fragments read ahead
     bf16x8 vfr[VPRE + 1][DB];
@@ -467,7 +478,7 @@ void sdpa_fwd_bf16_kernel(const FwdParams p) {
                        const uint16_t* kb, const uint16_t* vb, auto&& hook) {
         constexpr bool DO_S = decltype(do_s_tag)::value;
         constexpr bool DO_E = decltype(do_e_tag)::value;
-        float nn = 0.f;
+        float nn = 0.f, nn1 = 0.f;
         if constexpr (DO_E) {
             // online softmax (log2 domain, lazy rescale)
             if (__builtin_amdgcn_ballot_w64(mt_c > m_ref + kRescaleSlack) != 0) {
@@ -482,6 +493,7 @@ void sdpa_fwd_bf16_kernel(const FwdParams p) {
             }
             const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
             nn = bc_c - m_use;
+            if constexpr (ALIBI_LIN) nn1 = nn + a32;
         }
         bf16x8 ka[KPRE][2];
         if constexpr (DO_S) {
@@ -495,7 +507,7 @@ void sdpa_fwd_bf16_kernel(const FwdParams p) {
         // covers that wait. The other exponentials are spread over the remaining k-steps.
         constexpr int E0 = 8;
         auto expo = [&](int e) {
-            float pe = __builtin_amdgcn_exp2f(fmaf(cs[e >> 4][e & 15], cc_c, nn));
+            float pe = __builtin_amdgcn_exp2f(fmaf(cs[e >> 4][e & 15], cc_c, (ALIBI_LIN && (e >> 4)) ? nn1 : nn));
             pin(pe);
             cs[e >> 4][e & 15] = pe;
         };
@@ -553,6 +565,8 @@ void sdpa_fwd_bf16_kernel(const FwdParams p) {
         }
         u32x4 fb[4];
         float ext = -INFINITY;
+        // linear ALiBi: bias of key block 0 of this lane, slope * (jl - p)
+        const float bl0 = ALIBI_LIN ? aslope * (float)(jl - my_pos) : 0.f;
         bf16x2 ones2;
         ones2[0] = (__bf16)1.0f;
         ones2[1] = (__bf16)1.0f;
@@ -600,7 +614,11 @@ void sdpa_fwd_bf16_kernel(const FwdParams p) {
                     }
                 } else if (g == 1) {
                     if (per_elem) {
-                        if constexpr (ALIBI) {
+                        if constexpr (ALIBI_LIN) {
+#pragma unroll
+                            for (int e = 0; e < 32; ++e)
+                                ns[e >> 4][e & 15] = fmaf(al_a, (float)(e & 15), ns[e >> 4][e & 15]);
+                        } else if constexpr (ALIBI) {
                             // register e holds key jl + 32 (e >> 4) + (e & 15)
                             const float base = (float)(jl - my_pos);
 #pragma unroll
@@ -662,8 +680,16 @@ void sdpa_fwd_bf16_kernel(const FwdParams p) {
                     }
                 } else {
                     // row max over key block g - 2 (hidden keys are -inf)
+                    if constexpr (ALIBI_LIN) {
+                        // each block's maximum, scaled, plus its per-row bias slope * (jl + 32 jb - p)
+                        float eb = -INFINITY;
 #pragma unroll
-                    for (int v = 0; v < 16; ++v) ext = fmaxf(ext, ns[g - 2][v]);
+                        for (int v = 0; v < 16; ++v) eb = fmaxf(eb, ns[g - 2][v]);
+                        ext = fmaxf(ext, fmaf(eb, al_c, g == 2 ? bl0 : bl0 + a32));
+                    } else {
+#pragma unroll
+                        for (int v = 0; v < 16; ++v) ext = fmaxf(ext, ns[g - 2][v]);
+                    }
                     pin(ext);
                 }
             }
@@ -677,10 +703,12 @@ void sdpa_fwd_bf16_kernel(const FwdParams p) {
                 cc_c = kLog2e;
                 bc_c = 0.f;
             } else if (per_elem) {
-                // T5 near the diagonal: scores already in the log2 domain
+                // T5 near the diagonal, ALiBi: scores already in the log2 domain (linear
+                // ALiBi: raw scores plus the per-key part; scale and per-row part in the
+                // exponent)
                 mt_c = ext;
-                cc_c = 1.f;
-                bc_c = 0.f;
+                cc_c = ALIBI_LIN ? al_c : 1.f;
+                bc_c = ALIBI_LIN ? bl0 : 0.f;
             } else {
                 // max over the raw scores (scale > 0); hidden keys stay -inf through the FMA
                 mt_c = (ext == -INFINITY) ? -INFINITY : fmaf(ext, c_scale, bconst);

@@ -72,6 +72,13 @@ SMALL_BF16 = [
              ).replace(mask_kind=si.MASK_SLIDING, window=150),
     si.small(W["c2alibi"], B=1, Hq=4, Hkv=2, Sq=256, Sk=256, name_suffix="d64_neg").replace(
         D=64, scale_override=-0.1),
+    # the masked ALiBi path keeps the per-row part of the bias out of the scores: zero scale
+    # (floored score scale), rows that see no key, D = 64 sliding with a key prefix
+    si.small(W["c2alibi"], B=1, Hq=4, Hkv=2, Sq=260, Sk=260, name_suffix="zero_scale").replace(
+        scale_override=0.0),
+    si.small(W["c2alibi"], B=1, Hq=4, Hkv=2, Sq=300, Sk=100, name_suffix="q300_k100"),
+    si.small(W["c2alibi"], B=1, Hq=8, Hkv=1, Sq=230, Sk=610, name_suffix="d64_sliding_q230_k610"
+             ).replace(D=64, mask_kind=si.MASK_SLIDING, window=97),
     si.small(W["c4t5u"], B=2, Hq=3, Hkv=3, Sq=333, Sk=333, name_suffix="s333"),
     si.small(W["c4t5u"], B=1, Hq=4, Hkv=2, Sq=300, Sk=300, name_suffix="none").replace(
         mask_kind=si.MASK_NONE),
