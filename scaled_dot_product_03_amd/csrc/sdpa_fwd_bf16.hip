@@ -10,13 +10,13 @@
 //
 // Work decomposition (one work item = one query tile of one (batch, head), one workgroup per
 // item or, for large launches, a persistent grid of one workgroup per CU walking the items;
-// 32 query rows per wave; D = 64 and 128: 8 waves, two per SIMD; D = 32: 4 waves, up to four
-// workgroups per CU; D = 256: 4 waves, one per SIMD, whose O accumulators need the whole
-// register file):
+// 32 query rows per wave; D = 64 and 128: 8 waves, two per SIMD (D = 64 with a full bias: 4
+// waves, two workgroups per CU); D = 32: 4 waves, up to four workgroups per CU; D = 256: 4
+// waves, one per SIMD, whose O accumulators need the whole register file):
 //   * each wave owns 32 query rows; its Q fragment stays in VGPRs for the whole item;
 //   * keys are visited in tiles of 64, ascending. K and V tiles are copied global -> LDS by
-//     the DMA path of the load unit (global_load_lds_dwordx4) into a K ring (2 slots; 3 for
-//     D = 64 with a full bias) and a 2-slot V ring, stored row-major ([key][d]) with
+//     the DMA path of the load unit (global_load_lds_dwordx4) into a 2-slot K ring (a full
+//     bias tile rides in the K slot) and a 2-slot V ring, stored row-major ([key][d]) with
 //     XOR-swizzled 16-byte chunks; K runs one tile ahead of V;
 //   * scores are computed transposed, S^T = K . Q^T, with v_mfma_f32_32x32x16_bf16: each lane
 //     then holds one query row (lane % 32) and 32 of the tile's keys, so the row max/sum are
@@ -55,11 +55,13 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 
 // waves per workgroup, and the waves per SIMD the register budget is sized for
-template <int D> constexpr int waves_of() { return (D == 64 || D == 128) ? 8 : 4; }
+template <int D, int BIAS> constexpr int waves_of() {
+    return ((D == 64 && BIAS != BIAS_FULL) || D == 128) ? 8 : 4;
+}
 template <int D, int BIAS> constexpr int waves_per_eu_of() {
     return D == 256 ? 1 : ((D == 32 && BIAS != BIAS_FULL) ? 3 : 2);
 }
-template <int D> constexpr int rows_of() { return 32 * waves_of<D>(); }   // query rows per workgroup
+template <int D, int BIAS> constexpr int rows_of() { return 32 * waves_of<D, BIAS>(); }   // query rows per workgroup
 // Instances that take a persistent grid: dense, no full bias, D = 64 and 128 (not T5 at 128).
 // The work loop costs ~15 VGPRs; the excluded instances would spill with it.
 constexpr bool persist_ok(int D, int bias, bool varlen) {
@@ -133,11 +135,11 @@ __device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
 
 
 template <int D, int MASK, int BIAS, bool OUT_F32, bool VARLEN>
-__global__ __launch_bounds__(64 * waves_of<D>(), (waves_per_eu_of<D, BIAS>()))
+__global__ __launch_bounds__((64 * waves_of<D, BIAS>()), (waves_per_eu_of<D, BIAS>()))
 void sdpa_fwd_bf16_kernel(const FwdParams p) {
-    constexpr int kWaves = waves_of<D>();
+    constexpr int kWaves = waves_of<D, BIAS>();
     constexpr int kThreads = 64 * kWaves;
-    constexpr int kBM = rows_of<D>();
+    constexpr int kBM = rows_of<D, BIAS>();
     constexpr int CH = D / 8;           // 16-byte chunks per K/V row
     constexpr int KS = D / 16;          // k-steps of Q.K^T
     constexpr int DB = D / 32;          // 32-wide d blocks of O^T
@@ -146,11 +148,12 @@ void sdpa_fwd_bf16_kernel(const FwdParams p) {
     // LDS: K ring (NKS slots, each a K tile followed, for a full bias, by the [256 rows][64 keys]
     // bias tile of the same keys), then the V ring (NVS slots).
     constexpr bool FB = BIAS == BIAS_FULL;
-    // A full bias streams from HBM with the K tiles: for D = 64 the K ring is 3 deep (K tiles
-    // are fetched two iterations before use), which the LDS holds; otherwise 2 deep. At
-    // D = 256 the K and V rings fill the LDS: the bias is read from HBM by each lane instead.
+    // A full bias streams from HBM with the K tiles through the 2-slot K ring. At D = 64 the
+    // workgroup has 4 waves (128 rows, 64 KB of LDS) so that two workgroups share a CU and
+    // one computes while the other waits for its next bias tile. At D = 256 the K and V rings
+    // fill the LDS: the bias is read from HBM by each lane instead.
     constexpr bool FB_LDS = FB && D != 256;
-    constexpr int NKS = (FB && D == 64) ? 3 : 2;
+    constexpr int NKS = 2;
     constexpr int NVS = 2;
     constexpr int BTILE = FB_LDS ? kBM * kBN : 0;
     constexpr int KSTAGE = TILE + BTILE;
@@ -870,7 +873,7 @@ template <int D, int MASK, int BIAS, bool OUT_F32, bool VARLEN>
 static hipError_t launch_one(FwdParams p, hipStream_t stream) {
     const int grid = fwd_grid(p, persist_of<D, BIAS, VARLEN>());
     hipLaunchKernelGGL((sdpa_fwd_bf16_kernel<D, MASK, BIAS, OUT_F32, VARLEN>), dim3(grid),
-                       dim3(64 * waves_of<D>()), 0, stream, p);
+                       dim3(64 * waves_of<D, BIAS>()), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -909,13 +912,13 @@ static hipError_t launch_dim(FwdParams p, int mask, int bias, bool out_f32, hipS
 }
 
 // query tiles per (batch, head) and the XCD grouping of a launch
-static bool fwd_geometry(FwdParams& p, int D) {
+static bool fwd_geometry(FwdParams& p, int D, int bias) {
     int bm = 0;
     switch (D) {
-        case 32: bm = rows_of<32>(); break;
-        case 64: bm = rows_of<64>(); break;
-        case 128: bm = rows_of<128>(); break;
-        case 256: bm = rows_of<256>(); break;
+        case 32: bm = rows_of<32, BIAS_NONE>(); break;
+        case 64: bm = bias == BIAS_FULL ? rows_of<64, BIAS_FULL>() : rows_of<64, BIAS_NONE>(); break;
+        case 128: bm = rows_of<128, BIAS_NONE>(); break;
+        case 256: bm = rows_of<256, BIAS_NONE>(); break;
         default: return false;
     }
     p.n_qt = (p.Sq + bm - 1) / bm;
@@ -924,13 +927,13 @@ static bool fwd_geometry(FwdParams& p, int D) {
 }
 
 hipError_t fwd_bf16_workgroups(FwdParams p, int D, int bias, long long* workgroups) {
-    if (!fwd_geometry(p, D)) return hipErrorInvalidValue;
+    if (!fwd_geometry(p, D, bias)) return hipErrorInvalidValue;
     *workgroups = fwd_grid(p, persist_ok(D, bias, p.cu_q != nullptr));
     return hipSuccess;
 }
 
 hipError_t launch_fwd_bf16(FwdParams p, int D, int mask, int bias, bool out_f32, hipStream_t s) {
-    if (!fwd_geometry(p, D)) return hipErrorInvalidValue;
+    if (!fwd_geometry(p, D, bias)) return hipErrorInvalidValue;
     switch (D) {
         case 32: return launch_dim<32>(p, mask, bias, out_f32, s);
         case 64: return launch_dim<64>(p, mask, bias, out_f32, s);

@@ -137,7 +137,7 @@ def test_launch_grid_query_null_out_pointer(lib):
     (dict(B=3, Hq=4, Hkv=4, Sq=129, D=32), 3 * 4 * 2),
     (dict(B=1, Hq=4, Hkv=2, Sq=8, D=64), 4),                          # 256 rows a tile
     (dict(B=1, Hq=6, Hkv=2, Sq=4097, D=128, bias_kind=1, bias=P), 6 * 17),   # T5 at D = 128
-    (dict(B=8, Hq=8, Hkv=8, Sq=4096, D=64, bias_kind=2, bias=P), 8 * 8 * 16),  # full bias
+    (dict(B=8, Hq=8, Hkv=8, Sq=4096, D=64, bias_kind=2, bias=P), 8 * 8 * 32),  # full bias: 128 rows
 ])
 def test_launch_grid_query_one_workgroup_per_tile(lib, kw, tiles):
     assert _grid(lib, **kw) == (0, tiles)

@@ -60,6 +60,16 @@ SMALL_BF16 = [
         scale_override=-0.1),
     si.small(W["c4full"], B=1, Hq=2, Hkv=2, Sq=136, Sk=136, name_suffix="neg_scale").replace(
         scale_override=-0.1),
+    # full bias at D = 64 (its own 4-slot ring): 1, 2, 3 and 5 key tiles (the ring's start and
+    # wrap), a ragged last query tile, a band that starts past key tile 0, Sq < Sk causal
+    si.small(W["c4full"], B=1, Hq=2, Hkv=2, Sq=300, Sk=64, name_suffix="q300_k64"),
+    si.small(W["c4full"], B=1, Hq=2, Hkv=2, Sq=300, Sk=128, name_suffix="q300_k128"),
+    si.small(W["c4full"], B=1, Hq=2, Hkv=2, Sq=300, Sk=192, name_suffix="q300_k192"),
+    si.small(W["c4full"], B=2, Hq=2, Hkv=1, Sq=520, Sk=320, name_suffix="q520_k320"),
+    si.small(W["c4full"], B=1, Hq=2, Hkv=2, Sq=600, Sk=600, name_suffix="sliding_w200").replace(
+        mask_kind=si.MASK_SLIDING, window=200),
+    si.small(W["c4full"], B=1, Hq=2, Hkv=2, Sq=256, Sk=512, name_suffix="causal_q256_k512").replace(
+        mask_kind=si.MASK_CAUSAL),
     si.small(W["c3c"], B=1, Hq=2, Hkv=1, Sq=200, Sk=200, name_suffix="zero_scale").replace(
         scale_override=0.0),
     si.small(W["c4t5"], B=1, Hq=2, Hkv=2, Sq=140, Sk=140, name_suffix="zero_scale").replace(
