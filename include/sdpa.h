@@ -116,7 +116,8 @@ int sdpa_fwd_bf16_f32out(const void* q, const void* k, const void* v, float* out
 /*
  * Workgroups that sdpa_fwd and sdpa_fwd_bf16_f32out launch for this shape, mask and bias on the
  * current device (nothing is read, written or launched). A call forms one output tile per
- * (batch, query head, block of query rows; the block height depends on D); it launches one
+ * (batch, query head, block of query rows: 256 rows at D = 64 and 128, 128 rows at D = 32 and
+ * 256 and for SDPA_BIAS_FULL at D = 64); it launches one
  * workgroup per tile, or, for the kinds built for it (D = 64, or D = 128 with neither
  * SDPA_BIAS_T5 nor SDPA_BIAS_T5U; never SDPA_BIAS_FULL), when B*Hkv is a multiple
  * of 8 and there are at least two tiles per workgroup, a persistent grid of the device's CU
