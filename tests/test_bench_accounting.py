@@ -127,3 +127,33 @@ def test_no_gpu_exits_instead_of_falling_back(capsys):
         pytest.skip("a GPU is visible")
     assert bench.main(["--no-cpu-baseline", "--no-sweep"]) == 1
     assert "no GPU" in capsys.readouterr().err
+
+
+def _profile_sources(name):
+    if name.startswith("sdpa_bwd"):
+        return bench.KERNEL_SOURCES_BWD
+    if name.startswith("sdpa_decode"):
+        return bench.KERNEL_SOURCES_DEC
+    return bench.KERNEL_SOURCES
+
+
+def test_profiles_describe_the_committed_kernels():
+    """Every profile summary states the hash of the kernel sources it was taken on; it must be
+    the hash of the sources in the tree (a kernel change calls for new profiles), and the
+    traffic records the bench line reads must carry the same hash."""
+    import json
+    import re
+    pdir = os.path.join(ROOT, "profiles")
+    names = sorted(os.listdir(pdir))
+    assert names, "no profiles"
+    for name in names:
+        path = os.path.join(pdir, name)
+        want = bench.kernel_sha(_profile_sources(name))
+        if name.endswith(".json"):
+            with open(path) as f:
+                assert json.load(f)["kernel_sha"] == want, name
+        else:
+            with open(path) as f:
+                m = re.search(r"sha[^:]*\):\s*([0-9a-f]{16})", f.read())
+            assert m, f"{name}: no kernel source hash"
+            assert m.group(1) == want, name
