@@ -157,3 +157,13 @@ def test_profiles_describe_the_committed_kernels():
                 m = re.search(r"sha[^:]*\):\s*([0-9a-f]{16})", f.read())
             assert m, f"{name}: no kernel source hash"
             assert m.group(1) == want, name
+
+
+def test_headline_line_carries_measured_traffic():
+    """With the profiles matching the sources, the bench line's roofline entry carries the HBM
+    bytes measured by the byte counters (forward, gradients and decode headline workloads)."""
+    assert bench.load_traffic(si.WORKLOADS["c2"].name) is not None
+    assert bench.load_traffic(si.WORKLOADS["c2"].name, bwd=True) is not None
+    dec = [f for f in os.listdir(os.path.join(ROOT, "profiles")) if f.startswith("sdpa_decode")
+           and f.endswith(".json")]
+    assert dec
